@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Throughput of the chunked-prefill-with-past hot path on one MI355X.
+
+One step = one pass of the whole path of every layer of the workload over one
+chunk: RoPE(Q), RoPE(K), [padded-append snapshot], attention over past + C
+keys, KV append, [rollback], last-real-row selection -- all in libcp's HIP
+kernels.  Inputs are seeded synthetic tensors resident in HBM before timing.
+
+Each timed step gets its own pre-initialised `seen` array over the shared K/V
+buffers, so every step does exactly the same work (same positions, same rows
+written) and nothing but the path runs inside the timed region.  The K timed
+steps are captured once into a HIP graph and replayed (launch amortisation);
+the eager rate is reported beside it on stderr.
+
+Prints ONE JSON line on stdout.  metric: real chunk tokens per second per
+layer.  roofline: the attention call (the dominant kernel) timed alone with
+HIP events over a graph of back-to-back launches, against its algorithmic
+bytes or flops.  cpu_baseline: the CPU oracle timed on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+from chunked_prefill_attention_rope_amd import inputs as I  # noqa: E402
+
+METRIC = "chunk-prefill tok/s per layer; achieved TB/s or MFMA % of MI355X peak"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3     # fp32 vector
+
+WORKLOADS = {
+    "c1": "single fp32 layer, H4/KV1 D64, 48 cached, C16 (11 real), global, explicit mask",
+    "c2": "Gemma-270M-like global layer, bf16, H4/KV1 D256, 800 cached, C64 (52 real), "
+          "explicit per-head mask [1,4,64,864], select row 51",
+    "c3": "sliding ring W512 holding 1023 positions, bf16, H8/KV1 D256, C128 (127 real, "
+          "padded append with snapshot/rollback), in-kernel mask",
+    "c4": "Llama-8B-like GQA layer, bf16, B16 H32/KV8 D128, past U[0,4095], C128, global causal",
+    "c5": "long context, bf16, B4 H32/KV8 D128, 32768 past, C512, 5 sliding (W4096) + 1 global",
+}
+
+
+def layers_of(name):
+    return [I.config(name, l) for l in range(6)] if name == "c5" else [I.config(name)]
+
+
+def attended(cfg, b, i):
+    """(past rows, chunk rows) attended by real row i of sequence b (in-kernel rule)."""
+    seen = cfg.seen[b]
+    qpos = seen + i
+    L = cfg.live_count(b)
+    if cfg.ring:
+        R = cfg.cap - cfg.sink
+        ns = min(cfg.sink, seen)
+        lo = max(cfg.sink, seen - R)
+    else:
+        ns, lo = 0, 0
+    first = qpos - cfg.window + 1 if cfg.window else -(1 << 60)
+    npast = ns + max(0, seen - max(lo, first)) if L else 0
+    npast = min(npast, L)
+    nchunk = i + 1 if not cfg.window else min(i + 1, cfg.window)
+    return npast, nchunk
+
+
+def algorithmic(cfg):
+    """Algorithmic HBM bytes and flops of one attention launch: Q, the chunk's K/V, the
+    past K/V rows some real row attends, the output (and the explicit mask); flops
+    4*D per attended (query head, key) pair of a real row."""
+    es = 4 if cfg.dtype == I.F32 else 2
+    B, H, nKV, C, D = cfg.B, cfg.H, cfg.nKV, cfg.C, cfg.D
+    nbytes = 2 * B * H * C * D * es + 2 * B * nKV * C * D * es
+    pairs = 0
+    for b in range(B):
+        nv = cfg.n_valid[b]
+        for i in range(nv):
+            npast, nchunk = attended(cfg, b, i)
+            pairs += npast + nchunk
+        # every real row attends a suffix of the live past (plus the sinks); row 0's
+        # is the longest, so it is the union of the past rows that must be read
+        if nv:
+            nbytes += 2 * nKV * attended(cfg, b, 0)[0] * D * es
+    if cfg.explicit_mask:
+        nbytes += B * H * C * cfg.mask_ld() * 4
+    flops = 4 * D * H * pairs
+    return nbytes, flops
+
+
+class Layer:
+    """Device inputs, per-step caches and buffers of one layer."""
+
+    def __init__(self, cp, path, cfg, nsteps):
+        self.cfg = cfg
+        t = I.make_layer(cfg, nan_dead=False)
+        self.host = t
+        d = {k: v.to("cuda") for k, v in t.items()}
+        self.d = d
+        self.seen0 = d["seen"]
+        self.seen_all = d["seen"].repeat(nsteps, 1).contiguous()
+        self.caches = [cp.KVCache(d["kc"], d["vc"], self.seen_all[s], ring=cfg.ring,
+                                  sink=cfg.sink) for s in range(nsteps)]
+        self.mask = None
+        if cfg.explicit_mask:
+            self.mask = cp.build_mask(self.caches[0], d["n_valid"], cfg.H, cfg.C, cfg.mask_ld())
+        self.static = bool(cfg.ring) and any(n < cfg.C for n in cfg.n_valid)
+        self.window = 0 if cfg.explicit_mask else cfg.window
+        self.bufs = path.make_buffers(self.caches[0], d["q"], d["k"], d["v"], mask=self.mask,
+                                      window=self.window, static_append=self.static)
+
+    def reset(self):
+        self.seen_all.copy_(self.seen0.expand_as(self.seen_all))
+
+    def step(self, path, s):
+        d = self.d
+        path.chunk_step(self.caches[s], d["q"], d["k"], d["v"], d["cos"], d["sin"],
+                        d["n_valid"], self.bufs, mask=self.mask, window=self.window,
+                        static_append=self.static)
+
+    def attn_only(self, cp):
+        d, b = self.d, self.bufs
+        cp.attn_chunk_with_past(self.caches[0], b.q_rot, b.k_rot, d["v"], n_valid=d["n_valid"],
+                                mask=self.mask, window=self.window, scale=self.cfg.scale,
+                                out=b.out, workspace=b.workspace)
+
+
+def time_graph(fn, reps_inside, replays=1):
+    """Capture fn() once into a HIP graph; replay it `replays` times; ms per replay."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # warm the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    g.replay()  # warm replay
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(replays):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / replays, g
+
+
+def cpu_baseline(layers, seconds):
+    """The oracle as it stands, on host cores, over a bounded sample of the workload."""
+    from oracle import oracle as O
+    cores = O.num_threads()
+    masks = [O.build_mask(l.cfg.seen, l.cfg.n_valid, l.cfg.H, l.cfg.C, l.cfg.mask_ld(),
+                          l.cfg.cap, l.cfg.ring, l.cfg.sink, l.cfg.window)
+             if l.cfg.explicit_mask else None for l in layers]  # caller-side input, untimed
+    total_tok, total_s, reps, desc = 0, 0.0, 0, ""
+    deadline = time.perf_counter() + seconds
+    while True:
+        for lay, mask in zip(layers, masks):
+            cfg, t = lay.cfg, lay.host
+            nv = I.np_view
+            rows = None
+            if cfg.C * max(cfg.live_count(b) for b in range(cfg.B)) > 4_000_000:
+                rows = [0, cfg.C // 2, cfg.C - 1]  # sampled rows of a long-context layer
+            t0 = time.perf_counter()
+            qr = O.rope(nv(t["q"]), nv(t["cos"]), nv(t["sin"]))
+            kr = O.rope(nv(t["k"]), nv(t["cos"]), nv(t["sin"]))
+            out = O.attn(qr, kr, nv(t["v"]), nv(t["kc"]), nv(t["vc"]), nv(t["seen"]),
+                         nv(t["n_valid"]), mask, cfg.ring, cfg.sink,
+                         0 if mask is not None else cfg.window, cfg.scale, rows=rows)
+            if rows is None:
+                O.kv_append(nv(t["kc"]), nv(t["vc"]), nv(t["seen"]), kr, nv(t["v"]),
+                            nv(t["n_valid"]), cfg.ring, cfg.sink)
+            O.select_row(out, nv(t["n_valid"]), -1)
+            total_s += time.perf_counter() - t0
+            total_tok += (len(rows) * cfg.B) if rows else sum(cfg.n_valid)
+            desc = (f"{len(rows)} sampled chunk rows x {cfg.B} sequences per layer (attention "
+                    f"only)" if rows else "full layer step (rope, attention, append, select)")
+        reps += 1
+        if time.perf_counter() > deadline or reps >= 10000:
+            break
+    return {"value": total_tok / total_s, "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": f"{desc}, {reps} reps over {len(layers)} layer(s), {total_s:.1f} s; "
+                      f"{os.cpu_count()} host CPUs visible"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--eager", action="store_true", help="time eager launches, not a graph")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--attn-reps", type=int, default=200)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU: this path has no multi-GPU mode (see DESIGN.md for "
+              "how it would shard); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    from chunked_prefill_attention_rope_amd import cp, path
+
+    torch.cuda.set_device(0)
+    K, W = args.steps, args.warmup
+    layers = [Layer(cp, path, cfg, K + W) for cfg in layers_of(args.workload)]
+    torch.cuda.synchronize()
+    cfg0 = layers[0].cfg
+    tokens_per_layer = sum(cfg0.n_valid)
+    nl = len(layers)
+
+    def run_steps(lo, hi):
+        for s in range(lo, hi):
+            for lay in layers:
+                lay.step(path, s)
+
+    # warmup: W eager steps
+    run_steps(0, W)
+    torch.cuda.synchronize()
+
+    # eager rate over the K step slots
+    for lay in layers:
+        lay.reset()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run_steps(W, W + K)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / K
+
+    if args.eager:
+        ms_per_step = eager_ms
+        mode = "eager"
+    else:
+        # capture the K timed steps once, reset the per-step lengths, replay once (timed)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            run_steps(W, W + K)
+        torch.cuda.synchronize()
+        for lay in layers:
+            lay.reset()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        ms_per_step = t0.elapsed_time(t1) / K
+        mode = "hip-graph"
+        del g
+
+    value = tokens_per_layer * nl / (ms_per_step * 1e-3) / nl  # tok/s per layer
+
+    # dominant kernel: the attention call, timed alone (graph of back-to-back launches)
+    lay_dom = max(layers, key=lambda l: algorithmic(l.cfg)[1])
+    R = args.attn_reps
+    attn_ms, _ = time_graph(lambda: [lay_dom.attn_only(cp) for _ in range(R)], R)
+    attn_ms /= R
+    nbytes, flops = algorithmic(lay_dom.cfg)
+    intensity = flops / nbytes
+    ridge = (BF16_PEAK_TFLOPS if lay_dom.cfg.dtype == I.BF16 else FP32_PEAK_TFLOPS) * 1e12 / (
+        HBM_PEAK_GBS * 1e9)
+    if intensity < ridge:
+        achieved = nbytes / (attn_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5)}
+    else:
+        peak = BF16_PEAK_TFLOPS if lay_dom.cfg.dtype == I.BF16 else FP32_PEAK_TFLOPS
+        achieved = flops / (attn_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma" if lay_dom.cfg.dtype == I.BF16 else "alu",
+                "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 5)}
+    roof["traffic"] = None
+    roof["kernel"] = "cp_attn_chunk_with_past"
+    roof["avg_launch_us"] = round(attn_ms * 1e3, 3)
+    roof["algorithmic_bytes"] = nbytes
+    roof["algorithmic_flops"] = flops
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tok/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if cfg0.dtype == I.F32 else "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}",
+                   "layers_per_step": nl, "real_tokens_per_layer": tokens_per_layer,
+                   "launch": mode, "eager_ms_per_step": round(eager_ms, 6)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(layers, args.cpu_seconds)
+    print(f"[bench] {args.workload}: {mode} {ms_per_step * 1e3:.2f} us/step, eager "
+          f"{eager_ms * 1e3:.2f} us/step, attention {attn_ms * 1e3:.2f} us/launch",
+          file=sys.stderr, flush=True)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

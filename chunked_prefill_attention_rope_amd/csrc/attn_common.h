@@ -1,0 +1,126 @@
+// attn_common.h -- pieces shared by the two attention kernels of libcp.
+//
+// [SKaiNET] "Change (additive)": attention of C chunk rows over past + C keys
+// with an additive mask (0 attends, -1e30 masks) that carries the causal band,
+// the zero padding and the sliding window.  The keys are the live past rows in
+// chronological order followed by the chunk's own rows; the past is read as
+// it stands before the chunk is appended.
+#pragma once
+
+#include "cp_common.h"
+
+namespace cp {
+
+// Kernel parameters (passed by value).
+struct AttnParams {
+  const void *q, *kn, *vn, *kc, *vc;
+  void *out;
+  const int32_t *seen, *n_valid;
+  int32_t *status;
+  const float *mask;
+  int64_t mld, mhs, mbs;
+  float *wo;   // split partials: O [S][B][H][C][D]
+  float *wml;  // split partials: m, l [S][B][H][C][2]
+  int B, H, nKV, C, cap, ring, sink, window;
+  int G;       // query heads per KV head
+  int qpos;    // chunk rows per query tile
+  int hb;      // heads per tile (vector-ALU kernel)
+  int hgroups; // head groups per KV head (vector-ALU kernel)
+  int qtiles;  // query tiles per (b, kv head, head group)
+  int splits;
+  int full_tiles;
+  int mask_vec4;  // explicit mask rows may be read 16 bytes at a time
+  float sl2e;     // scale * log2(e)
+};
+
+// Ordered list of the key tiles one query tile needs.  Past tiles cover
+// columns [t*kt, t*kt + kt) of the live past, chunk tiles rows [t*kt, ...).
+// With the in-kernel mask, tiles no real row of the query tile attends
+// (older than the window, later than the last real row) are left out; part A
+// is the tiles holding pinned sink rows.
+struct TileSeq {
+  int nA, tB0, nB, tC0, nC;
+  __device__ int count() const { return nA + nB + nC; }
+  // returns true for a chunk tile; *first = first column (past) or row (chunk)
+  __device__ bool at(int u, int kt, int *first) const {
+    if (u < nA) {
+      *first = u * kt;
+      return false;
+    }
+    u -= nA;
+    if (u < nB) {
+      *first = (tB0 + u) * kt;
+      return false;
+    }
+    *first = (tC0 + u - nB) * kt;
+    return true;
+  }
+};
+
+__device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
+__device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
+
+__device__ __forceinline__ TileSeq make_tiles(const Live &g, int seen, int C, int kt, int i_min,
+                                              int i_last, int window, int sink, bool full) {
+  TileSeq s;
+  const int nPT = (g.L + kt - 1) / kt;
+  if (full) {
+    s.nA = 0;
+    s.tB0 = 0;
+    s.nB = nPT;
+    s.tC0 = 0;
+    s.nC = (C + kt - 1) / kt;
+    return s;
+  }
+  s.nA = (g.ns + kt - 1) / kt;
+  int cfirst = g.ns;
+  if (window > 0) {
+    const long pfirst = static_cast<long>(seen) + i_min - window + 1;
+    long d = pfirst - g.lo;
+    if (d < 0) d = 0;
+    if (d > g.L - g.ns) d = g.L - g.ns;
+    cfirst = g.ns + static_cast<int>(d);
+  }
+  s.tB0 = imax(s.nA, cfirst / kt);
+  s.nB = imax(0, nPT - s.tB0);
+  int jlo = 0;
+  if (window > 0 && seen >= sink) jlo = imax(0, i_min - window + 1);
+  const int jhi = i_last + 1;
+  s.tC0 = jlo / kt;
+  s.nC = imax(0, (jhi + kt - 1) / kt - s.tC0);
+  return s;
+}
+
+// True when every real row of the query tile attends every key of the tile,
+// so the in-kernel mask can be skipped for it.
+__device__ __forceinline__ bool tile_all_visible(bool chunk, int first, int kt, const Live &g,
+                                                 int seen, int C, int i_min, int i_last,
+                                                 int window) {
+  if (chunk) {
+    if (first + kt > C || first + kt - 1 > i_min) return false;
+    return window == 0 || i_last - first < window;
+  }
+  if (first + kt > g.L) return false;
+  if (window == 0) return true;
+  const int cn = imax(first, g.ns);  // first non-sink column: the oldest position
+  if (cn >= first + kt) return true;  // sink rows only
+  return (seen + i_last) - column_position(g, cn) < window;
+}
+
+// Additive mask value (log2 units applied later) of one (row, key) pair with
+// the in-kernel rule; -inf for keys outside the tile's valid range.
+__device__ __forceinline__ float inkernel_add(bool chunk, int col, const Live &g, int seen, int C,
+                                              int nv, int qpos_abs, int window, int sink) {
+  if (chunk) {
+    if (col >= C) return -INFINITY;
+    return attend(qpos_abs, seen + col, col < nv, window, sink) ? 0.f : kMasked;
+  }
+  if (col >= g.L) return -INFINITY;
+  return attend(qpos_abs, column_position(g, col), true, window, sink) ? 0.f : kMasked;
+}
+
+hipError_t launch_attn_valu(const AttnParams &p, int D, int dtype, hipStream_t s);
+hipError_t launch_attn_mfma(const AttnParams &p, int D, hipStream_t s);
+hipError_t launch_attn_combine(const AttnParams &p, int D, int dtype, hipStream_t s);
+
+}  // namespace cp

@@ -1,0 +1,278 @@
+// attn_valu.hip -- chunk attention on the vector ALUs (fp32 path, and the
+// fallback for shapes the matrix-core kernel does not take), plus the merge
+// of key-split partials.
+//
+// [SKaiNET] "Change (additive)": attention over past + C keys with the
+// additive per-head mask.  One workgroup = 16 query rows (hb heads of one KV
+// group x qpos chunk rows) x 16 lanes per row; a lane owns D/16 output
+// columns.  K/V tiles of 16 keys are staged in LDS as fp32 and shared by the
+// rows; scores are reduced across the 16 lanes of a row with cross-lane
+// shuffles; the softmax is the online (running max / running sum) form in
+// base 2 with scale*log2(e) folded into one FMA.  fp32 accumulation.
+#include "attn_common.h"
+
+namespace cp {
+namespace {
+
+constexpr int KTG = 16;   // keys per tile
+constexpr int ROWS = 16;  // query rows per workgroup
+
+template <typename T>
+__device__ __forceinline__ float ld(const T *p, size_t i);
+template <>
+__device__ __forceinline__ float ld<float>(const float *p, size_t i) {
+  return p[i];
+}
+template <>
+__device__ __forceinline__ float ld<uint16_t>(const uint16_t *p, size_t i) {
+  return bf16_to_f32(p[i]);
+}
+__device__ __forceinline__ void st(float *p, size_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void st(uint16_t *p, size_t i, float v) { p[i] = f32_to_bf16_rne(v); }
+
+template <typename T, int DPT, bool EXPLICIT>
+__global__ void __launch_bounds__(256) k_attn_valu(AttnParams p, int D) {
+  extern __shared__ float lds[];
+  float *Ks = lds;             // [KTG][D]
+  float *Vs = lds + KTG * D;   // [KTG][D]
+
+  const int tid = threadIdx.x;
+  const int r = tid / 16;      // row in the workgroup
+  const int ql = tid % 16;     // lane within the row
+
+  int w = blockIdx.x;
+  const int qtile = w % p.qtiles;
+  w /= p.qtiles;
+  const int hgrp = w % p.hgroups;
+  w /= p.hgroups;
+  const int split = w % p.splits;
+  const int bg = w / p.splits;
+  const int b = bg / p.nKV;
+  const int g = bg % p.nKV;
+
+  const int i_min = qtile * p.qpos;
+  const int hl = hgrp * p.hb + r / p.qpos;
+  const int i = i_min + r % p.qpos;
+  const bool row_ok = r < p.hb * p.qpos && hl < p.G && i < p.C;
+  const int head = g * p.G + (hl < p.G ? hl : 0);
+
+  const int seen = p.seen[b];
+  const bool lead = tid == 0 && qtile == 0 && hgrp == 0 && split == 0 && g == 0;
+  const int nv = read_nvalid(p.n_valid, b, p.C, lead ? p.status : nullptr);
+  bool bad = seen < 0 || (!p.ring && seen > p.cap);
+  if (bad && lead) flag(p.status, CP_DEV_SEEN);
+  const Live gl = live_geometry(bad ? 0 : seen, p.cap, p.ring, p.sink);
+  if (EXPLICIT && !bad && static_cast<int64_t>(gl.L) + p.C > p.mld) {
+    bad = true;
+    if (lead) flag(p.status, CP_DEV_MASK_LD);
+  }
+  const int i_end = imin(i_min + p.qpos, p.C);
+  const int i_last = imin(i_end, nv) - 1;
+  const bool any_real = !bad && i_last >= i_min;
+
+  float q[DPT], acc[DPT];
+  const T *Q = static_cast<const T *>(p.q);
+  const size_t qoff = ((static_cast<size_t>(b) * p.H + head) * p.C + (i < p.C ? i : 0)) * D;
+#pragma unroll
+  for (int e = 0; e < DPT; ++e) {
+    const int d = ql + 16 * e;
+    q[e] = (row_ok && d < D) ? ld<T>(Q, qoff + d) : 0.f;
+    acc[e] = 0.f;
+  }
+  float m_run = -INFINITY, l_run = 0.f;
+
+  TileSeq ts{};
+  int u0 = 0, u1 = 0;
+  if (any_real) {
+    ts = make_tiles(gl, seen, p.C, KTG, i_min, i_last, EXPLICIT ? 0 : p.window, p.sink,
+                    EXPLICIT || p.full_tiles);
+    const int n = ts.count();
+    u0 = static_cast<int>((static_cast<long>(n) * split) / p.splits);
+    u1 = static_cast<int>((static_cast<long>(n) * (split + 1)) / p.splits);
+  }
+  const T *KC = static_cast<const T *>(p.kc);
+  const T *VC = static_cast<const T *>(p.vc);
+  const T *KN = static_cast<const T *>(p.kn);
+  const T *VN = static_cast<const T *>(p.vn);
+  const size_t cbase = (static_cast<size_t>(b) * p.nKV + g) * p.cap;
+  const size_t nbase = (static_cast<size_t>(b) * p.nKV + g) * p.C;
+  const int qabs = seen + i;
+
+  for (int u = u0; u < u1; ++u) {
+    int first;
+    const bool chunk = ts.at(u, KTG, &first);
+    __syncthreads();
+    for (int e = tid; e < KTG * D; e += 256) {
+      const int kk = e / D, d = e % D;
+      const int col = first + kk;
+      float kv = 0.f, vv = 0.f;
+      if (chunk) {
+        if (col < p.C) {
+          kv = ld<T>(KN, (nbase + col) * D + d);
+          vv = ld<T>(VN, (nbase + col) * D + d);
+        }
+      } else if (col < gl.L) {
+        const int sl = slot_of(column_position(gl, col), p.cap, p.ring, p.sink);
+        kv = ld<T>(KC, (cbase + sl) * D + d);
+        vv = ld<T>(VC, (cbase + sl) * D + d);
+      }
+      Ks[e] = kv;
+      Vs[e] = vv;
+    }
+    __syncthreads();
+    const bool visible =
+        !EXPLICIT && tile_all_visible(chunk, first, KTG, gl, seen, p.C, i_min, i_last, p.window);
+    float t[KTG];
+    float m_tile = -INFINITY;
+#pragma unroll
+    for (int kk = 0; kk < KTG; ++kk) {
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < DPT; ++e) {
+        const int d = ql + 16 * e;
+        if (d < D) part = fmaf(q[e], Ks[kk * D + d], part);
+      }
+      part += __shfl_xor(part, 8, 16);
+      part += __shfl_xor(part, 4, 16);
+      part += __shfl_xor(part, 2, 16);
+      part += __shfl_xor(part, 1, 16);
+      const int col = first + kk;
+      float add;
+      if (EXPLICIT) {
+        const bool in = chunk ? col < p.C : col < gl.L;
+        if (!in) {
+          add = -INFINITY;
+        } else {
+          const int64_t mc = chunk ? static_cast<int64_t>(gl.L) + col : col;
+          add = row_ok ? p.mask[b * p.mbs + head * p.mhs + static_cast<int64_t>(i) * p.mld + mc]
+                       : 0.f;
+        }
+      } else if (visible) {
+        add = 0.f;
+      } else {
+        add = inkernel_add(chunk, col, gl, seen, p.C, nv, qabs, p.window, p.sink);
+      }
+      const float tv = add == -INFINITY ? -INFINITY : fmaf(part, p.sl2e, add * kLog2e);
+      t[kk] = tv;
+      m_tile = fmaxf(m_tile, tv);
+    }
+    const float m_new = fmaxf(m_run, m_tile);
+    // a row whose keys so far are all -inf keeps nothing: use 0 as reference
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int kk = 0; kk < KTG; ++kk) {
+      const float pk = __builtin_amdgcn_exp2f(t[kk] - m_use);
+      l_run += pk;
+#pragma unroll
+      for (int e = 0; e < DPT; ++e) {
+        const int d = ql + 16 * e;
+        if (d < D) acc[e] = fmaf(pk, Vs[kk * D + d], acc[e]);
+      }
+    }
+  }
+
+  if (!row_ok) return;
+  const size_t orow = (static_cast<size_t>(b) * p.H + head) * p.C + i;
+  const bool real = any_real && i < nv;
+  if (p.splits == 1) {
+    T *O = static_cast<T *>(p.out);
+    const float inv = real ? 1.f / l_run : 0.f;
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) {
+      const int d = ql + 16 * e;
+      if (d < D) st(O, orow * D + d, real ? acc[e] * inv : 0.f);
+    }
+  } else {
+    const size_t rows = static_cast<size_t>(p.B) * p.H * p.C;
+    float *WO = p.wo + (split * rows + orow) * D;
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) {
+      const int d = ql + 16 * e;
+      if (d < D) WO[d] = real ? acc[e] : 0.f;
+    }
+    if (ql == 0) {
+      float *ML = p.wml + (split * rows + orow) * 2;
+      ML[0] = real ? m_run : -INFINITY;
+      ML[1] = real ? l_run : 0.f;
+    }
+  }
+}
+
+// Merge key-split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+template <typename T>
+__global__ void __launch_bounds__(256) k_attn_combine(AttnParams p, int D) {
+  const size_t rows = static_cast<size_t>(p.B) * p.H * p.C;
+  const size_t total = rows * D;
+  T *O = static_cast<T *>(p.out);
+  for (size_t t = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; t < total;
+       t += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    const size_t row = t / D;
+    const int d = static_cast<int>(t % D);
+    const int i = static_cast<int>(row % p.C);
+    const int b = static_cast<int>(row / (static_cast<size_t>(p.H) * p.C));
+    const int nv = read_nvalid(p.n_valid, b, p.C, nullptr);
+    float res = 0.f;
+    if (i < nv) {
+      float M = -INFINITY;
+      for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.wml[(s * rows + row) * 2]);
+      float l = 0.f, o = 0.f;
+      if (M != -INFINITY) {
+        for (int s = 0; s < p.splits; ++s) {
+          const float ms = p.wml[(s * rows + row) * 2];
+          const float wgt = __builtin_amdgcn_exp2f(ms - M);
+          l = fmaf(wgt, p.wml[(s * rows + row) * 2 + 1], l);
+          o = fmaf(wgt, p.wo[(s * rows + row) * D + d], o);
+        }
+      }
+      res = l > 0.f ? o / l : 0.f;
+    }
+    st(O, t, res);
+  }
+}
+
+template <typename T, bool EXPLICIT>
+hipError_t launch_valu_t(const AttnParams &p, int D, hipStream_t s) {
+  const unsigned blocks = static_cast<unsigned>(p.qtiles) * p.hgroups * p.splits * p.B * p.nKV;
+  if (blocks == 0) return hipSuccess;
+  const size_t shm = 2 * KTG * static_cast<size_t>(D) * sizeof(float);
+  const int dpt = (D + 15) / 16;
+  if (dpt <= 1)
+    hipLaunchKernelGGL((k_attn_valu<T, 1, EXPLICIT>), dim3(blocks), dim3(256), shm, s, p, D);
+  else if (dpt <= 2)
+    hipLaunchKernelGGL((k_attn_valu<T, 2, EXPLICIT>), dim3(blocks), dim3(256), shm, s, p, D);
+  else if (dpt <= 4)
+    hipLaunchKernelGGL((k_attn_valu<T, 4, EXPLICIT>), dim3(blocks), dim3(256), shm, s, p, D);
+  else if (dpt <= 8)
+    hipLaunchKernelGGL((k_attn_valu<T, 8, EXPLICIT>), dim3(blocks), dim3(256), shm, s, p, D);
+  else
+    hipLaunchKernelGGL((k_attn_valu<T, 16, EXPLICIT>), dim3(blocks), dim3(256), shm, s, p, D);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_valu(const AttnParams &p, int D, int dtype, hipStream_t s) {
+  const bool ex = p.mask != nullptr;
+  if (dtype == CP_BF16)
+    return ex ? launch_valu_t<uint16_t, true>(p, D, s) : launch_valu_t<uint16_t, false>(p, D, s);
+  return ex ? launch_valu_t<float, true>(p, D, s) : launch_valu_t<float, false>(p, D, s);
+}
+
+hipError_t launch_attn_combine(const AttnParams &p, int D, int dtype, hipStream_t s) {
+  const size_t total = static_cast<size_t>(p.B) * p.H * p.C * D;
+  if (total == 0) return hipSuccess;
+  size_t blocks = (total + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  if (dtype == CP_BF16)
+    hipLaunchKernelGGL(k_attn_combine<uint16_t>, dim3(blocks), dim3(256), 0, s, p, D);
+  else
+    hipLaunchKernelGGL(k_attn_combine<float>, dim3(blocks), dim3(256), 0, s, p, D);
+  return hipGetLastError();
+}
+
+}  // namespace cp

@@ -1,0 +1,288 @@
+// cp_api.hip -- the extern "C" entry points of libcp (declared in cp.h).
+//
+// Host code only: argument validation (everything a host can check is
+// checked before anything is enqueued), the attention plan (kernel choice,
+// query tiling, key splits), and the launches.  No allocation, no global
+// mutable state, no stream synchronisation.
+#include <cmath>
+#include <cstdint>
+
+#include "attn_common.h"
+
+namespace cp {
+int mfma_keys_per_tile(int D);
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr int kNumCU = 256;
+
+int to_status(hipError_t e) { return e == hipSuccess ? CP_OK : CP_ERR_HIP; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t esize(int dtype) { return dtype == CP_BF16 ? 2 : 4; }
+
+int check_cache(const cp_cache *c) {
+  if (!c || !c->k || !c->v || !c->seen) return CP_ERR_ARG;
+  if (c->dtype != CP_F32 && c->dtype != CP_BF16) return CP_ERR_DTYPE;
+  if (c->reserved != 0 || (c->ring != 0 && c->ring != 1)) return CP_ERR_ARG;
+  if (c->B < 0 || c->nKV < 1 || c->cap < 1 || c->D < 1) return CP_ERR_SHAPE;
+  if (c->sink < 0 || c->sink >= c->cap) return CP_ERR_ARG;
+  return CP_OK;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace
+
+AttnPlan plan_attention(const cp_cache &c, const cp_attn_args &a, bool for_workspace) {
+  AttnPlan pl{};
+  const int G = a.H / c.nKV;
+  const bool aligned = aligned16(a.q) && aligned16(a.k_new) && aligned16(a.v_new) &&
+                       aligned16(a.out) && aligned16(c.k) && aligned16(c.v);
+  pl.mfma = c.dtype == CP_BF16 && (c.D == 64 || c.D == 128 || c.D == 256) && G <= 128 &&
+            !(a.flags & CP_ATTN_FORCE_GENERIC) && aligned;
+  int hgroups = 1;
+  if (pl.mfma) {
+    pl.qpos = 128 / G;
+    pl.kt = mfma_keys_per_tile(c.D);
+  } else {
+    const int hb = G < 16 ? G : 16;
+    hgroups = (G + hb - 1) / hb;
+    pl.qpos = 16 / hb;
+    pl.kt = 16;
+  }
+  pl.qtiles = (a.C + pl.qpos - 1) / pl.qpos;
+  pl.splits = 1;
+  const long base = static_cast<long>(pl.qtiles) * hgroups * c.B * c.nKV;
+  long keys = static_cast<long>(c.cap) + a.C;
+  if (a.window > 0 && !a.mask) {
+    const long wk = static_cast<long>(a.window) + pl.qpos + c.sink;
+    if (wk < keys) keys = wk;
+  }
+  const long tiles = (keys + pl.kt - 1) / pl.kt;
+  if (!(a.flags & CP_ATTN_NO_SPLIT) && base > 0 && base < kNumCU && tiles >= 4) {
+    long s = (2 * kNumCU + base - 1) / base;
+    if (s > tiles / 2) s = tiles / 2;
+    if (s > 64) s = 64;
+    pl.splits = s > 1 ? static_cast<int>(s) : 1;
+  }
+  if (pl.splits > 1 && !for_workspace &&
+      (!a.workspace || a.workspace_bytes < attn_workspace_bytes(c, a, pl)))
+    pl.splits = 1;
+  return pl;
+}
+
+size_t attn_workspace_bytes(const cp_cache &c, const cp_attn_args &a, const AttnPlan &p) {
+  if (p.splits <= 1) return 0;
+  const size_t rows = static_cast<size_t>(c.B) * a.H * a.C;
+  return round256(static_cast<size_t>(p.splits) * rows * c.D * sizeof(float)) +
+         round256(static_cast<size_t>(p.splits) * rows * 2 * sizeof(float));
+}
+
+hipError_t launch_attention(const cp_cache &c, const cp_attn_args &a, hipStream_t s) {
+  const AttnPlan pl = plan_attention(c, a, false);
+  AttnParams p{};
+  p.q = a.q;
+  p.kn = a.k_new;
+  p.vn = a.v_new;
+  p.kc = c.k;
+  p.vc = c.v;
+  p.out = a.out;
+  p.seen = c.seen;
+  p.n_valid = a.n_valid;
+  p.status = c.status;
+  p.mask = a.mask;
+  p.mld = a.mask_ld;
+  p.mhs = a.mask_head_stride;
+  p.mbs = a.mask_batch_stride;
+  p.B = c.B;
+  p.H = a.H;
+  p.nKV = c.nKV;
+  p.C = a.C;
+  p.cap = c.cap;
+  p.ring = c.ring;
+  p.sink = c.sink;
+  p.window = a.mask ? 0 : a.window;
+  p.G = a.H / c.nKV;
+  p.qpos = pl.qpos;
+  p.qtiles = pl.qtiles;
+  p.splits = pl.splits;
+  p.full_tiles = (a.flags & CP_ATTN_FULL_TILES) ? 1 : 0;
+  p.mask_vec4 = a.mask && aligned16(a.mask) && a.mask_ld % 4 == 0 && a.mask_head_stride % 4 == 0 &&
+                a.mask_batch_stride % 4 == 0;
+  p.sl2e = a.scale * kLog2e;
+  if (pl.splits > 1) {
+    const size_t rows = static_cast<size_t>(c.B) * a.H * a.C;
+    unsigned char *w = static_cast<unsigned char *>(a.workspace);
+    p.wo = reinterpret_cast<float *>(w);
+    p.wml = reinterpret_cast<float *>(
+        w + round256(static_cast<size_t>(pl.splits) * rows * c.D * sizeof(float)));
+  }
+  if (static_cast<size_t>(c.B) * a.H * a.C == 0) return hipSuccess;
+  hipError_t e;
+  if (pl.mfma) {
+    p.hb = p.G;
+    p.hgroups = 1;
+    e = launch_attn_mfma(p, c.D, s);
+  } else {
+    p.hb = p.G < 16 ? p.G : 16;
+    p.hgroups = (p.G + p.hb - 1) / p.hb;
+    e = launch_attn_valu(p, c.D, c.dtype, s);
+  }
+  if (e != hipSuccess || pl.splits == 1) return e;
+  return launch_attn_combine(p, c.D, c.dtype, s);
+}
+
+}  // namespace cp
+
+using namespace cp;
+
+extern "C" {
+
+const char *cp_status_str(int status) {
+  switch (status) {
+    case CP_OK:
+      return "ok";
+    case CP_ERR_ARG:
+      return "invalid argument (null pointer or out-of-range scalar)";
+    case CP_ERR_SHAPE:
+      return "unsupported or inconsistent shape";
+    case CP_ERR_DTYPE:
+      return "unsupported dtype";
+    case CP_ERR_WINDOW:
+      return "ring window too small for a padded append (cap <= C + sink)";
+    case CP_ERR_STATE:
+      return "rollback without a matching armed snapshot";
+    case CP_ERR_WORKSPACE:
+      return "workspace or snapshot buffer too small";
+    case CP_ERR_HIP:
+      return "HIP runtime error";
+    default:
+      return "unknown status";
+  }
+}
+
+int cp_abi_version(void) { return kAbiVersion; }
+
+size_t cp_struct_size(int which) {
+  switch (which) {
+    case 0:
+      return sizeof(cp_cache);
+    case 1:
+      return sizeof(cp_snapshot);
+    case 2:
+      return sizeof(cp_attn_args);
+    default:
+      return 0;
+  }
+}
+
+int cp_rope_chunk(const void *x, void *y, const float *cos, const float *sin, int B, int Hx,
+                  int C, int D, int Bt, int dtype, cp_stream_t stream) {
+  if (dtype != CP_F32 && dtype != CP_BF16) return CP_ERR_DTYPE;
+  if (B < 0 || Hx < 0 || C < 0 || D < 1) return CP_ERR_ARG;
+  if (D % 2 != 0) return CP_ERR_SHAPE;
+  if (Bt != 1 && Bt != B) return CP_ERR_ARG;
+  if (static_cast<size_t>(B) * Hx * C == 0) return CP_OK;  // empty: pointers may be NULL
+  if (!x || !y || !cos || !sin) return CP_ERR_ARG;
+  return to_status(launch_rope(x, y, cos, sin, B, Hx, C, D, Bt, dtype,
+                               static_cast<hipStream_t>(stream)));
+}
+
+int cp_kv_append(const cp_cache *cache, const void *k_new, const void *v_new, int C,
+                 const int32_t *n_rows, cp_stream_t stream) {
+  int st = check_cache(cache);
+  if (st != CP_OK) return st;
+  if (C < 0) return CP_ERR_ARG;
+  if (!cache->ring && C > cache->cap) return CP_ERR_SHAPE;
+  if (C == 0 || cache->B == 0) return CP_OK;  // nothing appended; pointers may be NULL
+  if (!k_new || !v_new) return CP_ERR_ARG;
+  return to_status(
+      launch_kv_append(*cache, k_new, v_new, C, n_rows, static_cast<hipStream_t>(stream)));
+}
+
+size_t cp_snapshot_bytes(const cp_cache *cache, int C) {
+  if (check_cache(cache) != CP_OK || C < 0) return 0;
+  return snapshot_header_bytes(cache->B) +
+         2 * round256(static_cast<size_t>(cache->B) * cache->nKV * C * cache->D *
+                      esize(cache->dtype));
+}
+
+int cp_kv_snapshot_padded_append(const cp_cache *cache, int C, const int32_t *n_valid,
+                                 cp_snapshot *snap, cp_stream_t stream) {
+  int st = check_cache(cache);
+  if (st != CP_OK) return st;
+  if (!snap || !snap->buf || C < 0) return CP_ERR_ARG;
+  if (cache->ring && cache->cap <= C + cache->sink) return CP_ERR_WINDOW;
+  if (!cache->ring && C > cache->cap) return CP_ERR_SHAPE;
+  if (snap->bytes < cp_snapshot_bytes(cache, C)) return CP_ERR_WORKSPACE;
+  st = to_status(launch_snapshot(*cache, C, n_valid, snap->buf, static_cast<hipStream_t>(stream)));
+  if (st != CP_OK) return st;
+  snap->cache_k = cache->k;
+  snap->C = C;
+  snap->armed = 1;
+  return CP_OK;
+}
+
+int cp_kv_rollback_padded_append(const cp_cache *cache, cp_snapshot *snap, cp_stream_t stream) {
+  int st = check_cache(cache);
+  if (st != CP_OK) return st;
+  if (!snap || !snap->buf) return CP_ERR_ARG;
+  if (!snap->armed || snap->cache_k != cache->k || snap->C < 0) return CP_ERR_STATE;
+  if (snap->bytes < cp_snapshot_bytes(cache, snap->C)) return CP_ERR_STATE;
+  st = to_status(launch_rollback(*cache, snap->C, snap->buf, static_cast<hipStream_t>(stream)));
+  if (st != CP_OK) return st;
+  snap->armed = 0;
+  return CP_OK;
+}
+
+static int check_attn(const cp_cache *cache, const cp_attn_args *a) {
+  int st = check_cache(cache);
+  if (st != CP_OK) return st;
+  if (!a) return CP_ERR_ARG;
+  const bool empty = static_cast<size_t>(cache->B) * a->C == 0;
+  if (!empty && (!a->q || !a->k_new || !a->v_new || !a->out)) return CP_ERR_ARG;
+  if (a->reserved != 0 || a->C < 0 || a->window < 0 || !std::isfinite(a->scale)) return CP_ERR_ARG;
+  if (a->H < 1 || a->H % cache->nKV != 0) return CP_ERR_SHAPE;
+  if (cache->D > 256) return CP_ERR_SHAPE;
+  if (!cache->ring && a->C > cache->cap) return CP_ERR_SHAPE;
+  if (a->mask && (a->mask_ld < a->C || a->mask_head_stride < 0 || a->mask_batch_stride < 0))
+    return CP_ERR_ARG;
+  return CP_OK;
+}
+
+size_t cp_attn_workspace_bytes(const cp_cache *cache, const cp_attn_args *args) {
+  if (check_attn(cache, args) != CP_OK) return 0;
+  return attn_workspace_bytes(*cache, *args, plan_attention(*cache, *args, true));
+}
+
+int cp_attn_chunk_with_past(const cp_cache *cache, const cp_attn_args *args, cp_stream_t stream) {
+  const int st = check_attn(cache, args);
+  if (st != CP_OK) return st;
+  return to_status(launch_attention(*cache, *args, static_cast<hipStream_t>(stream)));
+}
+
+int cp_build_mask(float *mask, int64_t ld, const cp_cache *cache, const int32_t *n_valid, int H,
+                  int C, int window, cp_stream_t stream) {
+  const int st = check_cache(cache);
+  if (st != CP_OK) return st;
+  if (ld < 0 || H < 1 || C < 0 || window < 0) return CP_ERR_ARG;
+  if (static_cast<size_t>(cache->B) * C * ld == 0) return CP_OK;
+  if (!mask) return CP_ERR_ARG;
+  return to_status(
+      launch_build_mask(mask, ld, *cache, n_valid, H, C, window, static_cast<hipStream_t>(stream)));
+}
+
+int cp_select_row(const void *x, void *y, const int32_t *idx, int offset, int B, int H, int C,
+                  int D, int dtype, cp_stream_t stream) {
+  if (dtype != CP_F32 && dtype != CP_BF16) return CP_ERR_DTYPE;
+  if (B < 0 || H < 0 || C < 0 || D < 1) return CP_ERR_ARG;
+  if (static_cast<size_t>(B) * H == 0) return CP_OK;
+  if (!y || !idx || (C > 0 && !x)) return CP_ERR_ARG;
+  return to_status(
+      launch_select(x, y, idx, offset, B, H, C, D, dtype, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+// cp_common.h -- internal helpers shared by the libcp HIP sources (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cp.h"
+
+namespace cp {
+
+constexpr float kMasked = -1e30f;  // additive value of a masked score
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- bf16 bits
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// ------------------------------------------------------------- cache layout
+
+// Geometry of one sequence's cache after `seen` positions were absorbed.
+struct Live {
+  int L;    // live rows
+  int ns;   // live sink rows (columns [0, ns) are positions [0, ns))
+  int lo;   // first live non-sink position; column c >= ns is position lo + (c - ns)
+};
+
+__device__ __forceinline__ Live live_geometry(int seen, int cap, int ring, int sink) {
+  Live g;
+  if (!ring) {
+    g.L = seen;
+    g.ns = 0;
+    g.lo = 0;
+    return g;
+  }
+  const int R = cap - sink;
+  g.ns = seen < sink ? seen : sink;
+  g.lo = seen - R > sink ? seen - R : sink;
+  g.L = g.ns + (seen > g.lo ? seen - g.lo : 0);
+  return g;
+}
+
+// Absolute position of past column c (chronological order of live rows).
+__device__ __forceinline__ int column_position(const Live &g, int c) {
+  return c < g.ns ? c : g.lo + (c - g.ns);
+}
+
+// Physical slot of absolute position p.
+__device__ __forceinline__ int slot_of(int p, int cap, int ring, int sink) {
+  if (!ring || p < cap) return p;
+  return sink + (p - sink) % (cap - sink);
+}
+
+// In-kernel attend rule: causal, real key, inside the window or a sink row.
+__device__ __forceinline__ bool attend(int qpos, int kpos, bool key_real, int window, int sink) {
+  if (!key_real || kpos > qpos) return false;
+  return window == 0 || qpos - kpos < window || kpos < sink;
+}
+
+__device__ __forceinline__ void flag(int32_t *status, int bits) {
+  if (status) atomicOr(status, bits);
+}
+
+// Reads n_valid[b] (or C when absent), clamped to [0, C].
+__device__ __forceinline__ int read_nvalid(const int32_t *n_valid, int b, int C, int32_t *status) {
+  if (!n_valid) return C;
+  int nv = n_valid[b];
+  if (nv < 0 || nv > C) {
+    flag(status, CP_DEV_NVALID);
+    nv = nv < 0 ? 0 : C;
+  }
+  return nv;
+}
+
+// --------------------------------------------------------- host launchers
+
+hipError_t launch_rope(const void *x, void *y, const float *cos, const float *sin, int B, int Hx,
+                       int C, int D, int Bt, int dtype, hipStream_t s);
+hipError_t launch_kv_append(const cp_cache &c, const void *k_new, const void *v_new, int C,
+                            const int32_t *n_rows, hipStream_t s);
+hipError_t launch_snapshot(const cp_cache &c, int C, const int32_t *n_valid, void *buf,
+                           hipStream_t s);
+hipError_t launch_rollback(const cp_cache &c, int C, const void *buf, hipStream_t s);
+hipError_t launch_build_mask(float *mask, int64_t ld, const cp_cache &c, const int32_t *n_valid,
+                             int H, int C, int window, hipStream_t s);
+hipError_t launch_select(const void *x, void *y, const int32_t *idx, int off, int B, int H, int C,
+                         int D, int dtype, hipStream_t s);
+
+// Snapshot buffer layout: header of 2*B int32 (seen_before, n_valid) padded to
+// 256 bytes, then K rows [B][nKV][C][D], then V rows of the same shape.
+inline size_t snapshot_header_bytes(int B) {
+  size_t h = sizeof(int32_t) * 2 * static_cast<size_t>(B);
+  return (h + 255) & ~static_cast<size_t>(255);
+}
+
+// Attention plan chosen on the host.
+struct AttnPlan {
+  bool mfma;      // bf16 matrix-core kernel, else the vector-ALU kernel
+  int splits;     // key splits (1 = direct output)
+  int qtiles;     // query tiles per (b, kv head)
+  int qpos;       // chunk rows per query tile
+  int kt;         // keys per tile
+};
+
+AttnPlan plan_attention(const cp_cache &c, const cp_attn_args &a, bool for_workspace);
+size_t attn_workspace_bytes(const cp_cache &c, const cp_attn_args &a, const AttnPlan &p);
+hipError_t launch_attention(const cp_cache &c, const cp_attn_args &a, hipStream_t s);
+
+}  // namespace cp

@@ -1,0 +1,296 @@
+/*
+ * cp.h -- C ABI of libcp: chunked prefill with past on MI355X (gfx950).
+ *
+ * One transformer layer's hot path for a chunk of C prompt tokens padded to
+ * a fixed C, against an external KV cache:
+ *
+ *   cp_rope_chunk (Q)  -> cp_rope_chunk (K) -> [cp_kv_snapshot_padded_append]
+ *   -> cp_attn_chunk_with_past -> cp_kv_append -> [cp_kv_rollback_padded_append]
+ *   -> cp_select_row
+ *
+ * Sources:
+ *   [SKaiNET] SKaiNET-transformers PR #417, "functiongemma: chunk prefill-with-
+ *             past graph gemma_prefill_with_past", section "Change (additive)":
+ *             heads-first [heads, C, headDim] tensors, RoPE from per-position
+ *             [C, headDim] cos/sin tables, attention over past + C keys with an
+ *             additive per-head mask [1, nHeads, C, past+C] (0 attends, -1e30
+ *             masks; it carries the causal band, the zero padding and the
+ *             sliding window), K/V extended by the chunk, one selected row;
+ *             section "Validation": select on row 51 of a 52-token chunk.
+ *   [TICO]    Samsung/TICO issue #586, "Enable prefill-decode modeling",
+ *             sections "Runtime behavior" and "Mask/cache layout used in the
+ *             runtime": the KV cache is owned by the runtime, outside the
+ *             graph; past tokens packed in the first past_len slots; the
+ *             runtime writes the delta K/V into the external cache.
+ *   [cactus]  cactus PR #716, "Pad the chunked-prefill tail for sliding-window
+ *             models", section "Fix" and the review hardening: sliding caches
+ *             evict chronologically; a padded append over-evicts up to
+ *             pad_count of the oldest window rows; snapshot/rollback of a
+ *             padded append leaves the cache byte-identical to an unpadded
+ *             prefill; windows with window <= chunk + sink are rejected; bytes
+ *             beyond the live length are a dead region no consumer reads.
+ *
+ * Conventions (all entry points):
+ *   - Every data pointer is DEVICE memory owned by the caller.  The library
+ *     allocates nothing, frees nothing, keeps no global mutable state and
+ *     never synchronises the stream.  `stream` is a hipStream_t passed as an
+ *     opaque pointer (NULL = the default stream); all work is enqueued on it.
+ *   - Tensors are dense, row-major, last dimension contiguous.  Storage
+ *     dtypes: CP_F32 (float) or CP_BF16 (bfloat16 bit patterns).
+ *   - Empty work (a zero extent) is a no-op that returns CP_OK; the data
+ *     pointers of empty tensors may then be NULL.
+ *   - Return value: CP_OK (0) or a negative CP_ERR_* code.  Every error a
+ *     host can detect (null pointers, bad shapes, dtypes, window guard,
+ *     snapshot state, workspace size) is detected before anything is
+ *     enqueued, so a failing call has no effect.  Values that live on the
+ *     device (seen, n_valid) are checked by the kernels: they never read or
+ *     write out of bounds, skip or clamp the offending sequence, and OR a
+ *     CP_DEV_* bit into cache->status when that pointer is non-NULL.
+ *   - Calls on one stream are ordered; calls that touch the same cache on
+ *     different streams must be ordered by the caller.
+ */
+#ifndef CP_H
+#define CP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *cp_stream_t; /* hipStream_t */
+
+/* ---- status codes returned by every entry point ---- */
+#define CP_OK 0
+#define CP_ERR_ARG (-1)       /* null pointer or out-of-range scalar argument */
+#define CP_ERR_SHAPE (-2)     /* unsupported or inconsistent shape (D odd, H % nKV, C > cap, ...) */
+#define CP_ERR_DTYPE (-3)     /* dtype not CP_F32 / CP_BF16, or not supported by the call */
+#define CP_ERR_WINDOW (-4)    /* ring with cap <= C + sink cannot take a padded append */
+#define CP_ERR_STATE (-5)     /* rollback without a matching, armed snapshot */
+#define CP_ERR_WORKSPACE (-6) /* workspace or snapshot buffer too small */
+#define CP_ERR_HIP (-7)       /* the HIP runtime refused a launch */
+
+/* ---- bits the kernels OR into cache->status (device int32) ---- */
+#define CP_DEV_OVERFLOW 1 /* global append would pass cap: that sequence was not appended */
+#define CP_DEV_NVALID 2   /* n_valid / n_rows outside [0, C]: clamped */
+#define CP_DEV_MASK_LD 4  /* explicit mask narrower than live past + C: rows written as 0 */
+#define CP_DEV_ROLLBACK 8 /* rollback on a sequence that did not take exactly C rows */
+#define CP_DEV_SEEN 16    /* seen negative, or above cap for a global cache: sequence skipped */
+
+/* ---- storage dtypes ---- */
+#define CP_F32 0
+#define CP_BF16 1
+
+/*
+ * External KV cache of one layer ([TICO] "Mask/cache layout"; [cactus] "Fix").
+ *
+ *   k, v    [B, nKV, cap, D] storage dtype.  Global cache (ring = 0): absolute
+ *           position p lives in slot p, p < cap.  Sliding ring (ring = 1):
+ *           `sink` pinned slots hold positions 0..sink-1; position p >= sink
+ *           lives in slot sink + (p - sink) mod (cap - sink), so appending
+ *           evicts the oldest non-sink row.  Slots that hold no live row are
+ *           the dead region: never read, contents unspecified.
+ *   seen    device int32 [B]: positions absorbed so far by each sequence.
+ *           Live rows: global [0, seen); ring the sink rows below
+ *           min(sink, seen) and positions [max(sink, seen - (cap - sink)), seen).
+ *   status  device int32 or NULL: sticky CP_DEV_* error bits.
+ *   sink    pinned rows of a ring (0 for none); they are never evicted and are
+ *           attended regardless of the window.
+ */
+typedef struct cp_cache {
+  void *k;
+  void *v;
+  int32_t *seen;
+  int32_t *status;
+  int32_t B, nKV, cap, D;
+  int32_t dtype;
+  int32_t ring;
+  int32_t sink;
+  int32_t reserved; /* must be 0 */
+} cp_cache;
+
+/*
+ * Snapshot of the rows a padded ring append would over-evict ([cactus]
+ * "Fix": snapshot_cache_padded_append / rollback_cache_padded_append).
+ * `buf` is a caller-owned device buffer of at least cp_snapshot_bytes()
+ * bytes.  The other fields are filled by cp_kv_snapshot_padded_append and
+ * consumed by cp_kv_rollback_padded_append; initialise them to zero.
+ */
+typedef struct cp_snapshot {
+  void *buf;
+  size_t bytes;
+  const void *cache_k; /* identity of the cache the snapshot was taken from */
+  int32_t C;
+  int32_t armed; /* 1 between a snapshot and its rollback */
+} cp_snapshot;
+
+/*
+ * Arguments of the chunk attention ([SKaiNET] "Change (additive)":
+ * attnWithPastChunk).
+ *
+ *   q          [B, H, C, D]   queries, RoPE already applied
+ *   k_new      [B, nKV, C, D] the chunk's keys, RoPE already applied
+ *   v_new      [B, nKV, C, D] the chunk's values
+ *   out        [B, H, C, D]   output, storage dtype; pad rows written as 0
+ *   n_valid    device int32 [B] real rows per sequence (rows >= n_valid are
+ *              padding), or NULL when all C rows are real
+ *   mask       NULL: the mask is computed in the kernel from seen, n_valid,
+ *              window and sink (causal inside the chunk, pad keys masked,
+ *              sliding window of `window` positions counting the query).
+ *              Otherwise an explicit fp32 additive mask: element (b, h, i, col)
+ *              at mask[b*mask_batch_stride + h*mask_head_stride + i*mask_ld
+ *              + col]; columns are the live past rows in chronological order
+ *              then the C chunk rows; mask_ld >= live past + C (a sequence
+ *              that violates this is flagged CP_DEV_MASK_LD and zeroed).
+ *              A head stride of 0 broadcasts one mask over the heads.
+ *   workspace  optional device scratch for the key-split path; size from
+ *              cp_attn_workspace_bytes().  With less, the call runs unsplit.
+ *   H          query heads (multiple of cache->nKV; head h reads KV head
+ *              h / (H / nKV))
+ *   C          chunk rows
+ *   window     sliding window in positions (0 = none); in-kernel mask only
+ *   scale      softmax scale applied to q.k before the mask is added
+ *   flags      CP_ATTN_* below
+ *
+ * The cache is read as it stands BEFORE the chunk is appended.
+ */
+typedef struct cp_attn_args {
+  const void *q;
+  const void *k_new;
+  const void *v_new;
+  void *out;
+  const int32_t *n_valid;
+  const float *mask;
+  int64_t mask_ld;
+  int64_t mask_head_stride;
+  int64_t mask_batch_stride;
+  void *workspace;
+  size_t workspace_bytes;
+  int32_t H;
+  int32_t C;
+  int32_t window;
+  float scale;
+  uint32_t flags;
+  int32_t reserved; /* must be 0 */
+} cp_attn_args;
+
+#define CP_ATTN_NO_SPLIT 1u      /* one pass per query tile, no key split */
+#define CP_ATTN_FORCE_GENERIC 2u /* use the vector-ALU kernel even for bf16 */
+#define CP_ATTN_FULL_TILES 4u    /* visit every key tile (no window skipping) */
+
+/* ---- introspection ---- */
+
+/* Text of a CP_OK / CP_ERR_* code. */
+const char *cp_status_str(int status);
+
+/* ABI version of this header (bumped on any layout change). */
+int cp_abi_version(void);
+
+/* sizeof of the ABI structs: which = 0 cp_cache, 1 cp_snapshot, 2 cp_attn_args. */
+size_t cp_struct_size(int which);
+
+/* ---- RoPE ---- */
+
+/*
+ * Rotary embedding from caller-supplied per-position tables ([SKaiNET]
+ * "Change (additive)"; [TICO] "Runtime behavior": (cos_t, sin_t) at the
+ * absolute position).  Half-split pairing, j < D/2:
+ *   y[j]     = x[j]     * cos[j]     - x[j+D/2] * sin[j]
+ *   y[j+D/2] = x[j+D/2] * cos[j+D/2] + x[j]     * sin[j+D/2]
+ * evaluated in fp64 on the exact fp32 operands, rounded to fp32, then to
+ * the storage dtype (bf16: round to nearest even).
+ *
+ *   x, y   [B, Hx, C, D] storage dtype; y may equal x (in place)
+ *   cos, sin  fp32 [Bt, C, D]; Bt = 1 shares one table over the batch,
+ *          Bt = B gives each sequence its own positions
+ * Errors: CP_ERR_ARG (null, negative sizes, Bt not 1 or B),
+ *         CP_ERR_SHAPE (D odd), CP_ERR_DTYPE.
+ */
+int cp_rope_chunk(const void *x, void *y, const float *cos, const float *sin, int B, int Hx,
+                  int C, int D, int Bt, int dtype, cp_stream_t stream);
+
+/* ---- KV cache ---- */
+
+/*
+ * Append rows [0, n_rows[b]) of the chunk's K/V at positions seen[b],
+ * seen[b] + 1, ... and advance seen[b] by n_rows[b] ([SKaiNET] K/V extended
+ * by the chunk; [TICO] runtime writes the delta K/V; [cactus] chronological
+ * eviction for a ring).  n_rows == NULL appends all C rows (the static
+ * padded append).  Bit-exact row copies.
+ *
+ *   k_new, v_new  [B, nKV, C, D] storage dtype (k_new already rotated)
+ * Device checks: a global sequence with seen + n > cap is skipped
+ * (CP_DEV_OVERFLOW); n outside [0, C] is clamped (CP_DEV_NVALID).
+ * Errors: CP_ERR_ARG, CP_ERR_SHAPE, CP_ERR_DTYPE.
+ */
+int cp_kv_append(const cp_cache *cache, const void *k_new, const void *v_new, int C,
+                 const int32_t *n_rows, cp_stream_t stream);
+
+/* Bytes a snapshot of a C-row padded append of `cache` needs (0 on bad args). */
+size_t cp_snapshot_bytes(const cp_cache *cache, int C);
+
+/*
+ * Before a padded append of C rows (n_valid[b] real): save, per sequence,
+ * the rows the padded append evicts but an exact append of n_valid rows
+ * would keep -- positions [max(sink, seen+n_valid-R), max(sink, seen+C-R)),
+ * R = cap - sink, at most C - n_valid rows -- and record seen and n_valid.
+ * A global cache saves no rows (its pad rows land in the dead region).
+ * Errors: CP_ERR_WINDOW for a ring with cap <= C + sink (nothing enqueued),
+ *         CP_ERR_WORKSPACE if snap->bytes < cp_snapshot_bytes(), CP_ERR_ARG,
+ *         CP_ERR_SHAPE.
+ */
+int cp_kv_snapshot_padded_append(const cp_cache *cache, int C, const int32_t *n_valid,
+                                 cp_snapshot *snap, cp_stream_t stream);
+
+/*
+ * After the padded append: write the saved rows back to their slots and set
+ * seen = seen_before + n_valid, so the live region is byte-identical to an
+ * exact append of the n_valid real rows.  Pad rows left in slots that are
+ * not live are dead region.  A sequence whose seen is not seen_before + C
+ * is left alone and flagged CP_DEV_ROLLBACK.
+ * Errors: CP_ERR_STATE (snapshot not armed, taken from another cache, or
+ *         for another C), CP_ERR_ARG.
+ */
+int cp_kv_rollback_padded_append(const cp_cache *cache, cp_snapshot *snap, cp_stream_t stream);
+
+/* ---- attention ---- */
+
+/* Workspace bytes that let cp_attn_chunk_with_past split keys (0 if never). */
+size_t cp_attn_workspace_bytes(const cp_cache *cache, const cp_attn_args *args);
+
+/*
+ * Grouped-query attention of the chunk over the live past plus the C chunk
+ * keys, softmax(scale * q.k + mask) v, fp32 accumulation (bf16 matrix
+ * cores for CP_BF16).  See cp_attn_args.
+ * Errors: CP_ERR_ARG, CP_ERR_SHAPE (H % nKV, D not in {64, 128, 256} for
+ *         bf16 or D > 256, C < 0), CP_ERR_DTYPE, CP_ERR_HIP.
+ */
+int cp_attn_chunk_with_past(const cp_cache *cache, const cp_attn_args *args, cp_stream_t stream);
+
+/*
+ * Materialise the explicit mask from the in-kernel rule ([SKaiNET] mask
+ * layout [B, H, C, ld]; 0 attends, -1e30 masks; columns past live + C are
+ * masked).  n_valid may be NULL (all rows real).
+ * Errors: CP_ERR_ARG, CP_ERR_SHAPE.
+ */
+int cp_build_mask(float *mask, int64_t ld, const cp_cache *cache, const int32_t *n_valid, int H,
+                  int C, int window, cp_stream_t stream);
+
+/* ---- row selection ---- */
+
+/*
+ * y[b, h, :] = x[b, h, idx[b] + offset, :] ([SKaiNET] one-hot selected row;
+ * "Validation": row 51 = last real row).  Pass n_valid with offset -1 for
+ * the last real row.  Rows outside [0, C) give zeros.
+ *   x [B, H, C, D], y [B, H, D], idx device int32 [B].
+ * Errors: CP_ERR_ARG, CP_ERR_DTYPE.
+ */
+int cp_select_row(const void *x, void *y, const int32_t *idx, int offset, int B, int H, int C,
+                  int D, int dtype, cp_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CP_H */

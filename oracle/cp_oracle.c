@@ -369,12 +369,14 @@ int orc_build_mask(float *mask, const int32_t *seen, const int32_t *n_valid, int
  * element (b, h, i, col) is at mask[b*mbs + h*mhs + i*mld + col].
  *
  * q: [B, H, C, D]; kn, vn: [B, nKV, C, D]; kc, vc: [B, nKV, cap, D], all in
- * the storage dtype.  out: [B, H, C, D] fp64.
+ * the storage dtype.  out: [B, H, C, D] fp64.  rows (optional, [C] bytes):
+ * compute only chunk rows i with rows[i] != 0 (others are written as zeros),
+ * so that single rows of a large workload can be checked one by one.
  */
 int orc_attn(const void *q, const void *kn, const void *vn, const void *kc, const void *vc,
              const int32_t *seen, const int32_t *n_valid, const float *mask, long mld, long mhs,
              long mbs, int B, int H, int nKV, int C, int D, int cap, int ring, int sink, int window,
-             float scale, int dtype, double *out) {
+             float scale, int dtype, const uint8_t *rows, double *out) {
   if (!q || !kn || !vn || !kc || !vc || !seen || !out) return ORC_EARG;
   if (B < 0 || H <= 0 || nKV <= 0 || H % nKV || C < 0 || D <= 0 || cap <= 0) return ORC_EARG;
   const int G = H / nKV;
@@ -427,7 +429,7 @@ int orc_attn(const void *q, const void *kn, const void *vn, const void *kc, cons
       const size_t nbase = ((size_t)b * nKV + g) * (size_t)C;
       for (int i = 0; i < C; ++i) {
         double *o = out + (((size_t)b * H + h) * C + i) * (size_t)D;
-        if (i >= nv) {
+        if (i >= nv || (rows && !rows[i])) {
           for (int d = 0; d < D; ++d) o[d] = 0.0;
           continue;
         }

@@ -35,7 +35,7 @@ def lib():
         L.orc_build_mask.argtypes = [vp, i32p, i32p, ip, ip, ip, ctypes.c_long, ip, ip, ip, ip]
         L.orc_attn.argtypes = [vp, vp, vp, vp, vp, i32p, i32p, vp, ctypes.c_long, ctypes.c_long,
                                ctypes.c_long, ip, ip, ip, ip, ip, ip, ip, ip, ip, ctypes.c_float,
-                               ip, vp]
+                               ip, vp, vp]
         L.orc_select_row.argtypes = [vp, vp, i32p, ip, ip, ip, ip, ip]
         for f in ("orc_rope", "orc_slot", "orc_live_positions", "orc_kv_append",
                   "orc_padded_overevicted", "orc_build_mask", "orc_attn", "orc_select_row",
@@ -130,8 +130,11 @@ def build_mask(seen, n_valid, H, C, ld, cap, ring=0, sink=0, window=0):
     return m
 
 
-def attn(q, kn, vn, kc, vc, seen, n_valid=None, mask=None, ring=0, sink=0, window=0, scale=None):
-    """Attention of the chunk over past + C keys; returns fp64 [B,H,C,D]."""
+def attn(q, kn, vn, kc, vc, seen, n_valid=None, mask=None, ring=0, sink=0, window=0, scale=None,
+         rows=None):
+    """Attention of the chunk over past + C keys; returns fp64 [B,H,C,D].
+
+    rows: optional iterable of chunk rows to compute (the others are zeros)."""
     q, kn, vn, kc, vc = _c(q), _c(kn), _c(vn), _c(kc), _c(vc)
     seen = _c(seen, np.int32)
     n_valid = _c(n_valid, np.int32)
@@ -147,11 +150,15 @@ def attn(q, kn, vn, kc, vc, seen, n_valid=None, mask=None, ring=0, sink=0, windo
         mld = mask.shape[3]
         mhs = mld * C if mask.shape[1] == H else 0
         mbs = mask.shape[1] * C * mld if mask.shape[0] == B else 0
+    sel = None
+    if rows is not None:
+        sel = np.zeros(C, dtype=np.uint8)
+        sel[np.asarray(list(rows), dtype=np.int64)] = 1
     out = np.zeros((B, H, C, D), dtype=np.float64)
     _check(lib().orc_attn(_ptr(q), _ptr(kn), _ptr(vn), _ptr(kc), _ptr(vc), _ptr(seen),
                           _ptr(n_valid), _ptr(mask), mld, mhs, mbs, B, H, nKV, C, D, cap,
                           int(ring), int(sink), int(window), float(scale), _dtype_code(q),
-                          _ptr(out)), "attn")
+                          _ptr(sel), _ptr(out)), "attn")
     return out
 
 

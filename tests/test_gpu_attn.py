@@ -1,0 +1,253 @@
+"""GPU parity of the chunk attention (HIP path through the C ABI vs the CPU oracle).
+
+Tolerance: max over real rows of max_d |out - ref| / max_d |ref| <= 1e-4 (fp32
+storage) or 2e-2 (bf16 storage, fp32 accumulation), ref = the oracle's fp64
+result.  Identities the kernels must keep exactly (explicit vs in-kernel
+mask on one key partition, determinism, selection) are checked bitwise.
+"""
+import numpy as np
+import pytest
+import torch
+
+from chunked_prefill_attention_rope_amd import inputs as I
+from oracle import oracle as O
+from tests.gpu_helpers import TOL, bits, dev, real_rows_mask, rowwise_rel_err, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def cp():
+    from chunked_prefill_attention_rope_amd import cp as mod
+    return mod
+
+
+def _np(t):
+    return I.np_view(t)
+
+
+def _setup(cp, cfg, nan_dead=True):
+    t = I.make_layer(cfg, nan_dead=nan_dead)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cache = cp.KVCache(dev(t["kc"]), dev(t["vc"]), dev(t["seen"]), ring=cfg.ring, sink=cfg.sink,
+                       status=status)
+    return t, cache, status
+
+
+def _run(cp, cfg, t, cache, explicit=False, flags=0, workspace=True):
+    q, k, v = dev(t["q"]), dev(t["k"]), dev(t["v"])
+    nv = dev(t["n_valid"])
+    mask = None
+    if explicit:
+        mask = cp.build_mask(cache, nv, cfg.H, cfg.C, cfg.mask_ld(), window=cfg.window)
+    ws = None
+    if workspace:
+        nb = cp.attn_workspace_bytes(cache, q, k, v, mask=mask, window=cfg.window, flags=flags)
+        if nb:
+            ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    out = cp.attn_chunk_with_past(cache, q, k, v, n_valid=nv, mask=mask,
+                                  window=0 if explicit else cfg.window, scale=cfg.scale,
+                                  workspace=ws, flags=flags)
+    torch.cuda.synchronize()
+    return out, mask
+
+
+def _oracle(cfg, t, rows=None):
+    return O.attn(_np(t["q"]), _np(t["k"]), _np(t["v"]), _np(t["kc"]), _np(t["vc"]),
+                  _np(t["seen"]), _np(t["n_valid"]), None, cfg.ring, cfg.sink, cfg.window,
+                  cfg.scale, rows=rows)
+
+
+def _check(cfg, out, ref, rows=None):
+    got = to_f64(out)
+    m = real_rows_mask(cfg, got.shape)
+    if rows is not None:
+        keep = np.zeros(cfg.C, dtype=bool)
+        keep[list(rows)] = True
+        m &= keep[None, None, :]
+    err = rowwise_rel_err(got, ref, m)
+    assert np.isfinite(got[m]).all()
+    # pad rows are written as zeros
+    assert (got[~real_rows_mask(cfg, got.shape)] == 0).all()
+    assert err <= TOL[cfg.dtype], err
+    return err
+
+
+SMALL = [
+    dict(name="gqa4_d64", dtype=I.BF16, B=2, H=8, nKV=2, D=64, C=40, cap=200, seen=[0, 131],
+         n_valid=[40, 23]),
+    dict(name="gqa4_d128", dtype=I.BF16, B=2, H=8, nKV=2, D=128, C=70, cap=400, seen=[65, 300],
+         n_valid=[70, 1]),
+    dict(name="gqa8_d256_ring", dtype=I.BF16, B=1, H=8, nKV=1, D=256, C=48, cap=96, ring=1,
+         window=96, seen=[250], n_valid=[47]),
+    dict(name="gqa2_d128_window", dtype=I.BF16, B=2, H=4, nKV=2, D=128, C=64, cap=256, window=50,
+         seen=[100, 30], n_valid=[64, 60]),
+    dict(name="ring_sink", dtype=I.BF16, B=2, H=4, nKV=1, D=128, C=32, cap=80, ring=1, sink=4,
+         window=70, seen=[3, 400], n_valid=[32, 29]),
+    dict(name="gqa3_d64", dtype=I.BF16, B=1, H=6, nKV=2, D=64, C=33, cap=128, seen=[77],
+         n_valid=[30]),
+    dict(name="mha_d128", dtype=I.BF16, B=1, H=2, nKV=2, D=128, C=130, cap=300, seen=[100],
+         n_valid=[129]),
+    dict(name="fp32_d64", dtype=I.F32, B=2, H=4, nKV=1, D=64, C=16, cap=64, seen=[48, 20],
+         n_valid=[11, 16]),
+    dict(name="fp32_d128_ring", dtype=I.F32, B=1, H=4, nKV=2, D=128, C=24, cap=64, ring=1,
+         window=64, seen=[150], n_valid=[20]),
+    dict(name="odd_d40", dtype=I.BF16, B=1, H=4, nKV=1, D=40, C=12, cap=50, seen=[9],
+         n_valid=[12]),
+]
+
+
+@pytest.mark.parametrize("kw", SMALL, ids=lambda c: c["name"])
+@pytest.mark.parametrize("mode", ["inkernel", "explicit"])
+@pytest.mark.parametrize("kernel", ["auto", "generic"])
+@pytest.mark.parametrize("split", ["split", "nosplit"])
+def test_attention_matches_oracle(cp, kw, mode, kernel, split):
+    kw = dict(kw)
+    kw.pop("name")
+    cfg = I.small(**kw)
+    t, cache, status = _setup(cp, cfg)
+    flags = (cp.ATTN_FORCE_GENERIC if kernel == "generic" else 0) | (
+        cp.ATTN_NO_SPLIT if split == "nosplit" else 0)
+    out, _ = _run(cp, cfg, t, cache, explicit=(mode == "explicit"), flags=flags)
+    ref = _oracle(cfg, t)
+    _check(cfg, out, ref)
+    assert int(status.item()) == 0
+
+
+@pytest.mark.parametrize("kw", SMALL[:6], ids=lambda c: c["name"])
+@pytest.mark.parametrize("kernel", [0, 2])
+def test_explicit_mask_equals_inkernel_bitwise(cp, kw, kernel):
+    """With the same key partition (no split), the explicit mask built from the rule and
+    the in-kernel rule give identical outputs: masked terms are exact zeros."""
+    kw = dict(kw)
+    kw.pop("name")
+    cfg = I.small(**kw)
+    t, cache, _ = _setup(cp, cfg)
+    flags = cp.ATTN_NO_SPLIT | kernel
+    a, _ = _run(cp, cfg, t, cache, explicit=True, flags=flags)
+    b, _ = _run(cp, cfg, t, cache, explicit=False, flags=flags)
+    # compare values (+0 and -0 count as equal)
+    assert torch.equal(a.float(), b.float())
+
+
+@pytest.mark.parametrize("kw", SMALL[:5], ids=lambda c: c["name"])
+def test_run_twice_is_deterministic(cp, kw):
+    kw = dict(kw)
+    kw.pop("name")
+    cfg = I.small(**kw)
+    t, cache, _ = _setup(cp, cfg)
+    a, _ = _run(cp, cfg, t, cache)
+    b, _ = _run(cp, cfg, t, cache)
+    np.testing.assert_array_equal(bits(a), bits(b))
+
+
+def test_padded_equals_unpadded_on_real_rows(cp):
+    """[cactus] "Fix": a padded chunk gives the real rows an unpadded chunk gives."""
+    cfg = I.small(dtype=I.BF16, B=1, H=8, nKV=2, D=128, C=64, cap=400, seen=[300],
+                  n_valid=[37])
+    t, cache, _ = _setup(cp, cfg)
+    full, _ = _run(cp, cfg, t, cache, flags=cp.ATTN_NO_SPLIT)
+    q, k, v = (dev(t[n][:, :, :37].contiguous()) for n in ("q", "k", "v"))
+    part = cp.attn_chunk_with_past(cache, q, k, v, n_valid=None, scale=cfg.scale,
+                                   flags=cp.ATTN_NO_SPLIT)
+    torch.cuda.synchronize()
+    ref = _oracle(cfg, t)[:, :, :37]
+    e1 = rowwise_rel_err(to_f64(part), ref)
+    e2 = rowwise_rel_err(to_f64(full)[:, :, :37], ref)
+    assert e1 <= TOL[I.BF16] and e2 <= TOL[I.BF16]
+    d = rowwise_rel_err(to_f64(part), to_f64(full)[:, :, :37])
+    assert d <= TOL[I.BF16]
+
+
+def test_chunk_equals_sequential_decode_steps(cp):
+    """[TICO] decode contract: C one-token steps, each appending its K/V, give the chunk's
+    real rows (within tolerance), and leave a byte-identical cache."""
+    cfg = I.small(dtype=I.BF16, B=1, H=4, nKV=1, D=128, C=24, cap=80, ring=1, window=80,
+                  seen=[150], n_valid=[21])
+    t, cache, _ = _setup(cp, cfg)
+    q, k, v, nv = dev(t["q"]), dev(t["k"]), dev(t["v"]), dev(t["n_valid"])
+    chunk = cp.attn_chunk_with_past(cache, q, k, v, n_valid=nv, window=cfg.window,
+                                    scale=cfg.scale)
+    cp.kv_append(cache, k, v, nv)
+    torch.cuda.synchronize()
+    k_chunk, v_chunk = bits(cache.k), bits(cache.v)
+    # same start state, token by token
+    t2, cache2, _ = _setup(cp, cfg)
+    steps = []
+    one = torch.ones(1, dtype=torch.int32, device="cuda")
+    for i in range(21):
+        sl = slice(i, i + 1)
+        qi, ki, vi = (dev(t2[n][:, :, sl].contiguous()) for n in ("q", "k", "v"))
+        steps.append(cp.attn_chunk_with_past(cache2, qi, ki, vi, n_valid=one, window=cfg.window,
+                                             scale=cfg.scale))
+        cp.kv_append(cache2, ki, vi, one)
+    torch.cuda.synchronize()
+    seq = torch.cat(steps, dim=2)
+    d = rowwise_rel_err(to_f64(seq), to_f64(chunk)[:, :, :21])
+    assert d <= TOL[I.BF16]
+    ref = _oracle(cfg, t)[:, :, :21]
+    assert rowwise_rel_err(to_f64(seq), ref) <= TOL[I.BF16]
+    assert cache2.seen.item() == cache.seen.item() == 171
+    np.testing.assert_array_equal(bits(cache2.k), k_chunk)
+    np.testing.assert_array_equal(bits(cache2.v), v_chunk)
+
+
+def test_mask_too_narrow_is_flagged_and_zeroed(cp):
+    cfg = I.small(dtype=I.BF16, B=1, H=4, nKV=1, D=128, C=16, cap=64, seen=[40], n_valid=[16])
+    t, cache, status = _setup(cp, cfg)
+    mask = torch.zeros((1, 4, 16, 40), dtype=torch.float32, device="cuda")  # needs 56 columns
+    out = cp.attn_chunk_with_past(cache, dev(t["q"]), dev(t["k"]), dev(t["v"]),
+                                  n_valid=dev(t["n_valid"]), mask=mask, scale=cfg.scale)
+    torch.cuda.synchronize()
+    assert int(status.item()) & cp.DEV_MASK_LD
+    assert (out.float() == 0).all()
+
+
+def test_empty_chunk_and_no_real_rows(cp):
+    cfg = I.small(dtype=I.BF16, B=2, H=4, nKV=1, D=128, C=16, cap=64, seen=[10, 20],
+                  n_valid=[0, 0])
+    t, cache, _ = _setup(cp, cfg)
+    out, _ = _run(cp, cfg, t, cache)
+    assert (out.float() == 0).all()
+    z = torch.empty((2, 4, 0, 128), dtype=torch.bfloat16, device="cuda")
+    zk = torch.empty((2, 1, 0, 128), dtype=torch.bfloat16, device="cuda")
+    cp.attn_chunk_with_past(cache, z, zk, zk, scale=cfg.scale)
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------ the named workloads
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+@pytest.mark.parametrize("mode", ["inkernel", "explicit"])
+def test_workload_attention_full(cp, name, mode):
+    cfg = I.config(name)
+    t, cache, status = _setup(cp, cfg)
+    out, _ = _run(cp, cfg, t, cache, explicit=(mode == "explicit"))
+    _check(cfg, out, _oracle(cfg, t))
+    assert int(status.item()) == 0
+
+
+def test_workload_c4_full(cp):
+    cfg = I.config("c4")
+    t, cache, status = _setup(cp, cfg)
+    out, _ = _run(cp, cfg, t, cache)
+    _check(cfg, out, _oracle(cfg, t))
+    assert int(status.item()) == 0
+
+
+@pytest.mark.parametrize("layer", [0, 5])
+def test_workload_c5_sampled_rows(cp, layer):
+    """Long context (32768 past, C = 512): rows sampled across the chunk, every head."""
+    cfg = I.config("c5", layer)
+    t, cache, status = _setup(cp, cfg, nan_dead=(layer == 5))
+    out, _ = _run(cp, cfg, t, cache)
+    rows = [0, 1, 31, 32, 255, 300, 510, 511]
+    ref = O.attn(_np(t["q"][:1]), _np(t["k"][:1]), _np(t["v"][:1]), _np(t["kc"][:1]),
+                 _np(t["vc"][:1]), _np(t["seen"][:1]), _np(t["n_valid"][:1]), None, cfg.ring,
+                 cfg.sink, cfg.window, cfg.scale, rows=rows)
+    got = to_f64(out)[:1]
+    m = np.zeros(got.shape[:3], dtype=bool)
+    m[:, :, rows] = True
+    err = rowwise_rel_err(got, ref, m)
+    assert err <= TOL[I.BF16], err
+    assert int(status.item()) == 0

@@ -449,3 +449,13 @@ def test_golden_cactus_tail():
     kept = O.live_positions(seen + tail, g["window"], 1, 0)
     assert list(ev) == list(kept[:len(ev)])
     assert all(p < seen for p in ev)
+
+
+def test_row_subset_matches_full_call():
+    """Computing selected rows only returns the same bits for those rows."""
+    cfg = I.small(**CASES[1])
+    t = _layer(cfg)
+    full = O.attn(t["q"], t["k"], t["v"], t["kc"], t["vc"], t["seen"], t["n_valid"])
+    part = O.attn(t["q"], t["k"], t["v"], t["kc"], t["vc"], t["seen"], t["n_valid"], rows=[0, 3])
+    np.testing.assert_array_equal(part[:, :, [0, 3]], full[:, :, [0, 3]])
+    assert (part[:, :, [1, 2, 4]] == 0).all()

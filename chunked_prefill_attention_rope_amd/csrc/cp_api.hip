@@ -244,7 +244,8 @@ static int check_attn(const cp_cache *cache, const cp_attn_args *a) {
   if (!a) return CP_ERR_ARG;
   const bool empty = static_cast<size_t>(cache->B) * a->C == 0;
   if (!empty && (!a->q || !a->k_new || !a->v_new || !a->out)) return CP_ERR_ARG;
-  if (a->reserved != 0 || a->C < 0 || a->window < 0 || !std::isfinite(a->scale)) return CP_ERR_ARG;
+  if (a->reserved != 0 || a->C < 0 || a->window < 0 || !std::isfinite(a->scale) || a->scale <= 0.f)
+    return CP_ERR_ARG;
   if (a->H < 1 || a->H % cache->nKV != 0) return CP_ERR_SHAPE;
   if (cache->D > 256) return CP_ERR_SHAPE;
   if (!cache->ring && a->C > cache->cap) return CP_ERR_SHAPE;

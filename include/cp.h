@@ -150,7 +150,7 @@ typedef struct cp_snapshot {
  *              h / (H / nKV))
  *   C          chunk rows
  *   window     sliding window in positions (0 = none); in-kernel mask only
- *   scale      softmax scale applied to q.k before the mask is added
+ *   scale      softmax scale (> 0) applied to q.k before the mask is added
  *   flags      CP_ATTN_* below
  *
  * The cache is read as it stands BEFORE the chunk is appended.
@@ -177,7 +177,8 @@ typedef struct cp_attn_args {
 
 #define CP_ATTN_NO_SPLIT 1u      /* one pass per query tile, no key split */
 #define CP_ATTN_FORCE_GENERIC 2u /* use the vector-ALU kernel even for bf16 */
-#define CP_ATTN_FULL_TILES 4u    /* visit every key tile (no window skipping) */
+#define CP_ATTN_FULL_TILES 4u    /* visit every key tile and apply the mask on each, as the
+                                    explicit-mask path does (same partition, same expressions) */
 
 /* ---- introspection ---- */
 

@@ -117,13 +117,14 @@ def test_attention_matches_oracle(cp, kw, mode, kernel, split):
 @pytest.mark.parametrize("kw", SMALL[:6], ids=lambda c: c["name"])
 @pytest.mark.parametrize("kernel", [0, 2])
 def test_explicit_mask_equals_inkernel_bitwise(cp, kw, kernel):
-    """With the same key partition (no split), the explicit mask built from the rule and
-    the in-kernel rule give identical outputs: masked terms are exact zeros."""
+    """On the same key partition with the mask evaluated on every tile (no split,
+    CP_ATTN_FULL_TILES), the explicit mask built from the rule and the in-kernel rule give
+    identical outputs: the additive values are identical and masked terms are exact zeros."""
     kw = dict(kw)
     kw.pop("name")
     cfg = I.small(**kw)
     t, cache, _ = _setup(cp, cfg)
-    flags = cp.ATTN_NO_SPLIT | kernel
+    flags = cp.ATTN_NO_SPLIT | cp.ATTN_FULL_TILES | kernel
     a, _ = _run(cp, cfg, t, cache, explicit=True, flags=flags)
     b, _ = _run(cp, cfg, t, cache, explicit=False, flags=flags)
     # compare values (+0 and -0 count as equal)

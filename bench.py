@@ -93,11 +93,26 @@ def algorithmic(cfg):
     return nbytes, flops
 
 
+def measured_traffic(workload, flags):
+    """HBM bytes per attention call from the committed rocprofv3 counter record
+    (FETCH_SIZE and WRITE_SIZE scaled by the copy-kernel calibration), or None when
+    none was taken for this workload or the attention sources changed since."""
+    from chunked_prefill_attention_rope_amd.profiling import source_digest
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if flags or not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(workload)
+    if not rec or rec.get("source_sha1") != source_digest():
+        return None
+    return rec["bytes_per_call"]
+
+
 class Layer:
     """Device inputs, per-step caches and buffers of one layer."""
 
-    def __init__(self, cp, path, cfg, nsteps):
+    def __init__(self, cp, path, cfg, nsteps, flags=0):
         self.cfg = cfg
+        self.flags = flags
         t = I.make_layer(cfg, nan_dead=False)
         self.host = t
         d = {k: v.to("cuda") for k, v in t.items()}
@@ -112,7 +127,7 @@ class Layer:
         self.static = bool(cfg.ring) and any(n < cfg.C for n in cfg.n_valid)
         self.window = 0 if cfg.explicit_mask else cfg.window
         self.bufs = path.make_buffers(self.caches[0], d["q"], d["k"], d["v"], mask=self.mask,
-                                      window=self.window, static_append=self.static)
+                                      window=self.window, static_append=self.static, flags=flags)
 
     def reset(self):
         self.seen_all.copy_(self.seen0.expand_as(self.seen_all))
@@ -121,13 +136,13 @@ class Layer:
         d = self.d
         path.chunk_step(self.caches[s], d["q"], d["k"], d["v"], d["cos"], d["sin"],
                         d["n_valid"], self.bufs, mask=self.mask, window=self.window,
-                        static_append=self.static)
+                        static_append=self.static, flags=self.flags)
 
     def attn_only(self, cp):
         d, b = self.d, self.bufs
         cp.attn_chunk_with_past(self.caches[0], b.q_rot, b.k_rot, d["v"], n_valid=d["n_valid"],
                                 mask=self.mask, window=self.window, scale=self.cfg.scale,
-                                out=b.out, workspace=b.workspace)
+                                out=b.out, workspace=b.workspace, flags=self.flags)
 
 
 def time_graph(fn, reps_inside, replays=1):
@@ -201,6 +216,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attn-reps", type=int, default=200)
+    ap.add_argument("--attn-flags", type=int, default=0,
+                    help="CP_ATTN_* flags for the attention call (e.g. a forced split count)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU: this path has no multi-GPU mode (see DESIGN.md for "
@@ -211,7 +228,7 @@ def main():
 
     torch.cuda.set_device(0)
     K, W = args.steps, args.warmup
-    layers = [Layer(cp, path, cfg, K + W) for cfg in layers_of(args.workload)]
+    layers = [Layer(cp, path, cfg, K + W, args.attn_flags) for cfg in layers_of(args.workload)]
     torch.cuda.synchronize()
     cfg0 = layers[0].cfg
     tokens_per_layer = sum(cfg0.n_valid)
@@ -282,7 +299,7 @@ def main():
         roof = {"bound": "mfma" if lay_dom.cfg.dtype == I.BF16 else "alu",
                 "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 5)}
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(args.workload, args.attn_flags)
     roof["kernel"] = "cp_attn_chunk_with_past"
     roof["avg_launch_us"] = round(attn_ms * 1e3, 3)
     roof["algorithmic_bytes"] = nbytes
@@ -295,7 +312,8 @@ def main():
         "dtype": "f32" if cfg0.dtype == I.F32 else "bf16", "data": "synthetic",
         "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}",
                    "layers_per_step": nl, "real_tokens_per_layer": tokens_per_layer,
-                   "launch": mode, "eager_ms_per_step": round(eager_ms, 6)},
+                   "launch": mode, "eager_ms_per_step": round(eager_ms, 6),
+                   "attn_flags": args.attn_flags},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

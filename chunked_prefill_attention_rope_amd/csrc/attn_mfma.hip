@@ -418,7 +418,7 @@ __global__ void __launch_bounds__(256)
         *reinterpret_cast<u32x2 *>(O + d) = w;
       }
     }
-  } else {
+  } else if (i < nv) {  // partials of real rows only: the merge writes pad rows as zeros
     const size_t rows = static_cast<size_t>(p.B) * p.H * p.C;
     float *WO = p.wo + (split * rows + orow) * D;
 #pragma unroll

@@ -187,7 +187,7 @@ __global__ void __launch_bounds__(256) k_attn_valu(AttnParams p, int D) {
       const int d = ql + 16 * e;
       if (d < D) st(O, orow * D + d, real ? acc[e] * inv : 0.f);
     }
-  } else {
+  } else if (i < nv) {  // partials of real rows only: the merge writes pad rows as zeros
     const size_t rows = static_cast<size_t>(p.B) * p.H * p.C;
     float *WO = p.wo + (split * rows + orow) * D;
 #pragma unroll
@@ -203,35 +203,54 @@ __global__ void __launch_bounds__(256) k_attn_valu(AttnParams p, int D) {
   }
 }
 
-// Merge key-split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-template <typename T>
+// Merge key-split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, for
+// VEC consecutive output columns per thread; pad rows are written as zeros.
+template <typename T, int VEC>
 __global__ void __launch_bounds__(256) k_attn_combine(AttnParams p, int D) {
   const size_t rows = static_cast<size_t>(p.B) * p.H * p.C;
-  const size_t total = rows * D;
+  const int per_row = D / VEC;
+  const size_t total = rows * per_row;
   T *O = static_cast<T *>(p.out);
   for (size_t t = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; t < total;
        t += static_cast<size_t>(gridDim.x) * blockDim.x) {
-    const size_t row = t / D;
-    const int d = static_cast<int>(t % D);
+    const size_t row = t / per_row;
+    const int d0 = static_cast<int>(t % per_row) * VEC;
     const int i = static_cast<int>(row % p.C);
     const int b = static_cast<int>(row / (static_cast<size_t>(p.H) * p.C));
     const int nv = read_nvalid(p.n_valid, b, p.C, nullptr);
-    float res = 0.f;
+    float res[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) res[e] = 0.f;
     if (i < nv) {
       float M = -INFINITY;
       for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.wml[(s * rows + row) * 2]);
-      float l = 0.f, o = 0.f;
+      float l = 0.f, o[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) o[e] = 0.f;
       if (M != -INFINITY) {
         for (int s = 0; s < p.splits; ++s) {
-          const float ms = p.wml[(s * rows + row) * 2];
-          const float wgt = __builtin_amdgcn_exp2f(ms - M);
-          l = fmaf(wgt, p.wml[(s * rows + row) * 2 + 1], l);
-          o = fmaf(wgt, p.wo[(s * rows + row) * D + d], o);
+          const float2 ml = *reinterpret_cast<const float2 *>(p.wml + (s * rows + row) * 2);
+          const float wgt = __builtin_amdgcn_exp2f(ml.x - M);
+          l = fmaf(wgt, ml.y, l);
+          const float *src = p.wo + (s * rows + row) * D + d0;
+          if constexpr (VEC == 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(src);
+            o[0] = fmaf(wgt, v.x, o[0]);
+            o[1] = fmaf(wgt, v.y, o[1]);
+            o[2] = fmaf(wgt, v.z, o[2]);
+            o[3] = fmaf(wgt, v.w, o[3]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) o[e] = fmaf(wgt, src[e], o[e]);
+          }
         }
       }
-      res = l > 0.f ? o / l : 0.f;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) res[e] = o[e] * inv;
     }
-    st(O, t, res);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) st(O, row * D + d0 + e, res[e]);
   }
 }
 
@@ -266,12 +285,20 @@ hipError_t launch_attn_valu(const AttnParams &p, int D, int dtype, hipStream_t s
 hipError_t launch_attn_combine(const AttnParams &p, int D, int dtype, hipStream_t s) {
   const size_t total = static_cast<size_t>(p.B) * p.H * p.C * D;
   if (total == 0) return hipSuccess;
-  size_t blocks = (total + 255) / 256;
+  const bool v4 = D % 4 == 0;
+  size_t blocks = (total / (v4 ? 4 : 1) + 255) / 256;
   if (blocks > 16384) blocks = 16384;
-  if (dtype == CP_BF16)
-    hipLaunchKernelGGL(k_attn_combine<uint16_t>, dim3(blocks), dim3(256), 0, s, p, D);
-  else
-    hipLaunchKernelGGL(k_attn_combine<float>, dim3(blocks), dim3(256), 0, s, p, D);
+  if (dtype == CP_BF16) {
+    if (v4)
+      hipLaunchKernelGGL((k_attn_combine<uint16_t, 4>), dim3(blocks), dim3(256), 0, s, p, D);
+    else
+      hipLaunchKernelGGL((k_attn_combine<uint16_t, 1>), dim3(blocks), dim3(256), 0, s, p, D);
+  } else {
+    if (v4)
+      hipLaunchKernelGGL((k_attn_combine<float, 4>), dim3(blocks), dim3(256), 0, s, p, D);
+    else
+      hipLaunchKernelGGL((k_attn_combine<float, 1>), dim3(blocks), dim3(256), 0, s, p, D);
+  }
   return hipGetLastError();
 }
 

@@ -62,9 +62,14 @@ AttnPlan plan_attention(const cp_cache &c, const cp_attn_args &a, bool for_works
     if (wk < keys) keys = wk;
   }
   const long tiles = (keys + pl.kt - 1) / pl.kt;
-  if (!(a.flags & CP_ATTN_NO_SPLIT) && base > 0 && base < kNumCU && tiles >= 4) {
+  const int forced = static_cast<int>((a.flags >> 8) & 0xffu);
+  if (forced > 0) {
+    pl.splits = forced > 64 ? 64 : forced;
+  } else if (!(a.flags & CP_ATTN_NO_SPLIT) && base > 0 && base < kNumCU && tiles >= 8) {
+    // Few query tiles: split the keys so that more CUs work, but keep >= 4 key tiles per
+    // split -- each split writes fp32 partials that a second kernel merges.
     long s = (2 * kNumCU + base - 1) / base;
-    if (s > tiles / 2) s = tiles / 2;
+    if (s > tiles / 4) s = tiles / 4;
     if (s > 64) s = 64;
     pl.splits = s > 1 ? static_cast<int>(s) : 1;
   }

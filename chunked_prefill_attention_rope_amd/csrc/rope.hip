@@ -4,8 +4,9 @@
 // tables, one pair per RoPE base; [TICO] "Runtime behavior": (cos_t, sin_t)
 // for the absolute position.  Half-split pairing (j with j + D/2).
 //
-// HBM-bound elementwise kernel: each thread rotates VEC consecutive pairs of
-// one row, reading the lower and upper halves with vector loads.  The math
+// HBM-bound elementwise kernel: each thread rotates the pairs of one 16-byte
+// slice of a row's lower half (and the matching upper-half slice), with
+// 16-byte loads and stores.  The math
 // runs in fp64: an fp32 x fp32 product is exact in fp64, so the difference
 // (or sum) of the two products is rounded exactly once, independent of FMA
 // contraction; the result is then rounded to fp32 and, for bf16 storage, to
@@ -20,17 +21,18 @@ template <typename T>
 struct Elem;
 template <>
 struct Elem<float> {
-  static __device__ __forceinline__ float load(const float *p, size_t i) { return p[i]; }
-  static __device__ __forceinline__ void store(float *p, size_t i, float v) { p[i] = v; }
+  static __device__ __forceinline__ float get(float v) { return v; }
+  static __device__ __forceinline__ float put(float v) { return v; }
 };
 template <>
 struct Elem<uint16_t> {
-  static __device__ __forceinline__ float load(const uint16_t *p, size_t i) {
-    return bf16_to_f32(p[i]);
-  }
-  static __device__ __forceinline__ void store(uint16_t *p, size_t i, float v) {
-    p[i] = f32_to_bf16_rne(v);
-  }
+  static __device__ __forceinline__ float get(uint16_t v) { return bf16_to_f32(v); }
+  static __device__ __forceinline__ uint16_t put(float v) { return f32_to_bf16_rne(v); }
+};
+
+template <typename T, int N>
+struct alignas(sizeof(T) * N) Pack {
+  T v[N];
 };
 
 __device__ __forceinline__ float rot_lo(float lo, float hi, float c, float s) {
@@ -44,11 +46,11 @@ __device__ __forceinline__ float rot_hi(float lo, float hi, float c, float s) {
   return static_cast<float>(a + b);
 }
 
-// One thread: VEC consecutive pairs (j .. j+VEC-1, j+h2 .. j+h2+VEC-1) of a row.
+// One thread: VEC consecutive pairs (j .. j+VEC-1, j+h2 .. j+h2+VEC-1) of a row,
+// moved with vector loads/stores (VEC > 1 needs 16-byte aligned rows and tables).
 // x and y may alias: every element is read and written by the same thread.
 template <typename T, int VEC>
-__global__ void __launch_bounds__(256) k_rope(const T *x, T *y,
-                                              const float *__restrict__ cosb,
+__global__ void __launch_bounds__(128) k_rope(const T *x, T *y, const float *__restrict__ cosb,
                                               const float *__restrict__ sinb, int B, int Hx, int C,
                                               int D, int Bt) {
   const int h2 = D / 2;
@@ -63,22 +65,25 @@ __global__ void __launch_bounds__(256) k_rope(const T *x, T *y,
     const int b = static_cast<int>(row / (static_cast<size_t>(Hx) * C));
     const size_t xo = row * D;
     const size_t to = (static_cast<size_t>(Bt == 1 ? 0 : b) * C + i) * D;
-    float lo[VEC], hi[VEC];
+    const Pack<T, VEC> lo = *reinterpret_cast<const Pack<T, VEC> *>(x + xo + j0);
+    const Pack<T, VEC> hi = *reinterpret_cast<const Pack<T, VEC> *>(x + xo + j0 + h2);
+    const Pack<float, VEC> cl = *reinterpret_cast<const Pack<float, VEC> *>(cosb + to + j0);
+    const Pack<float, VEC> sl = *reinterpret_cast<const Pack<float, VEC> *>(sinb + to + j0);
+    const Pack<float, VEC> ch = *reinterpret_cast<const Pack<float, VEC> *>(cosb + to + j0 + h2);
+    const Pack<float, VEC> sh = *reinterpret_cast<const Pack<float, VEC> *>(sinb + to + j0 + h2);
+    Pack<T, VEC> ylo, yhi;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      lo[e] = Elem<T>::load(x, xo + j0 + e);
-      hi[e] = Elem<T>::load(x, xo + j0 + h2 + e);
+      const float a = Elem<T>::get(lo.v[e]), c = Elem<T>::get(hi.v[e]);
+      ylo.v[e] = Elem<T>::put(rot_lo(a, c, cl.v[e], sl.v[e]));
+      yhi.v[e] = Elem<T>::put(rot_hi(a, c, ch.v[e], sh.v[e]));
     }
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      const int j = j0 + e;
-      const float ylo = rot_lo(lo[e], hi[e], cosb[to + j], sinb[to + j]);
-      const float yhi = rot_hi(lo[e], hi[e], cosb[to + j + h2], sinb[to + j + h2]);
-      Elem<T>::store(y, xo + j, ylo);
-      Elem<T>::store(y, xo + j + h2, yhi);
-    }
+    *reinterpret_cast<Pack<T, VEC> *>(y + xo + j0) = ylo;
+    *reinterpret_cast<Pack<T, VEC> *>(y + xo + j0 + h2) = yhi;
   }
 }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 template <typename T>
 hipError_t launch_t(const void *x, void *y, const float *cos, const float *sin, int B, int Hx,
@@ -88,21 +93,20 @@ hipError_t launch_t(const void *x, void *y, const float *cos, const float *sin, 
   if (rows == 0) return hipSuccess;
   auto grid_for = [&](int vec) {
     size_t total = rows * (h2 / vec);
-    size_t blocks = (total + 255) / 256;
+    size_t blocks = (total + 127) / 128;
     if (blocks > 65535 * 4) blocks = 65535 * 4;
     return static_cast<unsigned>(blocks);
   };
   const T *xi = static_cast<const T *>(x);
   T *yo = static_cast<T *>(y);
-  if (h2 % 8 == 0) {
-    hipLaunchKernelGGL((k_rope<T, 8>), dim3(grid_for(8)), dim3(256), 0, s, xi, yo, cos, sin, B,
-                       Hx, C, D, Bt);
-  } else if (h2 % 4 == 0) {
-    hipLaunchKernelGGL((k_rope<T, 4>), dim3(grid_for(4)), dim3(256), 0, s, xi, yo, cos, sin, B,
-                       Hx, C, D, Bt);
+  constexpr int V16 = 16 / sizeof(T);  // elements per 16 bytes
+  const bool al = aligned16(x) && aligned16(y) && aligned16(cos) && aligned16(sin);
+  if (al && h2 % V16 == 0) {
+    hipLaunchKernelGGL((k_rope<T, V16>), dim3(grid_for(V16)), dim3(128), 0, s, xi, yo, cos, sin,
+                       B, Hx, C, D, Bt);
   } else {
-    hipLaunchKernelGGL((k_rope<T, 1>), dim3(grid_for(1)), dim3(256), 0, s, xi, yo, cos, sin, B,
-                       Hx, C, D, Bt);
+    hipLaunchKernelGGL((k_rope<T, 1>), dim3(grid_for(1)), dim3(128), 0, s, xi, yo, cos, sin, B, Hx,
+                       C, D, Bt);
   }
   return hipGetLastError();
 }

@@ -26,7 +26,18 @@ def main():
     ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--step", action="store_true", help="whole layer step, not attention only")
     ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead: copy a buffer of this many bytes (counter calibration)")
     a = ap.parse_args()
+    if a.copy_bytes:
+        # a plain device copy of known size: reads and writes exactly copy_bytes each
+        src = torch.ones(a.copy_bytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(a.reps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"profile_attn: copy of {a.copy_bytes} bytes x{a.reps} done", flush=True)
+        return
     cfg = I.config(a.workload, a.layer)
     t = I.make_layer(cfg, nan_dead=False)
     d = {k: v.to("cuda") for k, v in t.items()}

@@ -1,0 +1,88 @@
+"""Summaries of rocprofv3 CSV output (kernel-trace stats and PMC counters).
+
+    python -m chunked_prefill_attention_rope_amd.profiling stats <kernel_stats.csv>
+    python -m chunked_prefill_attention_rope_amd.profiling pmc <counter_collection.csv> [regex]
+
+`stats` prints a markdown table of per-kernel calls and durations; `pmc`
+prints, per kernel, the counters summed over the dispatch's instances and
+averaged over its dispatches; `digest` prints the hash of the attention
+sources that a traffic measurement is tied to.
+"""
+import collections
+import csv
+import hashlib
+import os
+import re
+import sys
+
+_CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+# sources whose change invalidates counters measured on the attention call
+ATTN_SOURCES = ("attn_mfma.hip", "attn_valu.hip", "attn_common.h", "cp_common.h", "cp_api.hip")
+
+
+def source_digest(names=ATTN_SOURCES):
+    """sha1 over the given csrc files (identifies the kernel build a measurement used)."""
+    h = hashlib.sha1()
+    for n in names:
+        with open(os.path.join(_CSRC, n), "rb") as f:
+            h.update(n.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def kernel_stats(path):
+    rows = list(csv.DictReader(open(path)))
+    out = []
+    for r in rows:
+        out.append(dict(name=r["Name"], calls=int(r["Calls"]),
+                        avg_us=float(r["AverageNs"]) / 1e3, total_us=float(r["TotalDurationNs"]) / 1e3,
+                        min_us=float(r["MinNs"]) / 1e3, max_us=float(r["MaxNs"]) / 1e3,
+                        pct=float(r["Percentage"])))
+    return out
+
+
+def pmc_per_kernel(path, pattern=None):
+    """{kernel: {counter: mean over dispatches of the per-dispatch sum}}."""
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    names = {}
+    for r in csv.DictReader(open(path)):
+        if pattern and not re.search(pattern, r["Kernel_Name"]):
+            continue
+        d = int(r["Dispatch_Id"])
+        per[d][r["Counter_Name"]] += float(r["Counter_Value"])
+        names[d] = r["Kernel_Name"]
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for d, cs in per.items():
+        for c, v in cs.items():
+            agg[names[d]][c].append(v)
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in agg.items()}
+
+
+def short(name, n=90):
+    name = re.sub(r"\(anonymous namespace\)::", "", name)
+    return name if len(name) <= n else name[:n - 3] + "..."
+
+
+def main(argv):
+    if len(argv) >= 2 and argv[0] == "stats":
+        print("| kernel | calls | avg us | min us | max us | total us | % |")
+        print("|---|---:|---:|---:|---:|---:|---:|")
+        for k in kernel_stats(argv[1]):
+            print(f"| `{short(k['name'])}` | {k['calls']} | {k['avg_us']:.2f} | {k['min_us']:.2f} "
+                  f"| {k['max_us']:.2f} | {k['total_us']:.1f} | {k['pct']:.1f} |")
+        return 0
+    if len(argv) >= 2 and argv[0] == "pmc":
+        res = pmc_per_kernel(argv[1], argv[2] if len(argv) > 2 else None)
+        for k, cs in res.items():
+            print(f"- `{short(k)}`")
+            for c, v in sorted(cs.items()):
+                print(f"  - {c}: {v:.6g}")
+        return 0
+    if argv and argv[0] == "digest":
+        print(source_digest())
+        return 0
+    print(__doc__)
+    return 2
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))

@@ -179,6 +179,9 @@ typedef struct cp_attn_args {
 #define CP_ATTN_FORCE_GENERIC 2u /* use the vector-ALU kernel even for bf16 */
 #define CP_ATTN_FULL_TILES 4u    /* visit every key tile and apply the mask on each, as the
                                     explicit-mask path does (same partition, same expressions) */
+/* Force the number of key splits to n (1..64; needs the workspace for n) instead of
+   the planner's choice.  Placed in bits 8..15 of flags. */
+#define CP_ATTN_SPLITS(n) (((uint32_t)(n) & 0xffu) << 8)
 
 /* ---- introspection ---- */
 

@@ -22,9 +22,11 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        path = _build.LIB
-        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
-            _build.build()
+        path = os.environ.get("CP_ORACLE_LIB")  # a mutated copy (tests/oracle_mutations.py)
+        if not path:
+            path = _build.LIB
+            if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+                _build.build()
         L = ctypes.CDLL(path)
         vp, ip, i32p = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p
         L.orc_rope.argtypes = [vp, vp, vp, vp, ip, ip, ip, ip, ip, ip]

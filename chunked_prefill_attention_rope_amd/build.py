@@ -52,6 +52,11 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+    # a kernel whose body the host pass rejects silently loses its launch stub
+    nm = subprocess.run(["nm", "-C", tmp], capture_output=True, text=True, check=True).stdout
+    missing = [l for l in nm.splitlines() if " U " in l and "__device_stub__" in l]
+    if missing:
+        raise RuntimeError("kernel launch stubs missing from libcp.so:\n" + "\n".join(missing))
     os.replace(tmp, LIB)
     return LIB
 

@@ -32,10 +32,12 @@
 // exceeds it by more than 2^8 (exact: numerator and denominator share it), so
 // the O accumulator is rarely rescaled.
 //
-// Pipeline.  K/V tile t+1 is loaded from HBM into registers while tile t is
-// computed from LDS; chunk rows come from the caller's k_new / v_new, past
-// rows from the cache slots.  Tiles outside the window or past the last real
-// row are skipped.
+// Loads.  K/V tiles stream into a ring of LDS stages with direct-to-LDS loads
+// (global_load_lds_dwordx4, 1 KB per wave instruction), STAGES - 1 tiles ahead
+// of the one being computed, without passing through registers; the waits on
+// them are explicit (vmcnt) followed by a plain s_barrier.  Chunk rows come from
+// the caller's k_new / v_new, past rows from the cache slots.  Tiles outside
+// the window or past the last real row are skipped.
 #include "attn_common.h"
 
 namespace cp {
@@ -48,7 +50,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kRescaleSlack = 8.f;  // log2 units
 
@@ -56,6 +58,34 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const f32x2 v = {a, b};
   const bf16x2 r = __builtin_convertvector(v, bf16x2);
   return __builtin_bit_cast(uint32_t, r);
+}
+
+// One wave-wide direct-to-LDS load: each lane's 16 bytes at src land at
+// lds_base + 16 * lane.  The builtin only exists for the gfx950 device pass; the
+// host pass of a HIP kernel never runs device code, and would otherwise drop the
+// kernel's launch stub, so it gets an empty body.
+__device__ __forceinline__ void dma16(const uint16_t *src, uint16_t *lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_base, 16, 0, 0);
+#else
+  (void)src;
+  (void)lds_base;
+#endif
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void *ptr) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)ptr));
+}
+
+// ds_read_b64_tr_b16 issued as inline asm: the builtin makes the compiler drain all
+// in-flight direct-to-LDS loads before it, which would serialise the K/V ring.  The
+// result registers are only valid after lds_wait() below has been passed through them.
+__device__ __forceinline__ u32x2 tr_read(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
 }
 
 __device__ __forceinline__ f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
@@ -85,26 +115,62 @@ __device__ __forceinline__ int kswz(int r) {
 }
 __device__ __forceinline__ int vswz(int r) { return (r & 3) << 1; }
 
+// Per head size: keys per tile, LDS ring stages, waves per SIMD.  A stage holds
+// one K and one V tile (KT x D bf16 each).
 template <int D>
-struct WavesPerEU {
-  static constexpr int value = D >= 256 ? 1 : 2;
+struct Cfg;
+template <>
+struct Cfg<64> {
+  static constexpr int KT = 64, STAGES = 4, WAVES = 2;
+};
+template <>
+struct Cfg<128> {
+  static constexpr int KT = 64, STAGES = 2, WAVES = 2;
+};
+template <>
+struct Cfg<256> {
+  static constexpr int KT = 32, STAGES = 4, WAVES = 1;
 };
 
-template <int D, int KT, bool EXPLICIT>
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Wait until at most n * PER vector-memory loads of this wave are outstanding
+// (n = tiles issued after the one about to be consumed).
+template <int PER, int STAGES>
+__device__ __forceinline__ void wait_tiles_after(int n) {
+  if (STAGES > 3 && n >= 2) {
+    wait_vm<(STAGES > 3 ? 2 : 0) * PER>();
+  } else if (STAGES > 2 && n >= 1) {
+    wait_vm<(STAGES > 2 ? 1 : 0) * PER>();
+  } else {
+    wait_vm<0>();
+  }
+}
+
+template <int D, bool EXPLICIT>
 __global__ void __launch_bounds__(256)
-    __attribute__((amdgpu_waves_per_eu(WavesPerEU<D>::value, WavesPerEU<D>::value)))
+    __attribute__((amdgpu_waves_per_eu(Cfg<D>::WAVES, Cfg<D>::WAVES)))
     k_attn_mfma(AttnParams p) {
+  constexpr int KT = Cfg<D>::KT;
+  constexpr int STAGES = Cfg<D>::STAGES;
   constexpr int CPR = D / 8;         // 16-byte chunks per row
   constexpr int NK = KT * CPR;       // chunks per tile (K or V)
-  constexpr int NL = NK / 256;       // chunk loads per thread per tile
+  constexpr int NL = NK / 256;       // direct-to-LDS loads per wave per tile per tensor
+  constexpr int RPI = 64 / CPR;      // rows covered by one wave-wide 1 KB load
   constexpr int NS = D / 16;         // k-steps of QK^T
   constexpr int NKB = KT / 32;       // 32-key blocks per tile
   constexpr int NDB = D / 32;        // 32-dim blocks of the output
   constexpr int NPT = KT / 16;       // k-steps of PV
-  static_assert(NK % 256 == 0, "tile must split evenly over 256 threads");
+  constexpr int TILE = KT * D;       // bf16 elements of one K (or V) tile
+  static_assert(NK % 256 == 0, "tile must split evenly over 4 waves");
+  static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[KT * D];
+  // ring of STAGES x (K tile, V tile)
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[STAGES * 2 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -191,30 +257,30 @@ __global__ void __launch_bounds__(256)
   const int R = p.cap - p.sink;
   const bool small_ring = p.ring && R < KT;
 
-  // ---- global -> registers -> LDS staging (thread owns chunks tid + 256 e)
-  u32x4 kreg[NL], vreg[NL];
-  auto load_tile = [&](int u) {
+  // ---- direct-to-LDS staging.  Wave-wide load q (= wave * NL + e) fills 1 KB of
+  // the tile: rows q * RPI + lane / CPR, physical chunk lane % CPR, which holds the
+  // row's logical chunk (physical ^ swizzle).  Rows outside the tile's valid range
+  // read a valid row instead; their scores are masked to -inf.
+  auto issue = [&](int u, uint16_t *kdst, uint16_t *vdst) __attribute__((always_inline)) {
     int first;
     const bool chunk = ts.at(u, KT, &first);
-    // slot of the tile's first non-sink column (past tiles of a ring)
+    const int lim = chunk ? p.C : gl.L;
     int c_ns = imax(first, gl.ns), s_ns = 0;
-    if (!chunk && p.ring && c_ns < gl.L) s_ns = slot_of(gl.lo + (c_ns - gl.ns), p.cap, 1, p.sink);
+    if (!chunk && p.ring && !small_ring && c_ns < gl.L)
+      s_ns = slot_of(gl.lo + (c_ns - gl.ns), p.cap, 1, p.sink);
 #pragma unroll
     for (int e = 0; e < NL; ++e) {
-      const int idx = tid + 256 * e;
-      const int row = idx / CPR, ch = idx % CPR;
-      const int col = first + row;
-      const uint16_t *ks = nullptr, *vs = nullptr;
+      const int q = wave * NL + e;
+      const int row = q * RPI + lane / CPR, phys = lane % CPR;
+      int col = first + row;
+      if (col >= lim) col = lim - 1;
+      const uint16_t *kr, *vr;
       if (chunk) {
-        if (col < p.C) {
-          ks = KN + static_cast<size_t>(col) * D;
-          vs = VN + static_cast<size_t>(col) * D;
-        }
-      } else if (col < gl.L) {
+        kr = KN + static_cast<size_t>(col) * D;
+        vr = VN + static_cast<size_t>(col) * D;
+      } else {
         int sl;
-        if (!p.ring) {
-          sl = col;
-        } else if (col < gl.ns) {
+        if (!p.ring || col < gl.ns) {
           sl = col;
         } else if (!small_ring) {
           sl = s_ns + (col - c_ns);
@@ -222,25 +288,11 @@ __global__ void __launch_bounds__(256)
         } else {
           sl = slot_of(gl.lo + (col - gl.ns), p.cap, 1, p.sink);
         }
-        ks = KC + static_cast<size_t>(sl) * D;
-        vs = VC + static_cast<size_t>(sl) * D;
+        kr = KC + static_cast<size_t>(sl) * D;
+        vr = VC + static_cast<size_t>(sl) * D;
       }
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (ks) {
-        kv = *reinterpret_cast<const u32x4 *>(ks + ch * 8);
-        vv = *reinterpret_cast<const u32x4 *>(vs + ch * 8);
-      }
-      kreg[e] = kv;
-      vreg[e] = vv;
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int e = 0; e < NL; ++e) {
-      const int idx = tid + 256 * e;
-      const int row = idx / CPR, ch = idx % CPR;
-      *reinterpret_cast<u32x4 *>(&Ks[row * D + ((ch ^ kswz<D>(row)) << 3)]) = kreg[e];
-      *reinterpret_cast<u32x4 *>(&Vs[row * D + ((ch ^ vswz(row)) << 3)]) = vreg[e];
+      if (kdst) dma16(kr + ((phys ^ kswz<D>(row)) << 3), kdst + q * 512);
+      if (vdst) dma16(vr + ((phys ^ vswz(row)) << 3), vdst + q * 512);
     }
   };
 
@@ -257,17 +309,8 @@ __global__ void __launch_bounds__(256)
     mrow = p.mask + b * p.mbs + head * p.mhs + static_cast<int64_t>(irow) * p.mld;
   const int qabs = seen + i;
 
-  if (u0 < u1) load_tile(u0);
-  for (int u = u0; u < u1; ++u) {
-    int first;
-    const bool chunk = ts.at(u, KT, &first);
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (u + 1 < u1) load_tile(u + 1);
-
-    // ---- S^T = K Q^T
-    f32x16 sacc[NKB];
+  // S^T = K Q^T for the tile whose K sits at Ks
+  auto qk = [&](const uint16_t *Ks, f32x16 (&sacc)[NKB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -281,13 +324,19 @@ __global__ void __launch_bounds__(256)
         sacc[kb] = mfma(__builtin_bit_cast(bf16x8, a), qf[s], sacc[kb]);
       }
     }
+  };
 
+  // mask, online softmax and O^T += V^T P^T for tile u (scores in sacc, V at Vs)
+  auto softmax_pv = [&](int u, f32x16 (&sacc)[NKB], const uint16_t *Vs)
+                            __attribute__((always_inline)) {
+    int first;
+    const bool chunk = ts.at(u, KT, &first);
     // ---- tile classification (wave-uniform): does every real row of this wave
     // attend every key of the tile?  Then no mask work at all.
     const int lim = chunk ? p.C : gl.L;
     const int64_t mbase = chunk ? static_cast<int64_t>(gl.L) + first : first;
     // additive bias of key kk of this lane's row (explicit mask or rule), -inf out of range
-    auto bias4 = [&](int kk, float *a4) {
+    auto bias4 = [&](int kk, float *a4) __attribute__((always_inline)) {
       if (EXPLICIT) {
         if (mrow && p.mask_vec4 && first + kk + 3 < lim && ((mbase + kk) & 3) == 0) {
           const float4 mv = *reinterpret_cast<const float4 *>(mrow + mbase + kk);
@@ -382,21 +431,54 @@ __global__ void __launch_bounds__(256)
       }
     }
 
-    // ---- O^T += V^T P^T, V^T gathered by transpose reads
+    // ---- O^T += V^T P^T, V^T gathered by transpose reads (one batch per 32 dims)
+    const uint32_t vbase = lds_addr(Vs) + 2 * (v_key * D);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const int voff = (((4 * db + v_cl) ^ v_sw) << 3) + v_el;
+      const uint32_t va = vbase + 2 * ((((4 * db + v_cl) ^ v_sw) << 3) + v_el);
+      u32x2 w[2 * NPT];
 #pragma unroll
       for (int t = 0; t < NPT; ++t) {
-        const uint16_t *v0 = &Vs[(16 * t + v_key) * D + voff];
-        const uint16_t *v1 = &Vs[(16 * t + 8 + v_key) * D + voff];
-        const s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(v0));
-        const s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(v1));
-        const u32x2 w0 = __builtin_bit_cast(u32x2, a0), w1 = __builtin_bit_cast(u32x2, a1);
-        const u32x4 a = {w0[0], w0[1], w1[0], w1[1]};
+        w[2 * t] = tr_read(va + 2 * (16 * t * D));
+        w[2 * t + 1] = tr_read(va + 2 * ((16 * t + 8) * D));
+      }
+      if constexpr (NPT == 4) {
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5]),
+                       "+v"(w[6]), "+v"(w[7]));
+      } else {
+        static_assert(NPT == 2, "PV k-steps per tile");
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
+      }
+#pragma unroll
+      for (int t = 0; t < NPT; ++t) {
+        const u32x4 a = {w[2 * t][0], w[2 * t][1], w[2 * t + 1][0], w[2 * t + 1][1]};
         oacc[db] = mfma(__builtin_bit_cast(bf16x8, a), pb[t], oacc[db]);
       }
     }
+  };
+
+  // tile u lives in stage u % STAGES of a ring of (K, V) tiles (a key split starts
+  // at u0 > 0)
+  for (int j = 0; j < STAGES - 1; ++j)
+    if (u0 + j < u1) {
+      uint16_t *st = ring + ((u0 + j) % STAGES) * 2 * TILE;
+      issue(u0 + j, st, st + TILE);
+    }
+  for (int u = u0; u < u1; ++u) {
+    // tile u has landed in this wave's share of the ring once at most the loads of
+    // the tiles issued after it are outstanding; the barrier makes that true for all
+    // waves and also guarantees every wave has finished reading the stage refilled
+    wait_tiles_after<2 * NL, STAGES>(imin(u1 - 1, u + STAGES - 2) - u);
+    __builtin_amdgcn_s_barrier();
+    if (u + STAGES - 1 < u1) {
+      uint16_t *st = ring + ((u + STAGES - 1) % STAGES) * 2 * TILE;
+      issue(u + STAGES - 1, st, st + TILE);
+    }
+    const uint16_t *Ks = ring + (u % STAGES) * 2 * TILE;
+    f32x16 sacc[NKB];
+    qk(Ks, sacc);
+    softmax_pv(u, sacc, Ks + TILE);
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -442,14 +524,14 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-template <int D, int KT>
+template <int D>
 hipError_t launch_d(const AttnParams &p, hipStream_t s) {
   const unsigned blocks = static_cast<unsigned>(p.qtiles) * p.splits * p.B * p.nKV;
   if (blocks == 0) return hipSuccess;
   if (p.mask)
-    hipLaunchKernelGGL((k_attn_mfma<D, KT, true>), dim3(blocks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_attn_mfma<D, true>), dim3(blocks), dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL((k_attn_mfma<D, KT, false>), dim3(blocks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_attn_mfma<D, false>), dim3(blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -458,16 +540,18 @@ hipError_t launch_d(const AttnParams &p, hipStream_t s) {
 hipError_t launch_attn_mfma(const AttnParams &p, int D, hipStream_t s) {
   switch (D) {
     case 64:
-      return launch_d<64, 64>(p, s);
+      return launch_d<64>(p, s);
     case 128:
-      return launch_d<128, 64>(p, s);
+      return launch_d<128>(p, s);
     case 256:
-      return launch_d<256, 32>(p, s);
+      return launch_d<256>(p, s);
     default:
       return hipErrorInvalidValue;
   }
 }
 
-int mfma_keys_per_tile(int D) { return D == 256 ? 32 : 64; }
+int mfma_keys_per_tile(int D) {
+  return D == 256 ? Cfg<256>::KT : (D == 128 ? Cfg<128>::KT : Cfg<64>::KT);
+}
 
 }  // namespace cp

@@ -4,7 +4,8 @@
 // under an additive mask per head.  Both products are dense contractions, so
 // they run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
 //
-// Work split.  A workgroup is 4 waves x 32 query rows; the 128 rows are the G
+// Work split.  A workgroup holds 4 x 32 query rows (one wave per 32 rows, or two
+// waves sharing them for D = 256, see Cfg); the 128 rows are the G
 // query heads of one KV head times qpos = 128 / G chunk rows, so every K/V
 // tile staged in LDS serves the whole GQA group (read from HBM once per query
 // tile).  Workgroups are mapped so that consecutive query tiles of one
@@ -115,21 +116,25 @@ __device__ __forceinline__ int kswz(int r) {
 }
 __device__ __forceinline__ int vswz(int r) { return (r & 3) << 1; }
 
-// Per head size: keys per tile, LDS ring stages, waves per SIMD.  A stage holds
-// one K and one V tile (KT x D bf16 each).
+// Per head size: keys per tile, LDS ring stages, waves per SIMD, and the number of
+// wave groups the output dims are split over (DSPLIT).  A stage holds one K and one V
+// tile (KT x D bf16 each).  With DSPLIT = 2 a workgroup has 8 waves: waves w and
+// w + 4 own the same 32 query rows, both form the full scores and probabilities, and
+// each accumulates half of the output dims -- a 256-dim accumulator per wave would
+// leave room for only one wave per SIMD and nothing to hide LDS and MFMA latency.
 template <int D>
 struct Cfg;
 template <>
 struct Cfg<64> {
-  static constexpr int KT = 64, STAGES = 4, WAVES = 2;
+  static constexpr int KT = 64, STAGES = 4, WAVES = 2, DSPLIT = 1;
 };
 template <>
 struct Cfg<128> {
-  static constexpr int KT = 64, STAGES = 2, WAVES = 2;
+  static constexpr int KT = 64, STAGES = 2, WAVES = 2, DSPLIT = 1;
 };
 template <>
 struct Cfg<256> {
-  static constexpr int KT = 32, STAGES = 4, WAVES = 1;
+  static constexpr int KT = 32, STAGES = 4, WAVES = 2, DSPLIT = 2;
 };
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
@@ -152,21 +157,24 @@ __device__ __forceinline__ void wait_tiles_after(int n) {
 }
 
 template <int D, bool EXPLICIT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256 * Cfg<D>::DSPLIT)
     __attribute__((amdgpu_waves_per_eu(Cfg<D>::WAVES, Cfg<D>::WAVES)))
     k_attn_mfma(AttnParams p) {
   constexpr int KT = Cfg<D>::KT;
   constexpr int STAGES = Cfg<D>::STAGES;
+  constexpr int DSPLIT = Cfg<D>::DSPLIT;
+  constexpr int NW = 4 * DSPLIT;     // waves per workgroup
   constexpr int CPR = D / 8;         // 16-byte chunks per row
   constexpr int NK = KT * CPR;       // chunks per tile (K or V)
-  constexpr int NL = NK / 256;       // direct-to-LDS loads per wave per tile per tensor
+  constexpr int NL = NK / (64 * NW); // direct-to-LDS loads per wave per tile per tensor
   constexpr int RPI = 64 / CPR;      // rows covered by one wave-wide 1 KB load
   constexpr int NS = D / 16;         // k-steps of QK^T
   constexpr int NKB = KT / 32;       // 32-key blocks per tile
   constexpr int NDB = D / 32;        // 32-dim blocks of the output
+  constexpr int NDW = NDB / DSPLIT;  // ... accumulated by one wave
   constexpr int NPT = KT / 16;       // k-steps of PV
   constexpr int TILE = KT * D;       // bf16 elements of one K (or V) tile
-  static_assert(NK % 256 == 0, "tile must split evenly over 4 waves");
+  static_assert(NK % (64 * NW) == 0, "tile must split evenly over the waves");
   static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
 
   // ring of STAGES x (K tile, V tile)
@@ -177,6 +185,7 @@ __global__ void __launch_bounds__(256)
   const int wave = tid >> 6;
   const int n = lane & 31;
   const int hh = lane >> 5;
+  const int dgrp = wave / 4;         // which NDW dim blocks this wave accumulates
 
   // XCD-aware order: the hardware deals workgroups round-robin over 8 XCDs;
   // give each XCD a contiguous range of work items.
@@ -190,7 +199,7 @@ __global__ void __launch_bounds__(256)
   const int b = bg / p.nKV;
   const int g = bg % p.nKV;
 
-  const int r = wave * 32 + n;
+  const int r = (wave & 3) * 32 + n;
   const int hl = r / p.qpos;
   const int i_min = qtile * p.qpos;
   const int i = i_min + r % p.qpos;
@@ -229,9 +238,9 @@ __global__ void __launch_bounds__(256)
     }
   }
 
-  f32x16 oacc[NDB];
+  f32x16 oacc[NDW];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDW; ++db)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
@@ -404,7 +413,7 @@ __global__ void __launch_bounds__(256)
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDW; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
     }
@@ -434,8 +443,8 @@ __global__ void __launch_bounds__(256)
     // ---- O^T += V^T P^T, V^T gathered by transpose reads (one batch per 32 dims)
     const uint32_t vbase = lds_addr(Vs) + 2 * (v_key * D);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const uint32_t va = vbase + 2 * ((((4 * db + v_cl) ^ v_sw) << 3) + v_el);
+    for (int db = 0; db < NDW; ++db) {
+      const uint32_t va = vbase + 2 * ((((4 * (dgrp * NDW + db) + v_cl) ^ v_sw) << 3) + v_el);
       u32x2 w[2 * NPT];
 #pragma unroll
       for (int t = 0; t < NPT; ++t) {
@@ -489,10 +498,10 @@ __global__ void __launch_bounds__(256)
     uint16_t *O = static_cast<uint16_t *>(p.out) + orow * D;
     const float inv = real ? 1.f / l_tot : 0.f;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+    for (int db = 0; db < NDW; ++db) {
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const int d = 32 * db + 8 * rq + 4 * hh;
+        const int d = 32 * (dgrp * NDW + db) + 8 * rq + 4 * hh;
         const float o0 = oacc[db][4 * rq + 0] * inv, o1 = oacc[db][4 * rq + 1] * inv;
         const float o2 = oacc[db][4 * rq + 2] * inv, o3 = oacc[db][4 * rq + 3] * inv;
         const u32x2 w = {pack_bf16x2(real ? o0 : 0.f, real ? o1 : 0.f),
@@ -504,10 +513,10 @@ __global__ void __launch_bounds__(256)
     const size_t rows = static_cast<size_t>(p.B) * p.H * p.C;
     float *WO = p.wo + (split * rows + orow) * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+    for (int db = 0; db < NDW; ++db) {
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const int d = 32 * db + 8 * rq + 4 * hh;
+        const int d = 32 * (dgrp * NDW + db) + 8 * rq + 4 * hh;
         float4 w;
         w.x = real ? oacc[db][4 * rq + 0] : 0.f;
         w.y = real ? oacc[db][4 * rq + 1] : 0.f;
@@ -516,7 +525,7 @@ __global__ void __launch_bounds__(256)
         *reinterpret_cast<float4 *>(WO + d) = w;
       }
     }
-    if (hh == 0) {
+    if (hh == 0 && dgrp == 0) {
       float *ML = p.wml + (split * rows + orow) * 2;
       ML[0] = real ? m_run : -INFINITY;
       ML[1] = real ? l_tot : 0.f;
@@ -528,10 +537,11 @@ template <int D>
 hipError_t launch_d(const AttnParams &p, hipStream_t s) {
   const unsigned blocks = static_cast<unsigned>(p.qtiles) * p.splits * p.B * p.nKV;
   if (blocks == 0) return hipSuccess;
+  const dim3 threads(256 * Cfg<D>::DSPLIT);
   if (p.mask)
-    hipLaunchKernelGGL((k_attn_mfma<D, true>), dim3(blocks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_attn_mfma<D, true>), dim3(blocks), threads, 0, s, p);
   else
-    hipLaunchKernelGGL((k_attn_mfma<D, false>), dim3(blocks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_attn_mfma<D, false>), dim3(blocks), threads, 0, s, p);
   return hipGetLastError();
 }
 

@@ -204,9 +204,13 @@ __global__ void __launch_bounds__(256) k_attn_valu(AttnParams p, int D) {
 }
 
 // Merge key-split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, for
-// VEC consecutive output columns per thread; pad rows are written as zeros.
+// VEC consecutive output columns per thread; pad rows are written as zeros.  The
+// partials are fetched SB splits at a time (independent loads in flight together)
+// and folded into a running maximum, so a row costs ceil(splits / SB) memory round
+// trips instead of one per split.
 template <typename T, int VEC>
 __global__ void __launch_bounds__(256) k_attn_combine(AttnParams p, int D) {
+  constexpr int SB = 8;
   const size_t rows = static_cast<size_t>(p.B) * p.H * p.C;
   const int per_row = D / VEC;
   const size_t total = rows * per_row;
@@ -222,28 +226,51 @@ __global__ void __launch_bounds__(256) k_attn_combine(AttnParams p, int D) {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) res[e] = 0.f;
     if (i < nv) {
-      float M = -INFINITY;
-      for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.wml[(s * rows + row) * 2]);
-      float l = 0.f, o[VEC];
+      float M = -INFINITY, l = 0.f, o[VEC];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) o[e] = 0.f;
-      if (M != -INFINITY) {
-        for (int s = 0; s < p.splits; ++s) {
-          const float2 ml = *reinterpret_cast<const float2 *>(p.wml + (s * rows + row) * 2);
-          const float wgt = __builtin_amdgcn_exp2f(ml.x - M);
-          l = fmaf(wgt, ml.y, l);
-          const float *src = p.wo + (s * rows + row) * D + d0;
-          if constexpr (VEC == 4) {
-            const float4 v = *reinterpret_cast<const float4 *>(src);
-            o[0] = fmaf(wgt, v.x, o[0]);
-            o[1] = fmaf(wgt, v.y, o[1]);
-            o[2] = fmaf(wgt, v.z, o[2]);
-            o[3] = fmaf(wgt, v.w, o[3]);
-          } else {
+      for (int s0 = 0; s0 < p.splits; s0 += SB) {
+        float mv[SB], lv[SB], ov[SB][VEC];
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) o[e] = fmaf(wgt, src[e], o[e]);
+        for (int j = 0; j < SB; ++j) {
+          mv[j] = -INFINITY;
+          lv[j] = 0.f;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) ov[j][e] = 0.f;
+          if (s0 + j < p.splits) {
+            const size_t sr = (s0 + j) * rows + row;
+            const float2 ml = *reinterpret_cast<const float2 *>(p.wml + sr * 2);
+            mv[j] = ml.x;
+            lv[j] = ml.y;
+            const float *src = p.wo + sr * D + d0;
+            if constexpr (VEC == 4) {
+              const float4 v = *reinterpret_cast<const float4 *>(src);
+              ov[j][0] = v.x;
+              ov[j][1] = v.y;
+              ov[j][2] = v.z;
+              ov[j][3] = v.w;
+            } else {
+#pragma unroll
+              for (int e = 0; e < VEC; ++e) ov[j][e] = src[e];
+            }
           }
         }
+        float Mn = M;
+#pragma unroll
+        for (int j = 0; j < SB; ++j) Mn = fmaxf(Mn, mv[j]);
+        if (Mn == -INFINITY) continue;  // nothing attended so far
+        const float a = __builtin_amdgcn_exp2f(M - Mn);  // 0 while M = -inf
+        l *= a;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[e] *= a;
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+          const float wgt = __builtin_amdgcn_exp2f(mv[j] - Mn);
+          l = fmaf(wgt, lv[j], l);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) o[e] = fmaf(wgt, ov[j][e], o[e]);
+        }
+        M = Mn;
       }
       const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll

@@ -33,12 +33,20 @@
 // exceeds it by more than 2^8 (exact: numerator and denominator share it), so
 // the O accumulator is rarely rescaled.
 //
-// Loads.  K/V tiles stream into a ring of LDS stages with direct-to-LDS loads
-// (global_load_lds_dwordx4, 1 KB per wave instruction), STAGES - 1 tiles ahead
-// of the one being computed, without passing through registers; the waits on
-// them are explicit (vmcnt) followed by a plain s_barrier.  Chunk rows come from
-// the caller's k_new / v_new, past rows from the cache slots.  Tiles outside
-// the window or past the last real row are skipped.
+// Loads.  K/V tiles -- and, with an explicit mask, the tile's 128 x KT block of
+// mask values -- stream into a ring of LDS stages with direct-to-LDS loads
+// (global_load_lds, 1 KB per wave instruction for K/V, 256 bytes for the mask),
+// STAGES - 1 tiles ahead of the one being computed, without passing through
+// registers.  The loads of the next tile are spread between the MFMAs of this
+// tile's QK^T, so the issuing wave does not stall on the memory pipeline; the
+// waits on them are explicit (vmcnt) followed by a plain s_barrier.  Mask values
+// never wait in registers behind in-flight tile loads (loads complete in order).
+// Chunk rows come from the caller's k_new / v_new, past rows from the cache
+// slots.  Tiles outside the window or past the last real row are skipped.
+//
+// Pipelining inside a tile: K fragments are read one k-step ahead of the MFMAs,
+// and the V^T transpose reads of dim block db + 1 are in flight while block db
+// multiplies (the reads of block 0 overlap the softmax arithmetic).
 #include "attn_common.h"
 
 namespace cp {
@@ -89,6 +97,45 @@ __device__ __forceinline__ u32x2 tr_read(uint32_t addr) {
   return r;
 }
 
+// Lanes l and l ^ 32 hold the two halves of one query row's keys: combine them with
+// one v_permlane32_swap (no LDS round trip).  Both lanes get the same value.
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),
+                                                  __builtin_bit_cast(unsigned, v), false, false);
+  return fmaxf(__builtin_bit_cast(float, static_cast<unsigned>(r[0])),
+               __builtin_bit_cast(float, static_cast<unsigned>(r[1])));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),
+                                                  __builtin_bit_cast(unsigned, v), false, false);
+  return __builtin_bit_cast(float, static_cast<unsigned>(r[0])) +
+         __builtin_bit_cast(float, static_cast<unsigned>(r[1]));
+}
+
+// s_waitcnt lgkmcnt(N) that also marks the CNT transpose-read results w[] as written
+// by it, so no use of them is scheduled before the wait.  LDS operations complete in
+// order: the N reads issued after w[] may stay in flight.
+template <int N, int CNT>
+__device__ __forceinline__ void lds_wait_keep(u32x2 *w) {
+  static_assert(CNT == 4 || CNT == 8, "transpose reads per dim block");
+  static_assert(N == 0 || N == CNT, "reads left in flight");
+  if constexpr (CNT == 8) {
+    if constexpr (N == 0)
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5]),
+                     "+v"(w[6]), "+v"(w[7]));
+    else
+      asm volatile("s_waitcnt lgkmcnt(8)"
+                   : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5]),
+                     "+v"(w[6]), "+v"(w[7]));
+  } else {
+    if constexpr (N == 0)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
+    else
+      asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
+  }
+}
+
 __device__ __forceinline__ f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -116,26 +163,53 @@ __device__ __forceinline__ int kswz(int r) {
 }
 __device__ __forceinline__ int vswz(int r) { return (r & 3) << 1; }
 
-// Per head size: keys per tile, LDS ring stages, waves per SIMD, and the number of
-// wave groups the output dims are split over (DSPLIT).  A stage holds one K and one V
-// tile (KT x D bf16 each).  With DSPLIT = 2 a workgroup has 8 waves: waves w and
+// Per head size and mask mode: keys per tile, LDS ring stages, waves per SIMD, and
+// the number of wave groups the output dims are split over (DSPLIT).  A stage holds
+// one K and one V tile (KT x D bf16 each) and, with an explicit mask, the tile's
+// 128 x KT fp32 mask block.  With DSPLIT = 2 a workgroup has 8 waves: waves w and
 // w + 4 own the same 32 query rows, both form the full scores and probabilities, and
 // each accumulates half of the output dims -- a 256-dim accumulator per wave would
 // leave room for only one wave per SIMD and nothing to hide LDS and MFMA latency.
-template <int D>
+template <int D, bool EX>
 struct Cfg;
 template <>
-struct Cfg<64> {
+struct Cfg<64, false> {
   static constexpr int KT = 64, STAGES = 4, WAVES = 2, DSPLIT = 1;
 };
 template <>
-struct Cfg<128> {
+struct Cfg<64, true> {
+  static constexpr int KT = 32, STAGES = 3, WAVES = 2, DSPLIT = 1;
+};
+template <>
+struct Cfg<128, false> {
   static constexpr int KT = 64, STAGES = 2, WAVES = 2, DSPLIT = 1;
 };
 template <>
-struct Cfg<256> {
+struct Cfg<128, true> {
+  static constexpr int KT = 32, STAGES = 2, WAVES = 2, DSPLIT = 1;
+};
+template <>
+struct Cfg<256, false> {
   static constexpr int KT = 32, STAGES = 4, WAVES = 2, DSPLIT = 2;
 };
+template <>
+struct Cfg<256, true> {
+  static constexpr int KT = 32, STAGES = 3, WAVES = 2, DSPLIT = 2;
+};
+
+// One wave-wide 4-byte direct-to-LDS load (mask blocks: no alignment beyond 4 bytes).
+__device__ __forceinline__ void dma4(const float *src, float *lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_base, 4, 0, 0);
+#else
+  (void)src;
+  (void)lds_base;
+#endif
+}
+
+// Swizzle of the 16-byte chunks of row r of a 128 x 32 fp32 mask block (rows of
+// 128 bytes: rows r and r + 1 share a 256-byte bank line).
+__device__ __forceinline__ int mswz(int r) { return (r >> 1) & 7; }
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
 template <int N>
@@ -156,13 +230,18 @@ __device__ __forceinline__ void wait_tiles_after(int n) {
   }
 }
 
-template <int D, bool EXPLICIT>
-__global__ void __launch_bounds__(256 * Cfg<D>::DSPLIT)
-    __attribute__((amdgpu_waves_per_eu(Cfg<D>::WAVES, Cfg<D>::WAVES)))
+// EXPLICIT: the additive mask comes from memory.  EXT: use the explicit-mask tiling
+// (set with EXPLICIT, and for the in-kernel rule under CP_ATTN_FULL_TILES so that both
+// modes see the same key partition).
+template <int D, bool EXPLICIT, bool EXT>
+__global__ void __launch_bounds__((256 * Cfg<D, EXT>::DSPLIT))
+    __attribute__((amdgpu_waves_per_eu(Cfg<D, EXT>::WAVES, Cfg<D, EXT>::WAVES)))
     k_attn_mfma(AttnParams p) {
-  constexpr int KT = Cfg<D>::KT;
-  constexpr int STAGES = Cfg<D>::STAGES;
-  constexpr int DSPLIT = Cfg<D>::DSPLIT;
+  static_assert(EXT || !EXPLICIT, "explicit masks use the explicit tiling");
+  using CF = Cfg<D, EXT>;
+  constexpr int KT = CF::KT;
+  constexpr int STAGES = CF::STAGES;
+  constexpr int DSPLIT = CF::DSPLIT;
   constexpr int NW = 4 * DSPLIT;     // waves per workgroup
   constexpr int CPR = D / 8;         // 16-byte chunks per row
   constexpr int NK = KT * CPR;       // chunks per tile (K or V)
@@ -174,11 +253,18 @@ __global__ void __launch_bounds__(256 * Cfg<D>::DSPLIT)
   constexpr int NDW = NDB / DSPLIT;  // ... accumulated by one wave
   constexpr int NPT = KT / 16;       // k-steps of PV
   constexpr int TILE = KT * D;       // bf16 elements of one K (or V) tile
+  constexpr int MT = EXPLICIT ? 128 * KT * 2 : 0;     // mask block (in 16-bit units)
+  constexpr int STAGE = 2 * TILE + MT;
+  constexpr int NMK = EXPLICIT ? 128 * KT / (64 * NW) : 0;  // mask loads per wave per tile
+  constexpr int ND = 2 * NL + NMK;   // direct-to-LDS loads per wave per tile
+  static_assert(!EXPLICIT || (KT == 32 && (128 * KT) % (64 * NW) == 0), "mask block split");
   static_assert(NK % (64 * NW) == 0, "tile must split evenly over the waves");
   static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
 
-  // ring of STAGES x (K tile, V tile)
-  __shared__ __attribute__((aligned(1024))) uint16_t ring[STAGES * 2 * TILE];
+  // ring of STAGES x (K tile, V tile[, mask block])
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[STAGES * STAGE];
+  // explicit mask: element offset of the mask row of each of the 128 query rows
+  __shared__ int64_t mtab[EXPLICIT ? 128 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -225,17 +311,17 @@ __global__ void __launch_bounds__(256 * Cfg<D>::DSPLIT)
   const int wi_lo = wave_min_i(real_row ? i : 0x7fffffff);
   const int wi_hi = wave_max_i(real_row ? i : -1);
 
-  // Q^T fragments: lane holds q[row n][16 s + 8 hh .. + 7] for every k-step s.
-  bf16x8 qf[NS];
-  {
-    const uint16_t *Q = static_cast<const uint16_t *>(p.q) +
-                        ((static_cast<size_t>(b) * p.H + head) * p.C + irow) * D + 8 * hh;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row_ok) v = *reinterpret_cast<const u32x4 *>(Q + 16 * s);
-      qf[s] = __builtin_bit_cast(bf16x8, v);
+  if constexpr (EXPLICIT) {
+    // mask row of query row t (rows past the tile's end read a valid row; their
+    // results are discarded), then make the table visible to every wave.
+    if (tid < 128) {
+      const int hl_t = imin(tid / p.qpos, p.G - 1);
+      const int i_t = imin(i_min + tid % p.qpos, p.C - 1);
+      mtab[tid] = b * p.mbs + static_cast<int64_t>(g * p.G + hl_t) * p.mhs +
+                  static_cast<int64_t>(i_t) * p.mld;
     }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
   }
 
   f32x16 oacc[NDW];
@@ -270,38 +356,59 @@ __global__ void __launch_bounds__(256 * Cfg<D>::DSPLIT)
   // the tile: rows q * RPI + lane / CPR, physical chunk lane % CPR, which holds the
   // row's logical chunk (physical ^ swizzle).  Rows outside the tile's valid range
   // read a valid row instead; their scores are masked to -inf.
-  auto issue = [&](int u, uint16_t *kdst, uint16_t *vdst) __attribute__((always_inline)) {
-    int first;
+  int koff[NL], voff[NL];
+#pragma unroll
+  for (int e = 0; e < NL; ++e) {
+    const int row = (wave * NL + e) * RPI + lane / CPR, phys = lane % CPR;
+    koff[e] = (phys ^ kswz<D>(row)) << 3;
+    voff[e] = (phys ^ vswz(row)) << 3;
+  }
+  // source rows (cache slot or chunk row) of this wave's loads of tile u
+  auto plan = [&](int u, int *srow, int &first, int &lim) __attribute__((always_inline)) {
     const bool chunk = ts.at(u, KT, &first);
-    const int lim = chunk ? p.C : gl.L;
-    int c_ns = imax(first, gl.ns), s_ns = 0;
+    lim = chunk ? p.C : gl.L;
+    const int c_ns = imax(first, gl.ns);
+    int s_ns = 0;
     if (!chunk && p.ring && !small_ring && c_ns < gl.L)
       s_ns = slot_of(gl.lo + (c_ns - gl.ns), p.cap, 1, p.sink);
 #pragma unroll
     for (int e = 0; e < NL; ++e) {
-      const int q = wave * NL + e;
-      const int row = q * RPI + lane / CPR, phys = lane % CPR;
-      int col = first + row;
-      if (col >= lim) col = lim - 1;
-      const uint16_t *kr, *vr;
-      if (chunk) {
-        kr = KN + static_cast<size_t>(col) * D;
-        vr = VN + static_cast<size_t>(col) * D;
-      } else {
-        int sl;
-        if (!p.ring || col < gl.ns) {
-          sl = col;
-        } else if (!small_ring) {
+      const int row = (wave * NL + e) * RPI + lane / CPR;
+      const int col = imin(first + row, lim - 1);
+      int sl = col;
+      if (!chunk && p.ring && col >= gl.ns) {
+        if (!small_ring) {
           sl = s_ns + (col - c_ns);
           if (sl >= p.cap) sl -= R;
         } else {
           sl = slot_of(gl.lo + (col - gl.ns), p.cap, 1, p.sink);
         }
-        kr = KC + static_cast<size_t>(sl) * D;
-        vr = VC + static_cast<size_t>(sl) * D;
       }
-      if (kdst) dma16(kr + ((phys ^ kswz<D>(row)) << 3), kdst + q * 512);
-      if (vdst) dma16(vr + ((phys ^ vswz(row)) << 3), vdst + q * 512);
+      srow[e] = sl;
+    }
+    return chunk;
+  };
+  // load j of a tile into ring stage st: j < NL K rows, j < 2 NL V rows, else 256
+  // bytes of the mask block (float P = q * 64 + lane: row P / 32, physical chunk
+  // (P % 32) / 4 holding the row's logical chunk physical ^ mswz(row), columns
+  // clamped into the valid range -- those past it are masked to -inf)
+  auto dma = [&](int j, bool chunk, const int *srow, int first, int lim, uint16_t *st)
+                 __attribute__((always_inline)) {
+    if (j < 2 * NL) {
+      const int e = j < NL ? j : j - NL;
+      const int q = wave * NL + e;
+      const size_t r = static_cast<size_t>(srow[e]) * D;
+      if (j < NL)
+        dma16((chunk ? KN : KC) + r + koff[e], st + q * 512);
+      else
+        dma16((chunk ? VN : VC) + r + voff[e], st + TILE + q * 512);
+    } else if constexpr (EXPLICIT) {
+      const int q = wave * NMK + (j - 2 * NL);
+      const int P = q * 64 + lane;
+      const int row = P >> 5, pp = P & 31;
+      const int col = imin(first + 4 * ((pp >> 2) ^ mswz(row)) + (pp & 3), lim - 1);
+      const int64_t mcol = (chunk ? static_cast<int64_t>(gl.L) : 0) + col;
+      dma4(p.mask + mtab[row] + mcol, reinterpret_cast<float *>(st + 2 * TILE) + q * 64);
     }
   };
 
@@ -313,57 +420,110 @@ __global__ void __launch_bounds__(256 * Cfg<D>::DSPLIT)
   const int v_cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // chunk within a 32-dim block
   const int v_el = 4 * (lane & 1);
 
-  const float *mrow = nullptr;
-  if (EXPLICIT && row_ok)
-    mrow = p.mask + b * p.mbs + head * p.mhs + static_cast<int64_t>(irow) * p.mld;
   const int qabs = seen + i;
 
-  // S^T = K Q^T for the tile whose K sits at Ks
-  auto qk = [&](const uint16_t *Ks, f32x16 (&sacc)[NKB]) __attribute__((always_inline)) {
+  // In-kernel rule for this lane's row as column ranges.  A past column c attends
+  // iff c < pa1 (sink rows; for a global cache the first `sink` positions) or
+  // c >= pb0 (inside the window); a chunk row j iff j < cb1 (causal, real) and
+  // (j < ca1 (a sink position) or j >= cb0 (inside the window)).
+  int pa1 = 0x7fffffff, pb0 = 0, ca1 = 0x7fffffff, cb0 = 0;
+  const int cb1 = imin(i, nv - 1) + 1;
+  if (!EXPLICIT && p.window > 0) {
+    pa1 = p.ring ? gl.ns : p.sink;
+    pb0 = qabs - p.window + 1 - gl.lo + gl.ns;
+    ca1 = p.sink - seen;
+    cb0 = i - p.window + 1;
+  }
+
+  // V^T operand reads of one 32-dim block (2 * NPT transpose reads)
+  auto v_reads = [&](uint32_t vbase, int db, u32x2 *w) __attribute__((always_inline)) {
+    const uint32_t va = vbase + 2 * ((((4 * (dgrp * NDW + db) + v_cl) ^ v_sw) << 3) + v_el);
+#pragma unroll
+    for (int t = 0; t < NPT; ++t) {
+      w[2 * t] = tr_read(va + 2 * (16 * t * D));
+      w[2 * t + 1] = tr_read(va + 2 * ((16 * t + 8) * D));
+    }
+  };
+
+  // tile u lives in stage u % STAGES of a ring of (K, V) tiles (a key split starts
+  // at u0 > 0)
+  for (int j = 0; j < STAGES - 1; ++j)
+    if (u0 + j < u1) {
+      int srow[NL], f0, l0;
+      const bool ch = plan(u0 + j, srow, f0, l0);
+      uint16_t *st = ring + ((u0 + j) % STAGES) * STAGE;
+#pragma unroll
+      for (int l = 0; l < ND; ++l) dma(l, ch, srow, f0, l0, st);
+    }
+  // Q^T fragments: lane holds q[row n][16 s + 8 hh .. + 7] for every k-step s.  Loaded
+  // after the first tiles' loads are on their way, so that the two latencies overlap.
+  bf16x8 qf[NS];
+  {
+    const uint16_t *Q = static_cast<const uint16_t *>(p.q) +
+                        ((static_cast<size_t>(b) * p.H + head) * p.C + irow) * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row_ok) v = *reinterpret_cast<const u32x4 *>(Q + 16 * s);
+      qf[s] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  for (int u = u0; u < u1; ++u) {
+    // tile u has landed in this wave's share of the ring once at most the loads of
+    // the tiles issued after it are outstanding; the barrier makes that true for all
+    // waves and also guarantees every wave has finished reading the stage refilled
+    wait_tiles_after<ND, STAGES>(imin(u1 - 1, u + STAGES - 2) - u);
+    __builtin_amdgcn_s_barrier();
+    const uint16_t *Ks = ring + (u % STAGES) * STAGE;
+    const uint16_t *Vs = Ks + TILE;
+
+    // the tile STAGES - 1 ahead is loaded while this one's QK^T runs
+    const int w_pf = u + STAGES - 1;
+    const bool pf = w_pf < u1;
+    int srow[NL], pfirst = 0, plim = 1;
+    bool pch = false;
+#pragma unroll
+    for (int e = 0; e < NL; ++e) srow[e] = 0;
+    if (pf) pch = plan(w_pf, srow, pfirst, plim);
+    uint16_t *pst = ring + (w_pf % STAGES) * STAGE;
+
+    // ---- S^T = K Q^T, K fragments read one k-step ahead, loads spread over the steps
+    f32x16 sacc[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
+    u32x4 kf[2][NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+      kf[0][kb] = *reinterpret_cast<const u32x4 *>(&Ks[(32 * kb + n) * D + ((hh ^ k_sw) << 3)]);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const int off = ((2 * s + hh) ^ k_sw) << 3;
+      if (s + 1 < NS) {
+        const int off = ((2 * (s + 1) + hh) ^ k_sw) << 3;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const u32x4 a = *reinterpret_cast<const u32x4 *>(&Ks[(32 * kb + n) * D + off]);
-        sacc[kb] = mfma(__builtin_bit_cast(bf16x8, a), qf[s], sacc[kb]);
+        for (int kb = 0; kb < NKB; ++kb)
+          kf[(s + 1) & 1][kb] = *reinterpret_cast<const u32x4 *>(&Ks[(32 * kb + n) * D + off]);
       }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        sacc[kb] = mfma(__builtin_bit_cast(bf16x8, kf[s & 1][kb]), qf[s], sacc[kb]);
+#pragma unroll
+      for (int j = s * ND / NS; j < (s + 1) * ND / NS; ++j)
+        if (pf) dma(j, pch, srow, pfirst, plim, pst);
     }
-  };
 
-  // mask, online softmax and O^T += V^T P^T for tile u (scores in sacc, V at Vs)
-  auto softmax_pv = [&](int u, f32x16 (&sacc)[NKB], const uint16_t *Vs)
-                            __attribute__((always_inline)) {
+    // V^T reads of the first dim block go out before the softmax needs the ALUs
+    const uint32_t vbase = lds_addr(Vs) + 2 * (v_key * D);
+    u32x2 wv[2][2 * NPT];
+    v_reads(vbase, 0, wv[0]);
+
     int first;
     const bool chunk = ts.at(u, KT, &first);
     // ---- tile classification (wave-uniform): does every real row of this wave
     // attend every key of the tile?  Then no mask work at all.
     const int lim = chunk ? p.C : gl.L;
-    const int64_t mbase = chunk ? static_cast<int64_t>(gl.L) + first : first;
-    // additive bias of key kk of this lane's row (explicit mask or rule), -inf out of range
-    auto bias4 = [&](int kk, float *a4) __attribute__((always_inline)) {
-      if (EXPLICIT) {
-        if (mrow && p.mask_vec4 && first + kk + 3 < lim && ((mbase + kk) & 3) == 0) {
-          const float4 mv = *reinterpret_cast<const float4 *>(mrow + mbase + kk);
-          a4[0] = mv.x;
-          a4[1] = mv.y;
-          a4[2] = mv.z;
-          a4[3] = mv.w;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            a4[e] = first + kk + e < lim ? (mrow ? mrow[mbase + kk + e] : 0.f) : -INFINITY;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          a4[e] = inkernel_add(chunk, first + kk + e, gl, seen, p.C, nv, qabs, p.window, p.sink);
-      }
-    };
     bool visible;
     if (EXPLICIT || p.full_tiles) {
       visible = false;  // the mask is applied to every tile (same expressions in both modes)
@@ -390,22 +550,56 @@ __global__ void __launch_bounds__(256 * Cfg<D>::DSPLIT)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kb][e]);
       mt *= p.sl2e;
-    } else {
+    } else if constexpr (EXPLICIT) {
+      // mask block of this stage, row r of this lane; keys past the valid range -inf
+      const float *Ms = reinterpret_cast<const float *>(Ks + 2 * TILE) + r * KT;
+      const int xl = lim - first - 4 * hh;
+      const int msw = mswz(r);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
-          float a4[4];
-          bias4(32 * kb + 8 * rq + 4 * hh, a4);
+          const float4 mv =
+              *reinterpret_cast<const float4 *>(Ms + 4 * ((8 * kb + 2 * rq + hh) ^ msw));
+          const float m4[4] = {mv.x, mv.y, mv.z, mv.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float tv = fmaf(sacc[kb][4 * rq + e], p.sl2e, a4[e] * kLog2e);
+            const int k = 32 * kb + 8 * rq + e;
+            const float a = k < xl ? m4[e] : -INFINITY;
+            const float tv = fmaf(sacc[kb][4 * rq + e], p.sl2e, a * kLog2e);
             sacc[kb][4 * rq + e] = tv;
             mt = fmaxf(mt, tv);
           }
         }
+    } else {
+      // column c of key k of this lane is base + k; compare against range bounds
+      // shifted by base once per tile
+      const int base = first + 4 * hh;
+      const int xl = lim - base;
+      int xa, xb, xc = 0x7fffffff;
+      if (chunk) {
+        xa = ca1 == 0x7fffffff ? 0x7fffffff : ca1 - base;
+        xb = cb0 - base;
+        xc = cb1 - base;
+      } else {
+        xa = pa1 == 0x7fffffff ? 0x7fffffff : pa1 - base;
+        xb = pb0 - base;
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int k = 32 * kb + 8 * rq + e;
+            const bool att = (k < xc) & ((k < xa) | (k >= xb));
+            const float a = k < xl ? (att ? 0.f : kMasked) : -INFINITY;
+            const float tv = fmaf(sacc[kb][4 * rq + e], p.sl2e, a * kLog2e);
+            sacc[kb][4 * rq + e] = tv;
+            mt = fmaxf(mt, tv);
+          }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = pair_max(mt);
     const bool raise = mt > m_run + kRescaleSlack;
     if (__any(raise)) {
       const float m_new = raise ? mt : m_run;
@@ -440,57 +634,26 @@ __global__ void __launch_bounds__(256 * Cfg<D>::DSPLIT)
       }
     }
 
-    // ---- O^T += V^T P^T, V^T gathered by transpose reads (one batch per 32 dims)
-    const uint32_t vbase = lds_addr(Vs) + 2 * (v_key * D);
+    // ---- O^T += V^T P^T: the reads of dim block db + 1 are in flight while block db
+    // multiplies
 #pragma unroll
     for (int db = 0; db < NDW; ++db) {
-      const uint32_t va = vbase + 2 * ((((4 * (dgrp * NDW + db) + v_cl) ^ v_sw) << 3) + v_el);
-      u32x2 w[2 * NPT];
-#pragma unroll
-      for (int t = 0; t < NPT; ++t) {
-        w[2 * t] = tr_read(va + 2 * (16 * t * D));
-        w[2 * t + 1] = tr_read(va + 2 * ((16 * t + 8) * D));
-      }
-      if constexpr (NPT == 4) {
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5]),
-                       "+v"(w[6]), "+v"(w[7]));
+      u32x2 *cur = wv[db & 1];
+      if (db + 1 < NDW) {
+        v_reads(vbase, db + 1, wv[(db + 1) & 1]);
+        lds_wait_keep<2 * NPT, 2 * NPT>(cur);
       } else {
-        static_assert(NPT == 2, "PV k-steps per tile");
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
+        lds_wait_keep<0, 2 * NPT>(cur);
       }
 #pragma unroll
       for (int t = 0; t < NPT; ++t) {
-        const u32x4 a = {w[2 * t][0], w[2 * t][1], w[2 * t + 1][0], w[2 * t + 1][1]};
+        const u32x4 a = {cur[2 * t][0], cur[2 * t][1], cur[2 * t + 1][0], cur[2 * t + 1][1]};
         oacc[db] = mfma(__builtin_bit_cast(bf16x8, a), pb[t], oacc[db]);
       }
     }
-  };
-
-  // tile u lives in stage u % STAGES of a ring of (K, V) tiles (a key split starts
-  // at u0 > 0)
-  for (int j = 0; j < STAGES - 1; ++j)
-    if (u0 + j < u1) {
-      uint16_t *st = ring + ((u0 + j) % STAGES) * 2 * TILE;
-      issue(u0 + j, st, st + TILE);
-    }
-  for (int u = u0; u < u1; ++u) {
-    // tile u has landed in this wave's share of the ring once at most the loads of
-    // the tiles issued after it are outstanding; the barrier makes that true for all
-    // waves and also guarantees every wave has finished reading the stage refilled
-    wait_tiles_after<2 * NL, STAGES>(imin(u1 - 1, u + STAGES - 2) - u);
-    __builtin_amdgcn_s_barrier();
-    if (u + STAGES - 1 < u1) {
-      uint16_t *st = ring + ((u + STAGES - 1) % STAGES) * 2 * TILE;
-      issue(u + STAGES - 1, st, st + TILE);
-    }
-    const uint16_t *Ks = ring + (u % STAGES) * 2 * TILE;
-    f32x16 sacc[NKB];
-    qk(Ks, sacc);
-    softmax_pv(u, sacc, Ks + TILE);
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   if (!row_ok) return;
   const bool real = any_real && i < nv;
   const size_t orow = (static_cast<size_t>(b) * p.H + head) * p.C + i;
@@ -537,11 +700,15 @@ template <int D>
 hipError_t launch_d(const AttnParams &p, hipStream_t s) {
   const unsigned blocks = static_cast<unsigned>(p.qtiles) * p.splits * p.B * p.nKV;
   if (blocks == 0) return hipSuccess;
-  const dim3 threads(256 * Cfg<D>::DSPLIT);
   if (p.mask)
-    hipLaunchKernelGGL((k_attn_mfma<D, true>), dim3(blocks), threads, 0, s, p);
+    hipLaunchKernelGGL((k_attn_mfma<D, true, true>), dim3(blocks),
+                       dim3(256 * Cfg<D, true>::DSPLIT), 0, s, p);
+  else if (p.full_tiles)
+    hipLaunchKernelGGL((k_attn_mfma<D, false, true>), dim3(blocks),
+                       dim3(256 * Cfg<D, true>::DSPLIT), 0, s, p);
   else
-    hipLaunchKernelGGL((k_attn_mfma<D, false>), dim3(blocks), threads, 0, s, p);
+    hipLaunchKernelGGL((k_attn_mfma<D, false, false>), dim3(blocks),
+                       dim3(256 * Cfg<D, false>::DSPLIT), 0, s, p);
   return hipGetLastError();
 }
 
@@ -560,8 +727,10 @@ hipError_t launch_attn_mfma(const AttnParams &p, int D, hipStream_t s) {
   }
 }
 
-int mfma_keys_per_tile(int D) {
-  return D == 256 ? Cfg<256>::KT : (D == 128 ? Cfg<128>::KT : Cfg<64>::KT);
+int mfma_keys_per_tile(int D, bool explicit_tiling) {
+  if (explicit_tiling)
+    return D == 256 ? Cfg<256, true>::KT : (D == 128 ? Cfg<128, true>::KT : Cfg<64, true>::KT);
+  return D == 256 ? Cfg<256, false>::KT : (D == 128 ? Cfg<128, false>::KT : Cfg<64, false>::KT);
 }
 
 }  // namespace cp

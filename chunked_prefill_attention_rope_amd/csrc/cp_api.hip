@@ -10,7 +10,7 @@
 #include "attn_common.h"
 
 namespace cp {
-int mfma_keys_per_tile(int D);
+int mfma_keys_per_tile(int D, bool explicit_tiling);
 
 namespace {
 
@@ -46,7 +46,7 @@ AttnPlan plan_attention(const cp_cache &c, const cp_attn_args &a, bool for_works
   int hgroups = 1;
   if (pl.mfma) {
     pl.qpos = 128 / G;
-    pl.kt = mfma_keys_per_tile(c.D);
+    pl.kt = mfma_keys_per_tile(c.D, a.mask != nullptr || (a.flags & CP_ATTN_FULL_TILES));
   } else {
     const int hb = G < 16 ? G : 16;
     hgroups = (G + hb - 1) / hb;

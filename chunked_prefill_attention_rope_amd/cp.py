@@ -20,7 +20,12 @@ OK, ERR_ARG, ERR_SHAPE, ERR_DTYPE, ERR_WINDOW, ERR_STATE, ERR_WORKSPACE, ERR_HIP
 DEV_OVERFLOW, DEV_NVALID, DEV_MASK_LD, DEV_ROLLBACK, DEV_SEEN = 1, 2, 4, 8, 16
 F32, BF16 = 0, 1
 ATTN_NO_SPLIT, ATTN_FORCE_GENERIC, ATTN_FULL_TILES = 1, 2, 4
-ABI_VERSION = 1
+
+
+def ATTN_SPLITS(n: int) -> int:
+    """CP_ATTN_SPLITS(n): force n key splits (bits 8..15 of the flags)."""
+    return (int(n) & 0xFF) << 8
+ABI_VERSION = 2
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libcp.so is not built ({LIB_PATH}); run "
@@ -47,7 +52,8 @@ class AttnArgs(ctypes.Structure):
                 ("mask_batch_stride", ctypes.c_int64), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("H", ctypes.c_int32),
                 ("C", ctypes.c_int32), ("window", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("flags", ctypes.c_uint32), ("reserved", ctypes.c_int32)]
+                ("flags", ctypes.c_uint32), ("reserved", ctypes.c_int32),
+                ("select_out", ctypes.c_void_p)]
 
 
 _vp, _i = ctypes.c_void_p, ctypes.c_int
@@ -57,6 +63,7 @@ _SIGS = {
     "cp_abi_version": (_i, []),
     "cp_struct_size": (ctypes.c_size_t, [_i]),
     "cp_rope_chunk": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
+    "cp_rope_qk_chunk": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "cp_kv_append": (_i, [_P(CacheDesc), _vp, _vp, _i, _vp, _vp]),
     "cp_snapshot_bytes": (ctypes.c_size_t, [_P(CacheDesc), _i]),
     "cp_kv_snapshot_padded_append": (_i, [_P(CacheDesc), _i, _vp, _P(SnapshotDesc), _vp]),
@@ -135,6 +142,27 @@ def rope_chunk(x: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor,
                               _opt(sin, "sin", torch.float32), B, Hx, C, D, cos.shape[0],
                               _dtype_code(x), _stream()), "cp_rope_chunk")
     return out
+
+
+def rope_qk_chunk(q: torch.Tensor, k: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor,
+                  q_out: Optional[torch.Tensor] = None,
+                  k_out: Optional[torch.Tensor] = None):
+    """cp_rope_qk_chunk: q [B, H, C, D] and k [B, nKV, C, D] rotated by one launch."""
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    if k_out is None:
+        k_out = torch.empty_like(k)
+    B, H, C, D = q.shape
+    if k.shape[0] != B or k.shape[2:] != q.shape[2:] or k.dtype != q.dtype:
+        raise ValueError("k must be [B, nKV, C, D] of q's dtype")
+    if q_out.shape != q.shape or q_out.dtype != q.dtype or k_out.shape != k.shape \
+            or k_out.dtype != k.dtype:
+        raise ValueError("outputs must match their inputs")
+    _check(_lib.cp_rope_qk_chunk(_dev(q, "q"), _dev(q_out, "q_out"), _dev(k, "k"),
+                                 _dev(k_out, "k_out"), _opt(cos, "cos", torch.float32),
+                                 _opt(sin, "sin", torch.float32), B, H, k.shape[1], C, D,
+                                 cos.shape[0], _dtype_code(q), _stream()), "cp_rope_qk_chunk")
+    return q_out, k_out
 
 
 # ----------------------------------------------------------------- KV cache
@@ -223,7 +251,8 @@ def kv_rollback_padded_append(cache: KVCache, snap: Snapshot) -> None:
 
 # ---------------------------------------------------------------- attention
 
-def _attn_args(cache, q, k_new, v_new, out, n_valid, mask, window, scale, workspace, flags):
+def _attn_args(cache, q, k_new, v_new, out, n_valid, mask, window, scale, workspace, flags,
+               select_out=None):
     B, H, C, D = q.shape
     if scale is None:
         scale = float(torch.tensor(1.0 / D ** 0.5, dtype=torch.float32))
@@ -242,7 +271,8 @@ def _attn_args(cache, q, k_new, v_new, out, n_valid, mask, window, scale, worksp
     return AttnArgs(_dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
                     _dev(out, "out") if out is not None else None,
                     _opt(n_valid, "n_valid", torch.int32), mptr, mld, mhs, mbs, ws_ptr, ws_bytes,
-                    H, C, int(window), float(scale), int(flags), 0)
+                    H, C, int(window), float(scale), int(flags), 0,
+                    _dev(select_out, "select_out") if select_out is not None else None)
 
 
 def attn_workspace_bytes(cache: KVCache, q: torch.Tensor, k_new: torch.Tensor,
@@ -257,11 +287,19 @@ def attn_chunk_with_past(cache: KVCache, q: torch.Tensor, k_new: torch.Tensor,
                          mask: Optional[torch.Tensor] = None, window: int = 0,
                          scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                          workspace: Optional[torch.Tensor] = None,
-                         flags: int = 0) -> torch.Tensor:
-    """cp_attn_chunk_with_past over the cache as it stands (before the append)."""
+                         flags: int = 0,
+                         select_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """cp_attn_chunk_with_past over the cache as it stands (before the append).
+
+    select_out [B, H, D] (optional) also receives the last real row of each (b, h).
+    """
     if out is None:
         out = torch.empty_like(q)
-    a = _attn_args(cache, q, k_new, v_new, out, n_valid, mask, window, scale, workspace, flags)
+    if select_out is not None and (select_out.dtype != q.dtype or
+                                   select_out.shape != (q.shape[0], q.shape[1], q.shape[3])):
+        raise ValueError("select_out must be [B, H, D] of q's dtype")
+    a = _attn_args(cache, q, k_new, v_new, out, n_valid, mask, window, scale, workspace, flags,
+                   select_out)
     _check(_lib.cp_attn_chunk_with_past(ctypes.byref(cache.desc), ctypes.byref(a), _stream()),
            "cp_attn_chunk_with_past")
     return out

@@ -15,6 +15,7 @@ namespace cp {
 struct AttnParams {
   const void *q, *kn, *vn, *kc, *vc;
   void *out;
+  void *sel;   // optional [B][H][D]: copy of the row max(n_valid, 1) - 1 of out
   const int32_t *seen, *n_valid;
   int32_t *status;
   const float *mask;
@@ -59,6 +60,10 @@ struct TileSeq {
 
 __device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
+
+// Chunk row whose output is also written to the selection (the last real row; row 0,
+// all zeros, when a sequence has no real row).
+__device__ __forceinline__ int selected_row(int nv) { return nv > 0 ? nv - 1 : 0; }
 
 __device__ __forceinline__ TileSeq make_tiles(const Live &g, int seen, int C, int kt, int i_min,
                                               int i_last, int window, int sink, bool full) {

@@ -659,6 +659,9 @@ __global__ void __launch_bounds__((256 * Cfg<D, EXT>::DSPLIT))
   const size_t orow = (static_cast<size_t>(b) * p.H + head) * p.C + i;
   if (p.splits == 1) {
     uint16_t *O = static_cast<uint16_t *>(p.out) + orow * D;
+    uint16_t *S = p.sel && i == selected_row(nv)
+                      ? static_cast<uint16_t *>(p.sel) + (static_cast<size_t>(b) * p.H + head) * D
+                      : nullptr;
     const float inv = real ? 1.f / l_tot : 0.f;
 #pragma unroll
     for (int db = 0; db < NDW; ++db) {
@@ -670,6 +673,7 @@ __global__ void __launch_bounds__((256 * Cfg<D, EXT>::DSPLIT))
         const u32x2 w = {pack_bf16x2(real ? o0 : 0.f, real ? o1 : 0.f),
                          pack_bf16x2(real ? o2 : 0.f, real ? o3 : 0.f)};
         *reinterpret_cast<u32x2 *>(O + d) = w;
+        if (S) *reinterpret_cast<u32x2 *>(S + d) = w;
       }
     }
   } else if (i < nv) {  // partials of real rows only: the merge writes pad rows as zeros

@@ -181,11 +181,17 @@ __global__ void __launch_bounds__(256) k_attn_valu(AttnParams p, int D) {
   const bool real = any_real && i < nv;
   if (p.splits == 1) {
     T *O = static_cast<T *>(p.out);
+    T *S = p.sel && i == selected_row(nv)
+               ? static_cast<T *>(p.sel) + (static_cast<size_t>(b) * p.H + head) * D
+               : nullptr;
     const float inv = real ? 1.f / l_run : 0.f;
 #pragma unroll
     for (int e = 0; e < DPT; ++e) {
       const int d = ql + 16 * e;
-      if (d < D) st(O, orow * D + d, real ? acc[e] * inv : 0.f);
+      if (d < D) {
+        st(O, orow * D + d, real ? acc[e] * inv : 0.f);
+        if (S) st(S, d, real ? acc[e] * inv : 0.f);
+      }
     }
   } else if (i < nv) {  // partials of real rows only: the merge writes pad rows as zeros
     const size_t rows = static_cast<size_t>(p.B) * p.H * p.C;
@@ -278,6 +284,11 @@ __global__ void __launch_bounds__(256) k_attn_combine(AttnParams p, int D) {
     }
 #pragma unroll
     for (int e = 0; e < VEC; ++e) st(O, row * D + d0 + e, res[e]);
+    if (p.sel && i == selected_row(nv)) {
+      T *S = static_cast<T *>(p.sel) + (row / p.C) * D + d0;  // row / C = b * H + h
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) st(S, e, res[e]);
+    }
   }
 }
 

@@ -14,7 +14,7 @@ int mfma_keys_per_tile(int D, bool explicit_tiling);
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr int kNumCU = 256;
 
 int to_status(hipError_t e) { return e == hipSuccess ? CP_OK : CP_ERR_HIP; }
@@ -95,6 +95,7 @@ hipError_t launch_attention(const cp_cache &c, const cp_attn_args &a, hipStream_
   p.kc = c.k;
   p.vc = c.v;
   p.out = a.out;
+  p.sel = a.select_out;
   p.seen = c.seen;
   p.n_valid = a.n_valid;
   p.status = c.status;
@@ -194,6 +195,24 @@ int cp_rope_chunk(const void *x, void *y, const float *cos, const float *sin, in
   if (!x || !y || !cos || !sin) return CP_ERR_ARG;
   return to_status(launch_rope(x, y, cos, sin, B, Hx, C, D, Bt, dtype,
                                static_cast<hipStream_t>(stream)));
+}
+
+int cp_rope_qk_chunk(const void *q, void *q_out, const void *k, void *k_out, const float *cos,
+                     const float *sin, int B, int H, int nKV, int C, int D, int Bt, int dtype,
+                     cp_stream_t stream) {
+  if (dtype != CP_F32 && dtype != CP_BF16) return CP_ERR_DTYPE;
+  if (B < 0 || H < 0 || nKV < 0 || C < 0 || D < 1) return CP_ERR_ARG;
+  if (D % 2 != 0) return CP_ERR_SHAPE;
+  if (Bt != 1 && Bt != B) return CP_ERR_ARG;
+  const bool has_q = static_cast<size_t>(B) * H * C > 0;
+  const bool has_k = static_cast<size_t>(B) * nKV * C > 0;
+  if (!has_q && !has_k) return CP_OK;  // empty: pointers may be NULL
+  if (!cos || !sin || (has_q && (!q || !q_out)) || (has_k && (!k || !k_out))) return CP_ERR_ARG;
+  if (!has_q)
+    return to_status(launch_rope(k, k_out, cos, sin, B, nKV, C, D, Bt, dtype,
+                                 static_cast<hipStream_t>(stream)));
+  return to_status(launch_rope2(q, q_out, H, k, k_out, has_k ? nKV : 0, cos, sin, B, C, D, Bt,
+                                dtype, static_cast<hipStream_t>(stream)));
 }
 
 int cp_kv_append(const cp_cache *cache, const void *k_new, const void *v_new, int C,

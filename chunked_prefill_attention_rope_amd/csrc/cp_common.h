@@ -85,6 +85,10 @@ __device__ __forceinline__ int read_nvalid(const int32_t *n_valid, int b, int C,
 
 hipError_t launch_rope(const void *x, void *y, const float *cos, const float *sin, int B, int Hx,
                        int C, int D, int Bt, int dtype, hipStream_t s);
+// Two tensors (Q and K of a chunk) rotated by one launch from the same tables.
+hipError_t launch_rope2(const void *x0, void *y0, int H0, const void *x1, void *y1, int H1,
+                        const float *cos, const float *sin, int B, int C, int D, int Bt, int dtype,
+                        hipStream_t s);
 hipError_t launch_kv_append(const cp_cache &c, const void *k_new, const void *v_new, int C,
                             const int32_t *n_rows, hipStream_t s);
 hipError_t launch_snapshot(const cp_cache &c, int C, const int32_t *n_valid, void *buf,

@@ -11,9 +11,12 @@
 // All kernels are HBM-bound row copies: a thread moves one 16-byte chunk
 // (4-byte chunk when a row is not a multiple of 16 bytes), consecutive
 // threads cover consecutive bytes of a row.  The ring is a modular ring, so
-// an append writes O(n) rows rather than compacting the window.  Bookkeeping
-// (seen) is updated by a one-block kernel launched after the copy kernel on
-// the same stream, so every copy thread reads the pre-append value.
+// an append writes O(n) rows rather than compacting the window.  Every copy
+// thread must read the pre-append seen, so the bookkeeping update comes after
+// all of them: for a small append (up to kOneBlockChunks 16-byte chunks per
+// tensor) one 1024-thread workgroup copies and then, past a workgroup barrier,
+// updates seen itself -- one launch instead of two; a larger append runs the
+// copy kernel over the whole GPU followed by a one-block seen kernel.
 #include "cp_common.h"
 
 namespace cp {
@@ -73,6 +76,59 @@ __global__ void __launch_bounds__(256) k_append(cp_cache c, const void *__restri
     const size_t w = row_bytes / sizeof(W);
     static_cast<W *>(c.k)[dst * w + ch] = static_cast<const W *>(kn)[src * w + ch];
     static_cast<W *>(c.v)[dst * w + ch] = static_cast<const W *>(vn)[src * w + ch];
+  }
+}
+
+// Single-workgroup append: the copy, then (after every thread has read seen) the
+// seen update.  Each thread keeps kUnroll rows' chunks in flight at once.
+constexpr int kOneBlock = 1024, kUnroll = 8;
+constexpr size_t kOneBlockChunks = static_cast<size_t>(kOneBlock) * kUnroll;
+
+template <typename W>
+__global__ void __launch_bounds__(kOneBlock) k_append_one(cp_cache c, const void *__restrict__ kn,
+                                                         const void *__restrict__ vn, int C,
+                                                         const int32_t *__restrict__ n_rows,
+                                                         int cpr, size_t row_bytes) {
+  const size_t total = static_cast<size_t>(c.B) * c.nKV * C * cpr;
+  const size_t w = row_bytes / sizeof(W);
+  for (size_t t0 = threadIdx.x; t0 < total; t0 += static_cast<size_t>(kOneBlock) * kUnroll) {
+    W kv[kUnroll], vv[kUnroll];
+    size_t dst[kUnroll];
+    bool go[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const size_t t = t0 + static_cast<size_t>(u) * kOneBlock;
+      go[u] = false;
+      dst[u] = 0;
+      if (t >= total) continue;
+      const int ch = static_cast<int>(t % cpr);
+      size_t rest = t / cpr;
+      const int r = static_cast<int>(rest % C);
+      rest /= C;
+      const int g = static_cast<int>(rest % c.nKV);
+      const int b = static_cast<int>(rest / c.nKV);
+      const AppendPlan a = append_plan(c, n_rows, b, C, g == 0 && r == 0 && ch == 0);
+      if (a.skip || r >= a.n) continue;
+      const int p = a.s0 + r;
+      if (c.ring && p >= c.sink && p < a.s0 + a.n - (c.cap - c.sink)) continue;
+      const int sl = slot_of(p, c.cap, c.ring, c.sink);
+      const size_t src = ((static_cast<size_t>(b) * c.nKV + g) * C + r) * w + ch;
+      dst[u] = ((static_cast<size_t>(b) * c.nKV + g) * c.cap + sl) * w + ch;
+      kv[u] = static_cast<const W *>(kn)[src];
+      vv[u] = static_cast<const W *>(vn)[src];
+      go[u] = true;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (go[u]) {
+        static_cast<W *>(c.k)[dst[u]] = kv[u];
+        static_cast<W *>(c.v)[dst[u]] = vv[u];
+      }
+  }
+  __syncthreads();  // every read of seen above happens before it changes
+  for (int b = threadIdx.x; b < c.B; b += kOneBlock) {
+    const AppendPlan a = append_plan(c, n_rows, b, C, false);
+    if (!a.skip) c.seen[b] = a.s0 + a.n;
   }
 }
 
@@ -168,6 +224,64 @@ __global__ void __launch_bounds__(256) k_restore(cp_cache c, int C, const unsign
   }
 }
 
+// Single-workgroup rollback: restore the saved rows, then (after every thread has
+// compared seen) set seen.
+template <typename W>
+__global__ void __launch_bounds__(kOneBlock) k_restore_one(cp_cache c, int C,
+                                                          const unsigned char *__restrict__ buf,
+                                                          size_t hdr, int cpr, size_t row_bytes) {
+  const int32_t *h = reinterpret_cast<const int32_t *>(buf);
+  const size_t half = static_cast<size_t>(c.B) * c.nKV * C * row_bytes;
+  const W *sk = reinterpret_cast<const W *>(buf + hdr);
+  const W *sv = reinterpret_cast<const W *>(buf + hdr + half);
+  const size_t w = row_bytes / sizeof(W);
+  const size_t total = static_cast<size_t>(c.B) * c.nKV * C * cpr;
+  for (size_t t0 = threadIdx.x; t0 < total; t0 += static_cast<size_t>(kOneBlock) * kUnroll) {
+    W kv[kUnroll], vv[kUnroll];
+    size_t dst[kUnroll];
+    bool go[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const size_t t = t0 + static_cast<size_t>(u) * kOneBlock;
+      go[u] = false;
+      dst[u] = 0;
+      if (t >= total) continue;
+      const int ch = static_cast<int>(t % cpr);
+      size_t rest = t / cpr;
+      const int r = static_cast<int>(rest % C);
+      rest /= C;
+      const int g = static_cast<int>(rest % c.nKV);
+      const int b = static_cast<int>(rest / c.nKV);
+      const int s0 = h[b], nv = h[c.B + b];
+      if (s0 < 0 || c.seen[b] != s0 + C) continue;
+      int lo, hi;
+      overevicted(c, s0, nv, C, &lo, &hi);
+      if (r >= hi - lo) continue;
+      const int sl = slot_of(lo + r, c.cap, c.ring, c.sink);
+      dst[u] = ((static_cast<size_t>(b) * c.nKV + g) * c.cap + sl) * w + ch;
+      const size_t src = ((static_cast<size_t>(b) * c.nKV + g) * C + r) * w + ch;
+      kv[u] = sk[src];
+      vv[u] = sv[src];
+      go[u] = true;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (go[u]) {
+        static_cast<W *>(c.k)[dst[u]] = kv[u];
+        static_cast<W *>(c.v)[dst[u]] = vv[u];
+      }
+  }
+  __syncthreads();  // every comparison with seen above happens before it changes
+  for (int b = threadIdx.x; b < c.B; b += kOneBlock) {
+    const int s0 = h[b], nv = h[c.B + b];
+    if (s0 < 0 || c.seen[b] != s0 + C) {
+      flag(c.status, CP_DEV_ROLLBACK);
+      continue;
+    }
+    c.seen[b] = s0 + nv;
+  }
+}
+
 __global__ void k_rollback_seen(cp_cache c, int C, const unsigned char *__restrict__ buf) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= c.B) return;
@@ -197,6 +311,19 @@ hipError_t launch_kv_append(const cp_cache &c, const void *k_new, const void *v_
                             const int32_t *n_rows, hipStream_t s) {
   if (c.B == 0) return hipSuccess;
   const size_t rb = row_bytes_of(c);
+  {
+    const bool c16 = rb % 16 == 0;
+    const int cpr = static_cast<int>(c16 ? rb / 16 : rb / 4);
+    if (static_cast<size_t>(c.B) * c.nKV * C * cpr <= kOneBlockChunks) {
+      if (c16)
+        hipLaunchKernelGGL(k_append_one<Chunk16>, dim3(1), dim3(kOneBlock), 0, s, c, k_new,
+                           v_new, C, n_rows, cpr, rb);
+      else
+        hipLaunchKernelGGL(k_append_one<uint32_t>, dim3(1), dim3(kOneBlock), 0, s, c, k_new,
+                           v_new, C, n_rows, cpr, rb);
+      return hipGetLastError();
+    }
+  }
   if (C > 0) {
     if (rb % 16 == 0) {
       const int cpr = static_cast<int>(rb / 16);
@@ -240,6 +367,19 @@ hipError_t launch_rollback(const cp_cache &c, int C, const void *buf, hipStream_
   const size_t rb = row_bytes_of(c);
   const size_t hdr = snapshot_header_bytes(c.B);
   const unsigned char *b = static_cast<const unsigned char *>(buf);
+  {
+    const bool c16 = rb % 16 == 0;
+    const int cpr = static_cast<int>(c16 ? rb / 16 : rb / 4);
+    if (static_cast<size_t>(c.B) * c.nKV * C * cpr <= kOneBlockChunks) {
+      if (c16)
+        hipLaunchKernelGGL(k_restore_one<Chunk16>, dim3(1), dim3(kOneBlock), 0, s, c, C, b, hdr,
+                           cpr, rb);
+      else
+        hipLaunchKernelGGL(k_restore_one<uint32_t>, dim3(1), dim3(kOneBlock), 0, s, c, C, b, hdr,
+                           cpr, rb);
+      return hipGetLastError();
+    }
+  }
   if (C > 0) {
     if (rb % 16 == 0) {
       const int cpr = static_cast<int>(rb / 16);

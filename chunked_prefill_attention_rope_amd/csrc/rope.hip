@@ -46,27 +46,42 @@ __device__ __forceinline__ float rot_hi(float lo, float hi, float c, float s) {
   return static_cast<float>(a + b);
 }
 
+// One rotated tensor of a launch: x, y [B, Hx, C, D].
+template <typename T>
+struct RopeOp {
+  const T *x;
+  T *y;
+  int Hx;
+};
+
 // One thread: VEC consecutive pairs (j .. j+VEC-1, j+h2 .. j+h2+VEC-1) of a row,
 // moved with vector loads/stores (VEC > 1 needs 16-byte aligned rows and tables).
-// x and y may alias: every element is read and written by the same thread.
+// x and y may alias: every element is read and written by the same thread.  The grid
+// covers the rows of a, then those of b (b.Hx = 0 for a single tensor), so Q and K of
+// a chunk are rotated by one launch.
 template <typename T, int VEC>
-__global__ void __launch_bounds__(128) k_rope(const T *x, T *y, const float *__restrict__ cosb,
-                                              const float *__restrict__ sinb, int B, int Hx, int C,
-                                              int D, int Bt) {
+__global__ void __launch_bounds__(128) k_rope(RopeOp<T> a, RopeOp<T> bop,
+                                              const float *__restrict__ cosb,
+                                              const float *__restrict__ sinb, int B, int C, int D,
+                                              int Bt) {
   const int h2 = D / 2;
   const int per_row = h2 / VEC;
-  const size_t rows = static_cast<size_t>(B) * Hx * C;
+  const size_t rows_a = static_cast<size_t>(B) * a.Hx * C;
+  const size_t rows = rows_a + static_cast<size_t>(B) * bop.Hx * C;
   const size_t total = rows * per_row;
   for (size_t t = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; t < total;
        t += static_cast<size_t>(gridDim.x) * blockDim.x) {
-    const size_t row = t / per_row;
+    size_t row = t / per_row;
     const int j0 = static_cast<int>(t % per_row) * VEC;
+    const bool second = row >= rows_a;
+    const RopeOp<T> &op = second ? bop : a;
+    if (second) row -= rows_a;
     const int i = static_cast<int>(row % C);
-    const int b = static_cast<int>(row / (static_cast<size_t>(Hx) * C));
+    const int b = static_cast<int>(row / (static_cast<size_t>(op.Hx) * C));
     const size_t xo = row * D;
     const size_t to = (static_cast<size_t>(Bt == 1 ? 0 : b) * C + i) * D;
-    const Pack<T, VEC> lo = *reinterpret_cast<const Pack<T, VEC> *>(x + xo + j0);
-    const Pack<T, VEC> hi = *reinterpret_cast<const Pack<T, VEC> *>(x + xo + j0 + h2);
+    const Pack<T, VEC> lo = *reinterpret_cast<const Pack<T, VEC> *>(op.x + xo + j0);
+    const Pack<T, VEC> hi = *reinterpret_cast<const Pack<T, VEC> *>(op.x + xo + j0 + h2);
     const Pack<float, VEC> cl = *reinterpret_cast<const Pack<float, VEC> *>(cosb + to + j0);
     const Pack<float, VEC> sl = *reinterpret_cast<const Pack<float, VEC> *>(sinb + to + j0);
     const Pack<float, VEC> ch = *reinterpret_cast<const Pack<float, VEC> *>(cosb + to + j0 + h2);
@@ -74,22 +89,23 @@ __global__ void __launch_bounds__(128) k_rope(const T *x, T *y, const float *__r
     Pack<T, VEC> ylo, yhi;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      const float a = Elem<T>::get(lo.v[e]), c = Elem<T>::get(hi.v[e]);
-      ylo.v[e] = Elem<T>::put(rot_lo(a, c, cl.v[e], sl.v[e]));
-      yhi.v[e] = Elem<T>::put(rot_hi(a, c, ch.v[e], sh.v[e]));
+      const float xa = Elem<T>::get(lo.v[e]), xc = Elem<T>::get(hi.v[e]);
+      ylo.v[e] = Elem<T>::put(rot_lo(xa, xc, cl.v[e], sl.v[e]));
+      yhi.v[e] = Elem<T>::put(rot_hi(xa, xc, ch.v[e], sh.v[e]));
     }
-    *reinterpret_cast<Pack<T, VEC> *>(y + xo + j0) = ylo;
-    *reinterpret_cast<Pack<T, VEC> *>(y + xo + j0 + h2) = yhi;
+    *reinterpret_cast<Pack<T, VEC> *>(op.y + xo + j0) = ylo;
+    *reinterpret_cast<Pack<T, VEC> *>(op.y + xo + j0 + h2) = yhi;
   }
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 template <typename T>
-hipError_t launch_t(const void *x, void *y, const float *cos, const float *sin, int B, int Hx,
-                    int C, int D, int Bt, hipStream_t s) {
+hipError_t launch_t(const void *x0, void *y0, int H0, const void *x1, void *y1, int H1,
+                    const float *cos, const float *sin, int B, int C, int D, int Bt,
+                    hipStream_t s) {
   const int h2 = D / 2;
-  const size_t rows = static_cast<size_t>(B) * Hx * C;
+  const size_t rows = static_cast<size_t>(B) * (H0 + H1) * C;
   if (rows == 0) return hipSuccess;
   auto grid_for = [&](int vec) {
     size_t total = rows * (h2 / vec);
@@ -97,16 +113,17 @@ hipError_t launch_t(const void *x, void *y, const float *cos, const float *sin, 
     if (blocks > 65535 * 4) blocks = 65535 * 4;
     return static_cast<unsigned>(blocks);
   };
-  const T *xi = static_cast<const T *>(x);
-  T *yo = static_cast<T *>(y);
+  const RopeOp<T> a{static_cast<const T *>(x0), static_cast<T *>(y0), H0};
+  const RopeOp<T> b{static_cast<const T *>(x1), static_cast<T *>(y1), H1};
   constexpr int V16 = 16 / sizeof(T);  // elements per 16 bytes
-  const bool al = aligned16(x) && aligned16(y) && aligned16(cos) && aligned16(sin);
+  bool al = aligned16(x0) && aligned16(y0) && aligned16(cos) && aligned16(sin);
+  if (H1 > 0) al = al && aligned16(x1) && aligned16(y1);
   if (al && h2 % V16 == 0) {
-    hipLaunchKernelGGL((k_rope<T, V16>), dim3(grid_for(V16)), dim3(128), 0, s, xi, yo, cos, sin,
-                       B, Hx, C, D, Bt);
+    hipLaunchKernelGGL((k_rope<T, V16>), dim3(grid_for(V16)), dim3(128), 0, s, a, b, cos, sin,
+                       B, C, D, Bt);
   } else {
-    hipLaunchKernelGGL((k_rope<T, 1>), dim3(grid_for(1)), dim3(128), 0, s, xi, yo, cos, sin, B, Hx,
-                       C, D, Bt);
+    hipLaunchKernelGGL((k_rope<T, 1>), dim3(grid_for(1)), dim3(128), 0, s, a, b, cos, sin, B, C,
+                       D, Bt);
   }
   return hipGetLastError();
 }
@@ -115,8 +132,15 @@ hipError_t launch_t(const void *x, void *y, const float *cos, const float *sin, 
 
 hipError_t launch_rope(const void *x, void *y, const float *cos, const float *sin, int B, int Hx,
                        int C, int D, int Bt, int dtype, hipStream_t s) {
-  if (dtype == CP_BF16) return launch_t<uint16_t>(x, y, cos, sin, B, Hx, C, D, Bt, s);
-  return launch_t<float>(x, y, cos, sin, B, Hx, C, D, Bt, s);
+  return launch_rope2(x, y, Hx, nullptr, nullptr, 0, cos, sin, B, C, D, Bt, dtype, s);
+}
+
+hipError_t launch_rope2(const void *x0, void *y0, int H0, const void *x1, void *y1, int H1,
+                        const float *cos, const float *sin, int B, int C, int D, int Bt, int dtype,
+                        hipStream_t s) {
+  if (dtype == CP_BF16)
+    return launch_t<uint16_t>(x0, y0, H0, x1, y1, H1, cos, sin, B, C, D, Bt, s);
+  return launch_t<float>(x0, y0, H0, x1, y1, H1, cos, sin, B, C, D, Bt, s);
 }
 
 }  // namespace cp

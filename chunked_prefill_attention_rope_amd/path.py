@@ -3,7 +3,12 @@
 Order of the calls (the cache is read by attention before the chunk's rows
 are appended, so a ring never loses keys the chunk's first rows still need):
 
-    rope(Q), rope(K) -> [snapshot] -> attention -> append -> [rollback] -> select
+    rope(Q, K) -> [snapshot] -> attention (+ selected row) -> append -> [rollback]
+
+Q and K are rotated by one launch, the attention writes the last real row into
+the selection as it writes the output, and a small append updates seen in the
+same launch as its copy (the step's launch count: 3 kernels, 4 with a key split,
+plus the snapshot and rollback of a static padded append).
 
 ``static_append=True`` models a caller whose append always writes all C rows
 (a fixed-shape graph): the ring is protected by the padded-append snapshot and
@@ -49,14 +54,13 @@ def chunk_step(cache: cp.KVCache, q, k, v, cos, sin, n_valid, bufs: StepBuffers,
                mask: Optional[torch.Tensor] = None, window: int = 0,
                static_append: bool = False, flags: int = 0):
     """Run the whole hot path of one layer for one chunk; returns (out, selected row)."""
-    cp.rope_chunk(q, cos, sin, out=bufs.q_rot)
-    cp.rope_chunk(k, cos, sin, out=bufs.k_rot)
+    cp.rope_qk_chunk(q, k, cos, sin, q_out=bufs.q_rot, k_out=bufs.k_rot)
     if static_append:
         cp.kv_snapshot_padded_append(cache, q.shape[2], n_valid, bufs.snap)
     cp.attn_chunk_with_past(cache, bufs.q_rot, bufs.k_rot, v, n_valid=n_valid, mask=mask,
-                            window=window, out=bufs.out, workspace=bufs.workspace, flags=flags)
+                            window=window, out=bufs.out, workspace=bufs.workspace, flags=flags,
+                            select_out=bufs.sel)
     cp.kv_append(cache, bufs.k_rot, v, None if static_append else n_valid)
     if static_append:
         cp.kv_rollback_padded_append(cache, bufs.snap)
-    cp.select_row(bufs.out, n_valid, -1, out=bufs.sel)
     return bufs.out, bufs.sel

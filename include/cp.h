@@ -8,6 +8,9 @@
  *   -> cp_attn_chunk_with_past -> cp_kv_append -> [cp_kv_rollback_padded_append]
  *   -> cp_select_row
  *
+ * or, with fewer launches, cp_rope_qk_chunk -> [snapshot] -> cp_attn_chunk_with_past
+ * with select_out set -> cp_kv_append -> [rollback].
+ *
  * Sources:
  *   [SKaiNET] SKaiNET-transformers PR #417, "functiongemma: chunk prefill-with-
  *             past graph gemma_prefill_with_past", section "Change (additive)":
@@ -152,6 +155,12 @@ typedef struct cp_snapshot {
  *   window     sliding window in positions (0 = none); in-kernel mask only
  *   scale      softmax scale (> 0) applied to q.k before the mask is added
  *   flags      CP_ATTN_* below
+ *   select_out optional [B, H, D] storage dtype: also receives row
+ *              max(n_valid[b], 1) - 1 of out for every (b, h) -- the last real
+ *              row ([SKaiNET] "Validation": row 51 of a 52-token chunk), zeros
+ *              for a sequence without real rows -- bit-identical to
+ *              cp_select_row(out, n_valid, -1) for n_valid in [0, C] (n_valid
+ *              NULL selects row C - 1).  Not written when C = 0.
  *
  * The cache is read as it stands BEFORE the chunk is appended.
  */
@@ -173,6 +182,7 @@ typedef struct cp_attn_args {
   float scale;
   uint32_t flags;
   int32_t reserved; /* must be 0 */
+  void *select_out;
 } cp_attn_args;
 
 #define CP_ATTN_NO_SPLIT 1u      /* one pass per query tile, no key split */
@@ -213,6 +223,16 @@ size_t cp_struct_size(int which);
  */
 int cp_rope_chunk(const void *x, void *y, const float *cos, const float *sin, int B, int Hx,
                   int C, int D, int Bt, int dtype, cp_stream_t stream);
+
+/*
+ * The same rotation of a chunk's queries and keys in one launch: q, q_out
+ * [B, H, C, D] and k, k_out [B, nKV, C, D] with the shared tables; results
+ * bit-identical to two cp_rope_chunk calls.  q_out may equal q, k_out k.
+ * Errors: as cp_rope_chunk (CP_ERR_ARG also for H or nKV < 0).
+ */
+int cp_rope_qk_chunk(const void *q, void *q_out, const void *k, void *k_out, const float *cos,
+                     const float *sin, int B, int H, int nKV, int C, int D, int Bt, int dtype,
+                     cp_stream_t stream);
 
 /* ---- KV cache ---- */
 

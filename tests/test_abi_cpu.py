@@ -81,6 +81,18 @@ def test_rope_validation(cp):
     assert f(FAKE, FAKE, FAKE, FAKE, 3, 1, 1, 8, 2, cp.BF16, None) == cp.ERR_ARG
 
 
+def test_rope_qk_validation(cp):
+    f = cp.raw().cp_rope_qk_chunk
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE]
+    assert f(None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 4, 8, 1, cp.BF16, None) == cp.ERR_ARG
+    assert f(*args, 1, 2, 1, 4, 7, 1, cp.BF16, None) == cp.ERR_SHAPE
+    assert f(*args, 1, 2, 1, 4, 8, 1, 9, None) == cp.ERR_DTYPE
+    assert f(*args, 2, 2, 1, 4, 8, 3, cp.BF16, None) == cp.ERR_ARG
+    assert f(*args, 1, -1, 1, 4, 8, 1, cp.BF16, None) == cp.ERR_ARG
+    # empty work is a no-op, pointers may be NULL
+    assert f(None, None, None, None, None, None, 1, 2, 1, 0, 8, 1, cp.BF16, None) == cp.OK
+
+
 def test_append_validation(cp):
     f = cp.raw().cp_kv_append
     assert f(None, FAKE, FAKE, 4, None, None) == cp.ERR_ARG

@@ -131,6 +131,37 @@ def test_explicit_mask_equals_inkernel_bitwise(cp, kw, kernel):
     assert torch.equal(a.float(), b.float())
 
 
+@pytest.mark.parametrize("kw", SMALL, ids=lambda c: c["name"])
+@pytest.mark.parametrize("split", ["split", "nosplit"])
+def test_select_out_equals_select_row(cp, kw, split):
+    """The selection written by the attention (its epilogue, or the split merge) is
+    bit-identical to cp_select_row(out, n_valid, -1), including a sequence without
+    real rows (zeros)."""
+    kw = dict(kw)
+    kw.pop("name")
+    if kw["B"] > 1:
+        kw["n_valid"] = [0] + list(kw["n_valid"][1:])
+    cfg = I.small(**kw)
+    t, cache, _ = _setup(cp, cfg)
+    q, k, v = dev(t["q"]), dev(t["k"]), dev(t["v"])
+    nv = dev(t["n_valid"])
+    flags = cp.ATTN_NO_SPLIT if split == "nosplit" else cp.ATTN_SPLITS(3)
+    nb = cp.attn_workspace_bytes(cache, q, k, v, window=cfg.window, flags=flags)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    sel = torch.full((cfg.B, cfg.H, cfg.D), 7.0, dtype=q.dtype, device="cuda")
+    out = cp.attn_chunk_with_past(cache, q, k, v, n_valid=nv, window=cfg.window,
+                                  scale=cfg.scale, workspace=ws, flags=flags, select_out=sel)
+    ref = cp.select_row(out, nv, -1)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(sel), bits(ref))
+    # n_valid NULL selects row C - 1
+    sel2 = torch.zeros_like(sel)
+    out2 = cp.attn_chunk_with_past(cache, q, k, v, window=cfg.window, scale=cfg.scale,
+                                   workspace=ws, flags=flags, select_out=sel2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(sel2), bits(out2[:, :, cfg.C - 1]))
+
+
 @pytest.mark.parametrize("kw", SMALL[:5], ids=lambda c: c["name"])
 def test_run_twice_is_deterministic(cp, kw):
     kw = dict(kw)

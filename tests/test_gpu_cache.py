@@ -46,6 +46,28 @@ def test_rope_in_place_and_shared_table(cp):
     np.testing.assert_array_equal(bits(x), ref.view(np.uint8))
 
 
+@pytest.mark.parametrize("dtype", [I.F32, I.BF16])
+@pytest.mark.parametrize("D", [64, 256, 12])
+def test_rope_qk_one_launch_matches_oracle(cp, dtype, D):
+    """cp_rope_qk_chunk rotates Q and K of a chunk in one launch, bit-exact like two
+    cp_rope_chunk calls (D = 12 takes the unvectorised path)."""
+    cfg = I.small(dtype=dtype, B=2, H=6, nKV=2, D=D, C=23, seen=[5, 1000])
+    t = I.make_layer(cfg)
+    qo, ko = cp.rope_qk_chunk(dev(t["q"]), dev(t["k"]), dev(t["cos"]), dev(t["sin"]))
+    for got, x in ((qo, t["q"]), (ko, t["k"])):
+        ref = O.rope(_np(x), _np(t["cos"]), _np(t["sin"]))
+        np.testing.assert_array_equal(bits(got), ref.view(np.uint8))
+    # in place, shared table
+    cfg = I.small(dtype=dtype, B=2, H=4, nKV=1, D=D, C=9, seen=[70, 70])
+    t = I.make_layer(cfg)
+    q, k = dev(t["q"]), dev(t["k"])
+    cp.rope_qk_chunk(q, k, dev(t["cos"]), dev(t["sin"]), q_out=q, k_out=k)
+    np.testing.assert_array_equal(bits(q), O.rope(_np(t["q"]), _np(t["cos"]),
+                                                  _np(t["sin"])).view(np.uint8))
+    np.testing.assert_array_equal(bits(k), O.rope(_np(t["k"]), _np(t["cos"]),
+                                                  _np(t["sin"])).view(np.uint8))
+
+
 def test_rope_empty(cp):
     x = torch.empty((0, 4, 8, 64), dtype=torch.bfloat16, device="cuda")
     cos = torch.zeros((1, 8, 64), device="cuda")
@@ -86,6 +108,29 @@ def test_append_bit_exact(cp, case, dtype, D):
         np.testing.assert_array_equal(kg[b][:, sl], ko.view(np.uint8).reshape(kg.shape)[b][:, sl])
         np.testing.assert_array_equal(vg[b][:, sl], vo.view(np.uint8).reshape(vg.shape)[b][:, sl])
     assert kg.shape[-1] == D * es
+
+
+@pytest.mark.parametrize("ring", [0, 1])
+def test_append_large_takes_the_multi_block_path(cp, ring):
+    """Appends of more than 8192 16-byte chunks per tensor copy over the whole GPU and
+    update seen in a second launch; small ones do both in one workgroup."""
+    seen = [300, 0, 1200, 77] if ring else [300, 0, 500, 77]
+    cfg = I.small(dtype=I.BF16, B=4, H=8, nKV=8, D=128, C=128, cap=1024 if ring else 700,
+                  ring=ring, sink=4 if ring else 0, seen=seen, n_valid=[128, 100, 1, 64])
+    t = I.make_layer(cfg)
+    kc, vc, sd = dev(t["kc"]), dev(t["vc"]), dev(t["seen"])
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cache = cp.KVCache(kc, vc, sd, ring=cfg.ring, sink=cfg.sink, status=status)
+    cp.kv_append(cache, dev(t["k"]), dev(t["v"]), dev(t["n_valid"]))
+    ko, vo, so, live = O.kv_append(_np(t["kc"]), _np(t["vc"]), _np(t["seen"]), _np(t["k"]),
+                                   _np(t["v"]), _np(t["n_valid"]), cfg.ring, cfg.sink)
+    assert sd.cpu().tolist() == so.tolist()
+    assert int(status.item()) == 0
+    kg, vg = bits(kc), bits(vc)
+    for b in range(cfg.B):
+        sl = np.nonzero(live[b])[0]
+        np.testing.assert_array_equal(kg[b][:, sl], ko.view(np.uint8).reshape(kg.shape)[b][:, sl])
+        np.testing.assert_array_equal(vg[b][:, sl], vo.view(np.uint8).reshape(vg.shape)[b][:, sl])
 
 
 def test_append_all_rows_and_overflow_flag(cp):
@@ -129,6 +174,9 @@ ROLLBACK_CASES = [  # ([cactus] review: no eviction, overshoot, eviction, sink)
     dict(name="c3_primary", cap=512, sink=0, seen=[1023], C=128, nv=[127]),
     dict(name="c3_cactus", cap=512, sink=0, seen=[896], C=128, nv=[127]),
     dict(name="batch", cap=64, sink=2, seen=[10, 57, 300, 64], C=16, nv=[16, 5, 1, 9]),
+    # 4 x 2 x 512 rows of 128 bytes (bf16) = 32768 chunks: the multi-block rollback
+    dict(name="large", cap=1024, sink=0, seen=[5000, 1100, 700, 3000], C=512,
+         nv=[300, 1, 512, 17]),
 ]
 
 

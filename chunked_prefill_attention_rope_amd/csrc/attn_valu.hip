@@ -214,19 +214,22 @@ __global__ void __launch_bounds__(256) k_attn_valu(AttnParams p, int D) {
 // partials are fetched SB splits at a time (independent loads in flight together)
 // and folded into a running maximum, so a row costs ceil(splits / SB) memory round
 // trips instead of one per split.
-template <typename T, int VEC>
+// I: index type (32-bit when the element count allows; see the RoPE kernel).
+template <typename T, int VEC, typename I>
 __global__ void __launch_bounds__(256) k_attn_combine(AttnParams p, int D) {
   constexpr int SB = 8;
   const size_t rows = static_cast<size_t>(p.B) * p.H * p.C;
-  const int per_row = D / VEC;
-  const size_t total = rows * per_row;
+  const I per_row = D / VEC;
+  const I total = static_cast<I>(rows) * per_row;
   T *O = static_cast<T *>(p.out);
-  for (size_t t = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; t < total;
-       t += static_cast<size_t>(gridDim.x) * blockDim.x) {
-    const size_t row = t / per_row;
-    const int d0 = static_cast<int>(t % per_row) * VEC;
-    const int i = static_cast<int>(row % p.C);
-    const int b = static_cast<int>(row / (static_cast<size_t>(p.H) * p.C));
+  for (I t = blockIdx.x * static_cast<I>(blockDim.x) + threadIdx.x; t < total;
+       t += static_cast<I>(gridDim.x) * blockDim.x) {
+    const I row_i = t / per_row;
+    const size_t row = row_i;
+    const int d0 = static_cast<int>(t - row_i * per_row) * VEC;
+    const I bh = row_i / static_cast<I>(p.C);
+    const int i = static_cast<int>(row_i - bh * p.C);
+    const int b = static_cast<int>(bh / static_cast<I>(p.H));
     const int nv = read_nvalid(p.n_valid, b, p.C, nullptr);
     float res[VEC];
 #pragma unroll
@@ -285,7 +288,7 @@ __global__ void __launch_bounds__(256) k_attn_combine(AttnParams p, int D) {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) st(O, row * D + d0 + e, res[e]);
     if (p.sel && i == selected_row(nv)) {
-      T *S = static_cast<T *>(p.sel) + (row / p.C) * D + d0;  // row / C = b * H + h
+      T *S = static_cast<T *>(p.sel) + static_cast<size_t>(bh) * D + d0;  // bh = b * H + h
 #pragma unroll
       for (int e = 0; e < VEC; ++e) st(S, e, res[e]);
     }
@@ -326,17 +329,26 @@ hipError_t launch_attn_combine(const AttnParams &p, int D, int dtype, hipStream_
   const bool v4 = D % 4 == 0;
   size_t blocks = (total / (v4 ? 4 : 1) + 255) / 256;
   if (blocks > 16384) blocks = 16384;
+  const bool i32 = total < (size_t(1) << 31);
+#define CP_COMBINE(T, V)                                                                         \
+  do {                                                                                           \
+    if (i32)                                                                                     \
+      hipLaunchKernelGGL((k_attn_combine<T, V, uint32_t>), dim3(blocks), dim3(256), 0, s, p, D); \
+    else                                                                                         \
+      hipLaunchKernelGGL((k_attn_combine<T, V, size_t>), dim3(blocks), dim3(256), 0, s, p, D);   \
+  } while (0)
   if (dtype == CP_BF16) {
     if (v4)
-      hipLaunchKernelGGL((k_attn_combine<uint16_t, 4>), dim3(blocks), dim3(256), 0, s, p, D);
+      CP_COMBINE(uint16_t, 4);
     else
-      hipLaunchKernelGGL((k_attn_combine<uint16_t, 1>), dim3(blocks), dim3(256), 0, s, p, D);
+      CP_COMBINE(uint16_t, 1);
   } else {
     if (v4)
-      hipLaunchKernelGGL((k_attn_combine<float, 4>), dim3(blocks), dim3(256), 0, s, p, D);
+      CP_COMBINE(float, 4);
     else
-      hipLaunchKernelGGL((k_attn_combine<float, 1>), dim3(blocks), dim3(256), 0, s, p, D);
+      CP_COMBINE(float, 1);
   }
+#undef CP_COMBINE
   return hipGetLastError();
 }
 

@@ -13,7 +13,7 @@
 // threads cover consecutive bytes of a row.  The ring is a modular ring, so
 // an append writes O(n) rows rather than compacting the window.  Every copy
 // thread must read the pre-append seen, so the bookkeeping update comes after
-// all of them: for a small append (up to kOneBlockChunks 16-byte chunks per
+// all of them: for a tiny append (up to kOneBlockChunks 16-byte chunks per
 // tensor) one 1024-thread workgroup copies and then, past a workgroup barrier,
 // updates seen itself -- one launch instead of two; a larger append runs the
 // copy kernel over the whole GPU followed by a one-block seen kernel.
@@ -52,20 +52,22 @@ __device__ __forceinline__ AppendPlan append_plan(const cp_cache &c, const int32
 // Copy kernel of an append.  Row r of sequence b goes to position s0 + r; in
 // a ring only rows that are still live after the whole append are written
 // (an append longer than the window would otherwise write one slot twice).
-template <typename W>
+// I: index type, 32-bit when the chunk count allows (integer division is a software
+// sequence, a 64-bit one several times longer).
+template <typename W, typename I>
 __global__ void __launch_bounds__(256) k_append(cp_cache c, const void *__restrict__ kn,
                                                 const void *__restrict__ vn, int C,
                                                 const int32_t *__restrict__ n_rows, int cpr,
                                                 size_t row_bytes) {
-  const size_t total = static_cast<size_t>(c.B) * c.nKV * C * cpr;
-  for (size_t t = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; t < total;
-       t += static_cast<size_t>(gridDim.x) * blockDim.x) {
-    const int ch = static_cast<int>(t % cpr);
-    size_t rest = t / cpr;
-    const int r = static_cast<int>(rest % C);
-    rest /= C;
-    const int g = static_cast<int>(rest % c.nKV);
-    const int b = static_cast<int>(rest / c.nKV);
+  const I total = static_cast<I>(c.B) * c.nKV * C * cpr;
+  for (I t = blockIdx.x * static_cast<I>(blockDim.x) + threadIdx.x; t < total;
+       t += static_cast<I>(gridDim.x) * blockDim.x) {
+    const I row = t / static_cast<I>(cpr);
+    const int ch = static_cast<int>(t - row * cpr);
+    const I bg = row / static_cast<I>(C);
+    const int r = static_cast<int>(row - bg * C);
+    const int g = static_cast<int>(bg % static_cast<I>(c.nKV));
+    const int b = static_cast<int>(bg / static_cast<I>(c.nKV));
     const AppendPlan a = append_plan(c, n_rows, b, C, g == 0 && r == 0 && ch == 0);
     if (a.skip || r >= a.n) continue;
     const int p = a.s0 + r;
@@ -80,42 +82,59 @@ __global__ void __launch_bounds__(256) k_append(cp_cache c, const void *__restri
 }
 
 // Single-workgroup append: the copy, then (after every thread has read seen) the
-// seen update.  Each thread keeps kUnroll rows' chunks in flight at once.
-constexpr int kOneBlock = 1024, kUnroll = 8;
-constexpr size_t kOneBlockChunks = static_cast<size_t>(kOneBlock) * kUnroll;
+// seen update.  The per-sequence plans are formed once into LDS; a thread owns one
+// 16-byte column (cpr divides the block) of rows row0, row0 + rstep, ... and keeps
+// kUnroll of them in flight at once.
+constexpr int kOneBlock = 1024, kUnroll = 8, kOneBlockMaxB = 1024;
+// One CU moves only ~45 GB/s, so one workgroup pays off (it saves a launch, ~1.5 us)
+// only for copies of up to 16 KB per tensor.
+constexpr size_t kOneBlockChunks = 1024;
+
+// The single-workgroup kernels apply: small copy, cpr a power of two, B plans fit LDS.
+bool one_block_ok(const cp_cache &c, int C, int cpr) {
+  return static_cast<size_t>(c.B) * c.nKV * C * cpr <= kOneBlockChunks && c.B <= kOneBlockMaxB &&
+         (cpr & (cpr - 1)) == 0 && cpr <= kOneBlock;
+}
 
 template <typename W>
 __global__ void __launch_bounds__(kOneBlock) k_append_one(cp_cache c, const void *__restrict__ kn,
                                                          const void *__restrict__ vn, int C,
                                                          const int32_t *__restrict__ n_rows,
                                                          int cpr, size_t row_bytes) {
-  const size_t total = static_cast<size_t>(c.B) * c.nKV * C * cpr;
+  __shared__ int plan_s0[kOneBlockMaxB], plan_n[kOneBlockMaxB];  // n < 0: skipped
+  for (int b = threadIdx.x; b < c.B; b += kOneBlock) {
+    const AppendPlan a = append_plan(c, n_rows, b, C, true);
+    plan_s0[b] = a.s0;
+    plan_n[b] = a.skip ? -1 : a.n;
+  }
+  __syncthreads();  // also: every read of seen happens before the update below
+  const int ch = threadIdx.x & (cpr - 1);
+  const int rstep = kOneBlock / cpr;
+  const int rows = c.B * c.nKV * C;
   const size_t w = row_bytes / sizeof(W);
-  for (size_t t0 = threadIdx.x; t0 < total; t0 += static_cast<size_t>(kOneBlock) * kUnroll) {
+  const W *K = static_cast<const W *>(kn);
+  const W *V = static_cast<const W *>(vn);
+  for (int row0 = threadIdx.x / cpr; row0 < rows; row0 += rstep * kUnroll) {
     W kv[kUnroll], vv[kUnroll];
     size_t dst[kUnroll];
     bool go[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const size_t t = t0 + static_cast<size_t>(u) * kOneBlock;
+      const int row = row0 + u * rstep;
       go[u] = false;
       dst[u] = 0;
-      if (t >= total) continue;
-      const int ch = static_cast<int>(t % cpr);
-      size_t rest = t / cpr;
-      const int r = static_cast<int>(rest % C);
-      rest /= C;
-      const int g = static_cast<int>(rest % c.nKV);
-      const int b = static_cast<int>(rest / c.nKV);
-      const AppendPlan a = append_plan(c, n_rows, b, C, g == 0 && r == 0 && ch == 0);
-      if (a.skip || r >= a.n) continue;
-      const int p = a.s0 + r;
-      if (c.ring && p >= c.sink && p < a.s0 + a.n - (c.cap - c.sink)) continue;
+      if (row >= rows) continue;
+      const int bg = row / C, r = row - bg * C;
+      const int b = bg / c.nKV;
+      const int s0 = plan_s0[b], n = plan_n[b];
+      if (r >= n) continue;
+      const int p = s0 + r;
+      if (c.ring && p >= c.sink && p < s0 + n - (c.cap - c.sink)) continue;
       const int sl = slot_of(p, c.cap, c.ring, c.sink);
-      const size_t src = ((static_cast<size_t>(b) * c.nKV + g) * C + r) * w + ch;
-      dst[u] = ((static_cast<size_t>(b) * c.nKV + g) * c.cap + sl) * w + ch;
-      kv[u] = static_cast<const W *>(kn)[src];
-      vv[u] = static_cast<const W *>(vn)[src];
+      dst[u] = (static_cast<size_t>(bg) * c.cap + sl) * w + ch;
+      const size_t src = static_cast<size_t>(row) * w + ch;
+      kv[u] = K[src];
+      vv[u] = V[src];
       go[u] = true;
     }
 #pragma unroll
@@ -125,11 +144,8 @@ __global__ void __launch_bounds__(kOneBlock) k_append_one(cp_cache c, const void
         static_cast<W *>(c.v)[dst[u]] = vv[u];
       }
   }
-  __syncthreads();  // every read of seen above happens before it changes
-  for (int b = threadIdx.x; b < c.B; b += kOneBlock) {
-    const AppendPlan a = append_plan(c, n_rows, b, C, false);
-    if (!a.skip) c.seen[b] = a.s0 + a.n;
-  }
+  for (int b = threadIdx.x; b < c.B; b += kOneBlock)
+    if (plan_n[b] >= 0) c.seen[b] = plan_s0[b] + plan_n[b];
 }
 
 __global__ void k_append_seen(cp_cache c, const int32_t *__restrict__ n_rows, int C) {
@@ -154,7 +170,7 @@ __device__ __forceinline__ void overevicted(const cp_cache &c, int s0, int nv, i
   if (*hi < *lo) *hi = *lo;
 }
 
-template <typename W>
+template <typename W, typename I>
 __global__ void __launch_bounds__(256) k_snapshot(cp_cache c, int C, const int32_t *__restrict__ n_valid,
                                                   unsigned char *__restrict__ buf, size_t hdr,
                                                   int cpr, size_t row_bytes) {
@@ -172,14 +188,14 @@ __global__ void __launch_bounds__(256) k_snapshot(cp_cache c, int C, const int32
     if (s0 < 0) flag(c.status, CP_DEV_SEEN);
     if (!c.ring && s0 + C > c.cap) flag(c.status, CP_DEV_OVERFLOW);
   }
-  const size_t total = static_cast<size_t>(c.B) * c.nKV * C * cpr;
-  for (size_t t = gid; t < total; t += static_cast<size_t>(gridDim.x) * blockDim.x) {
-    const int ch = static_cast<int>(t % cpr);
-    size_t rest = t / cpr;
-    const int r = static_cast<int>(rest % C);
-    rest /= C;
-    const int g = static_cast<int>(rest % c.nKV);
-    const int b = static_cast<int>(rest / c.nKV);
+  const I total = static_cast<I>(c.B) * c.nKV * C * cpr;
+  for (I t = static_cast<I>(gid); t < total; t += static_cast<I>(gridDim.x) * blockDim.x) {
+    const I row = t / static_cast<I>(cpr);
+    const int ch = static_cast<int>(t - row * cpr);
+    const I bg = row / static_cast<I>(C);
+    const int r = static_cast<int>(row - bg * C);
+    const int g = static_cast<int>(bg % static_cast<I>(c.nKV));
+    const int b = static_cast<int>(bg / static_cast<I>(c.nKV));
     const int s0 = c.seen[b];
     const int nv = read_nvalid(n_valid, b, C, nullptr);
     if (s0 < 0) continue;
@@ -194,7 +210,7 @@ __global__ void __launch_bounds__(256) k_snapshot(cp_cache c, int C, const int32
   }
 }
 
-template <typename W>
+template <typename W, typename I>
 __global__ void __launch_bounds__(256) k_restore(cp_cache c, int C, const unsigned char *__restrict__ buf,
                                                  size_t hdr, int cpr, size_t row_bytes) {
   const int32_t *h = reinterpret_cast<const int32_t *>(buf);
@@ -202,15 +218,15 @@ __global__ void __launch_bounds__(256) k_restore(cp_cache c, int C, const unsign
   const W *sk = reinterpret_cast<const W *>(buf + hdr);
   const W *sv = reinterpret_cast<const W *>(buf + hdr + half);
   const size_t w = row_bytes / sizeof(W);
-  const size_t total = static_cast<size_t>(c.B) * c.nKV * C * cpr;
-  for (size_t t = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; t < total;
-       t += static_cast<size_t>(gridDim.x) * blockDim.x) {
-    const int ch = static_cast<int>(t % cpr);
-    size_t rest = t / cpr;
-    const int r = static_cast<int>(rest % C);
-    rest /= C;
-    const int g = static_cast<int>(rest % c.nKV);
-    const int b = static_cast<int>(rest / c.nKV);
+  const I total = static_cast<I>(c.B) * c.nKV * C * cpr;
+  for (I t = blockIdx.x * static_cast<I>(blockDim.x) + threadIdx.x; t < total;
+       t += static_cast<I>(gridDim.x) * blockDim.x) {
+    const I row = t / static_cast<I>(cpr);
+    const int ch = static_cast<int>(t - row * cpr);
+    const I bg = row / static_cast<I>(C);
+    const int r = static_cast<int>(row - bg * C);
+    const int g = static_cast<int>(bg % static_cast<I>(c.nKV));
+    const int b = static_cast<int>(bg / static_cast<I>(c.nKV));
     const int s0 = h[b], nv = h[c.B + b];
     if (s0 < 0 || c.seen[b] != s0 + C) continue;  // flagged by k_rollback_seen
     int lo, hi;
@@ -224,42 +240,50 @@ __global__ void __launch_bounds__(256) k_restore(cp_cache c, int C, const unsign
   }
 }
 
-// Single-workgroup rollback: restore the saved rows, then (after every thread has
-// compared seen) set seen.
+// Single-workgroup rollback: restore the saved rows, then set seen.  As the append:
+// per-sequence state formed once into LDS (every comparison with seen happens
+// before the barrier), one 16-byte column of rows per thread.
 template <typename W>
 __global__ void __launch_bounds__(kOneBlock) k_restore_one(cp_cache c, int C,
                                                           const unsigned char *__restrict__ buf,
                                                           size_t hdr, int cpr, size_t row_bytes) {
+  __shared__ int st_lo[kOneBlockMaxB], st_cnt[kOneBlockMaxB];  // cnt < 0: sequence left alone
   const int32_t *h = reinterpret_cast<const int32_t *>(buf);
+  for (int b = threadIdx.x; b < c.B; b += kOneBlock) {
+    const int s0 = h[b], nv = h[c.B + b];
+    int lo = 0, hi = 0;
+    if (s0 >= 0 && c.seen[b] == s0 + C) {
+      overevicted(c, s0, nv, C, &lo, &hi);
+      st_cnt[b] = hi - lo;
+    } else {
+      st_cnt[b] = -1;
+    }
+    st_lo[b] = lo;
+  }
+  __syncthreads();
   const size_t half = static_cast<size_t>(c.B) * c.nKV * C * row_bytes;
   const W *sk = reinterpret_cast<const W *>(buf + hdr);
   const W *sv = reinterpret_cast<const W *>(buf + hdr + half);
   const size_t w = row_bytes / sizeof(W);
-  const size_t total = static_cast<size_t>(c.B) * c.nKV * C * cpr;
-  for (size_t t0 = threadIdx.x; t0 < total; t0 += static_cast<size_t>(kOneBlock) * kUnroll) {
+  const int ch = threadIdx.x & (cpr - 1);
+  const int rstep = kOneBlock / cpr;
+  const int rows = c.B * c.nKV * C;
+  for (int row0 = threadIdx.x / cpr; row0 < rows; row0 += rstep * kUnroll) {
     W kv[kUnroll], vv[kUnroll];
     size_t dst[kUnroll];
     bool go[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const size_t t = t0 + static_cast<size_t>(u) * kOneBlock;
+      const int row = row0 + u * rstep;
       go[u] = false;
       dst[u] = 0;
-      if (t >= total) continue;
-      const int ch = static_cast<int>(t % cpr);
-      size_t rest = t / cpr;
-      const int r = static_cast<int>(rest % C);
-      rest /= C;
-      const int g = static_cast<int>(rest % c.nKV);
-      const int b = static_cast<int>(rest / c.nKV);
-      const int s0 = h[b], nv = h[c.B + b];
-      if (s0 < 0 || c.seen[b] != s0 + C) continue;
-      int lo, hi;
-      overevicted(c, s0, nv, C, &lo, &hi);
-      if (r >= hi - lo) continue;
-      const int sl = slot_of(lo + r, c.cap, c.ring, c.sink);
-      dst[u] = ((static_cast<size_t>(b) * c.nKV + g) * c.cap + sl) * w + ch;
-      const size_t src = ((static_cast<size_t>(b) * c.nKV + g) * C + r) * w + ch;
+      if (row >= rows) continue;
+      const int bg = row / C, r = row - bg * C;
+      const int b = bg / c.nKV;
+      if (r >= st_cnt[b]) continue;
+      const int sl = slot_of(st_lo[b] + r, c.cap, c.ring, c.sink);
+      dst[u] = (static_cast<size_t>(bg) * c.cap + sl) * w + ch;
+      const size_t src = static_cast<size_t>(row) * w + ch;
       kv[u] = sk[src];
       vv[u] = sv[src];
       go[u] = true;
@@ -271,14 +295,12 @@ __global__ void __launch_bounds__(kOneBlock) k_restore_one(cp_cache c, int C,
         static_cast<W *>(c.v)[dst[u]] = vv[u];
       }
   }
-  __syncthreads();  // every comparison with seen above happens before it changes
   for (int b = threadIdx.x; b < c.B; b += kOneBlock) {
-    const int s0 = h[b], nv = h[c.B + b];
-    if (s0 < 0 || c.seen[b] != s0 + C) {
+    if (st_cnt[b] < 0) {
       flag(c.status, CP_DEV_ROLLBACK);
       continue;
     }
-    c.seen[b] = s0 + nv;
+    c.seen[b] = h[b] + h[c.B + b];
   }
 }
 
@@ -307,36 +329,42 @@ size_t row_bytes_of(const cp_cache &c) {
 
 }  // namespace
 
+// 32-bit indices when every chunk index of a launch over B * nKV * C rows fits.
+static bool fits32(const cp_cache &c, int C, size_t row_bytes) {
+  return static_cast<size_t>(c.B) * c.nKV * C * (row_bytes / 4) < (size_t(1) << 31);
+}
+
+#define CP_LAUNCH_IDX(K, W, grid, ...)                                               \
+  do {                                                                              \
+    if (f32)                                                                        \
+      hipLaunchKernelGGL((K<W, uint32_t>), dim3(grid), dim3(256), 0, s, __VA_ARGS__); \
+    else                                                                            \
+      hipLaunchKernelGGL((K<W, size_t>), dim3(grid), dim3(256), 0, s, __VA_ARGS__);   \
+  } while (0)
+
 hipError_t launch_kv_append(const cp_cache &c, const void *k_new, const void *v_new, int C,
                             const int32_t *n_rows, hipStream_t s) {
   if (c.B == 0) return hipSuccess;
   const size_t rb = row_bytes_of(c);
-  {
-    const bool c16 = rb % 16 == 0;
-    const int cpr = static_cast<int>(c16 ? rb / 16 : rb / 4);
-    if (static_cast<size_t>(c.B) * c.nKV * C * cpr <= kOneBlockChunks) {
-      if (c16)
-        hipLaunchKernelGGL(k_append_one<Chunk16>, dim3(1), dim3(kOneBlock), 0, s, c, k_new,
-                           v_new, C, n_rows, cpr, rb);
-      else
-        hipLaunchKernelGGL(k_append_one<uint32_t>, dim3(1), dim3(kOneBlock), 0, s, c, k_new,
-                           v_new, C, n_rows, cpr, rb);
-      return hipGetLastError();
-    }
+  const bool c16 = rb % 16 == 0;
+  const int cpr = static_cast<int>(c16 ? rb / 16 : rb / 4);
+  const size_t total = static_cast<size_t>(c.B) * c.nKV * C * cpr;
+  if (one_block_ok(c, C, cpr)) {
+    if (c16)
+      hipLaunchKernelGGL(k_append_one<Chunk16>, dim3(1), dim3(kOneBlock), 0, s, c, k_new, v_new,
+                         C, n_rows, cpr, rb);
+    else
+      hipLaunchKernelGGL(k_append_one<uint32_t>, dim3(1), dim3(kOneBlock), 0, s, c, k_new, v_new,
+                         C, n_rows, cpr, rb);
+    return hipGetLastError();
   }
-  if (C > 0) {
-    if (rb % 16 == 0) {
-      const int cpr = static_cast<int>(rb / 16);
-      hipLaunchKernelGGL(k_append<Chunk16>, dim3(grid_for((size_t)c.B * c.nKV * C * cpr)),
-                         dim3(256), 0, s, c, k_new, v_new, C, n_rows, cpr, rb);
-    } else {
-      const int cpr = static_cast<int>(rb / 4);
-      hipLaunchKernelGGL(k_append<uint32_t>, dim3(grid_for((size_t)c.B * c.nKV * C * cpr)),
-                         dim3(256), 0, s, c, k_new, v_new, C, n_rows, cpr, rb);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  const bool f32 = fits32(c, C, rb);
+  if (c16)
+    CP_LAUNCH_IDX(k_append, Chunk16, grid_for(total), c, k_new, v_new, C, n_rows, cpr, rb);
+  else
+    CP_LAUNCH_IDX(k_append, uint32_t, grid_for(total), c, k_new, v_new, C, n_rows, cpr, rb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_append_seen, dim3((c.B + 255) / 256), dim3(256), 0, s, c, n_rows, C);
   return hipGetLastError();
 }
@@ -347,18 +375,16 @@ hipError_t launch_snapshot(const cp_cache &c, int C, const int32_t *n_valid, voi
   const size_t rb = row_bytes_of(c);
   const size_t hdr = snapshot_header_bytes(c.B);
   unsigned char *b = static_cast<unsigned char *>(buf);
+  const bool c16 = rb % 16 == 0;
+  const int cpr = static_cast<int>(c16 ? rb / 16 : rb / 4);
+  const size_t total = static_cast<size_t>(c.B) * c.nKV * C * cpr;
   // the grid always covers B threads: they write the header, even for C == 0
-  if (rb % 16 == 0) {
-    const int cpr = static_cast<int>(rb / 16);
-    const size_t total = (size_t)c.B * c.nKV * C * cpr;
-    hipLaunchKernelGGL(k_snapshot<Chunk16>, dim3(grid_for(total > (size_t)c.B ? total : c.B)),
-                       dim3(256), 0, s, c, C, n_valid, b, hdr, cpr, rb);
-  } else {
-    const int cpr = static_cast<int>(rb / 4);
-    const size_t total = (size_t)c.B * c.nKV * C * cpr;
-    hipLaunchKernelGGL(k_snapshot<uint32_t>, dim3(grid_for(total > (size_t)c.B ? total : c.B)),
-                       dim3(256), 0, s, c, C, n_valid, b, hdr, cpr, rb);
-  }
+  const unsigned grid = grid_for(total > static_cast<size_t>(c.B) ? total : c.B);
+  const bool f32 = fits32(c, C, rb);
+  if (c16)
+    CP_LAUNCH_IDX(k_snapshot, Chunk16, grid, c, C, n_valid, b, hdr, cpr, rb);
+  else
+    CP_LAUNCH_IDX(k_snapshot, uint32_t, grid, c, C, n_valid, b, hdr, cpr, rb);
   return hipGetLastError();
 }
 
@@ -367,34 +393,29 @@ hipError_t launch_rollback(const cp_cache &c, int C, const void *buf, hipStream_
   const size_t rb = row_bytes_of(c);
   const size_t hdr = snapshot_header_bytes(c.B);
   const unsigned char *b = static_cast<const unsigned char *>(buf);
-  {
-    const bool c16 = rb % 16 == 0;
-    const int cpr = static_cast<int>(c16 ? rb / 16 : rb / 4);
-    if (static_cast<size_t>(c.B) * c.nKV * C * cpr <= kOneBlockChunks) {
-      if (c16)
-        hipLaunchKernelGGL(k_restore_one<Chunk16>, dim3(1), dim3(kOneBlock), 0, s, c, C, b, hdr,
-                           cpr, rb);
-      else
-        hipLaunchKernelGGL(k_restore_one<uint32_t>, dim3(1), dim3(kOneBlock), 0, s, c, C, b, hdr,
-                           cpr, rb);
-      return hipGetLastError();
-    }
+  const bool c16 = rb % 16 == 0;
+  const int cpr = static_cast<int>(c16 ? rb / 16 : rb / 4);
+  const size_t total = static_cast<size_t>(c.B) * c.nKV * C * cpr;
+  if (one_block_ok(c, C, cpr)) {
+    if (c16)
+      hipLaunchKernelGGL(k_restore_one<Chunk16>, dim3(1), dim3(kOneBlock), 0, s, c, C, b, hdr, cpr,
+                         rb);
+    else
+      hipLaunchKernelGGL(k_restore_one<uint32_t>, dim3(1), dim3(kOneBlock), 0, s, c, C, b, hdr,
+                         cpr, rb);
+    return hipGetLastError();
   }
-  if (C > 0) {
-    if (rb % 16 == 0) {
-      const int cpr = static_cast<int>(rb / 16);
-      hipLaunchKernelGGL(k_restore<Chunk16>, dim3(grid_for((size_t)c.B * c.nKV * C * cpr)),
-                         dim3(256), 0, s, c, C, b, hdr, cpr, rb);
-    } else {
-      const int cpr = static_cast<int>(rb / 4);
-      hipLaunchKernelGGL(k_restore<uint32_t>, dim3(grid_for((size_t)c.B * c.nKV * C * cpr)),
-                         dim3(256), 0, s, c, C, b, hdr, cpr, rb);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  const bool f32 = fits32(c, C, rb);
+  if (c16)
+    CP_LAUNCH_IDX(k_restore, Chunk16, grid_for(total), c, C, b, hdr, cpr, rb);
+  else
+    CP_LAUNCH_IDX(k_restore, uint32_t, grid_for(total), c, C, b, hdr, cpr, rb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_rollback_seen, dim3((c.B + 255) / 256), dim3(256), 0, s, c, C, b);
   return hipGetLastError();
 }
+
+#undef CP_LAUNCH_IDX
 
 }  // namespace cp

@@ -59,26 +59,29 @@ struct RopeOp {
 // x and y may alias: every element is read and written by the same thread.  The grid
 // covers the rows of a, then those of b (b.Hx = 0 for a single tensor), so Q and K of
 // a chunk are rotated by one launch.
-template <typename T, int VEC>
+// I: index type -- 32-bit whenever the launch's element count allows (integer division
+// is a software sequence, and a 64-bit one several times longer).
+template <typename T, int VEC, typename I>
 __global__ void __launch_bounds__(128) k_rope(RopeOp<T> a, RopeOp<T> bop,
                                               const float *__restrict__ cosb,
                                               const float *__restrict__ sinb, int B, int C, int D,
                                               int Bt) {
   const int h2 = D / 2;
-  const int per_row = h2 / VEC;
-  const size_t rows_a = static_cast<size_t>(B) * a.Hx * C;
-  const size_t rows = rows_a + static_cast<size_t>(B) * bop.Hx * C;
-  const size_t total = rows * per_row;
-  for (size_t t = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; t < total;
-       t += static_cast<size_t>(gridDim.x) * blockDim.x) {
-    size_t row = t / per_row;
-    const int j0 = static_cast<int>(t % per_row) * VEC;
+  const I per_row = h2 / VEC;
+  const I rows_a = static_cast<I>(B) * a.Hx * C;
+  const I rows = rows_a + static_cast<I>(B) * bop.Hx * C;
+  const I total = rows * per_row;
+  for (I t = blockIdx.x * static_cast<I>(blockDim.x) + threadIdx.x; t < total;
+       t += static_cast<I>(gridDim.x) * blockDim.x) {
+    I row = t / per_row;
+    const int j0 = static_cast<int>(t - row * per_row) * VEC;
     const bool second = row >= rows_a;
     const RopeOp<T> &op = second ? bop : a;
     if (second) row -= rows_a;
-    const int i = static_cast<int>(row % C);
-    const int b = static_cast<int>(row / (static_cast<size_t>(op.Hx) * C));
-    const size_t xo = row * D;
+    const I bh = row / static_cast<I>(C);
+    const int i = static_cast<int>(row - bh * C);
+    const int b = static_cast<int>(bh / static_cast<I>(op.Hx));
+    const size_t xo = static_cast<size_t>(row) * D;
     const size_t to = (static_cast<size_t>(Bt == 1 ? 0 : b) * C + i) * D;
     const Pack<T, VEC> lo = *reinterpret_cast<const Pack<T, VEC> *>(op.x + xo + j0);
     const Pack<T, VEC> hi = *reinterpret_cast<const Pack<T, VEC> *>(op.x + xo + j0 + h2);
@@ -118,12 +121,21 @@ hipError_t launch_t(const void *x0, void *y0, int H0, const void *x1, void *y1, 
   constexpr int V16 = 16 / sizeof(T);  // elements per 16 bytes
   bool al = aligned16(x0) && aligned16(y0) && aligned16(cos) && aligned16(sin);
   if (H1 > 0) al = al && aligned16(x1) && aligned16(y1);
+  const bool i32 = rows * h2 < (size_t(1) << 31);
   if (al && h2 % V16 == 0) {
-    hipLaunchKernelGGL((k_rope<T, V16>), dim3(grid_for(V16)), dim3(128), 0, s, a, b, cos, sin,
-                       B, C, D, Bt);
+    if (i32)
+      hipLaunchKernelGGL((k_rope<T, V16, uint32_t>), dim3(grid_for(V16)), dim3(128), 0, s, a, b,
+                         cos, sin, B, C, D, Bt);
+    else
+      hipLaunchKernelGGL((k_rope<T, V16, size_t>), dim3(grid_for(V16)), dim3(128), 0, s, a, b,
+                         cos, sin, B, C, D, Bt);
   } else {
-    hipLaunchKernelGGL((k_rope<T, 1>), dim3(grid_for(1)), dim3(128), 0, s, a, b, cos, sin, B, C,
-                       D, Bt);
+    if (i32)
+      hipLaunchKernelGGL((k_rope<T, 1, uint32_t>), dim3(grid_for(1)), dim3(128), 0, s, a, b, cos,
+                         sin, B, C, D, Bt);
+    else
+      hipLaunchKernelGGL((k_rope<T, 1, size_t>), dim3(grid_for(1)), dim3(128), 0, s, a, b, cos,
+                         sin, B, C, D, Bt);
   }
   return hipGetLastError();
 }

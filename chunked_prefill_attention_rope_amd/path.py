@@ -5,10 +5,9 @@ are appended, so a ring never loses keys the chunk's first rows still need):
 
     rope(Q, K) -> [snapshot] -> attention (+ selected row) -> append -> [rollback]
 
-Q and K are rotated by one launch, the attention writes the last real row into
-the selection as it writes the output, and a small append updates seen in the
-same launch as its copy (the step's launch count: 3 kernels, 4 with a key split,
-plus the snapshot and rollback of a static padded append).
+Q and K are rotated by one launch, and the attention writes the last real row into
+the selection as it writes the output (a tiny append also updates seen in the
+same launch as its copy).
 
 ``static_append=True`` models a caller whose append always writes all C rows
 (a fixed-shape graph): the ring is protected by the padded-append snapshot and

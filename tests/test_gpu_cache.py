@@ -112,8 +112,9 @@ def test_append_bit_exact(cp, case, dtype, D):
 
 @pytest.mark.parametrize("ring", [0, 1])
 def test_append_large_takes_the_multi_block_path(cp, ring):
-    """Appends of more than 8192 16-byte chunks per tensor copy over the whole GPU and
-    update seen in a second launch; small ones do both in one workgroup."""
+    """Appends of more than 1024 16-byte chunks per tensor copy over the whole GPU and
+    update seen in a second launch; tiny ones do both in one workgroup (both paths are
+    also taken by the smaller cases above)."""
     seen = [300, 0, 1200, 77] if ring else [300, 0, 500, 77]
     cfg = I.small(dtype=I.BF16, B=4, H=8, nKV=8, D=128, C=128, cap=1024 if ring else 700,
                   ring=ring, sink=4 if ring else 0, seen=seen, n_valid=[128, 100, 1, 64])

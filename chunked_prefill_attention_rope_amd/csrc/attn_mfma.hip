@@ -4,11 +4,10 @@
 // under an additive mask per head.  Both products are dense contractions, so
 // they run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
 //
-// Work split.  A workgroup holds 4 x 32 query rows (one wave per 32 rows, or two
-// waves sharing them for D = 256, see Cfg); the 128 rows are the G
-// query heads of one KV head times qpos = 128 / G chunk rows, so every K/V
-// tile staged in LDS serves the whole GQA group (read from HBM once per query
-// tile).  Workgroups are mapped so that consecutive query tiles of one
+// Work split.  A workgroup holds ROWS = 128 or 256 query rows in groups of 32 (one
+// wave per group, or two waves sharing it for D = 256, see Cfg); the rows are the G
+// query heads of one KV head times qpos = ROWS / G chunk rows, so every K/V tile
+// staged in LDS serves the whole GQA group (read from HBM once per query tile).  Workgroups are mapped so that consecutive query tiles of one
 // (sequence, KV head) land on the same XCD and share its L2.
 //
 // Orientation.  Each wave computes S^T = K Q^T (32 keys x 32 queries per
@@ -33,7 +32,7 @@
 // exceeds it by more than 2^8 (exact: numerator and denominator share it), so
 // the O accumulator is rarely rescaled.
 //
-// Loads.  K/V tiles -- and, with an explicit mask, the tile's 128 x KT block of
+// Loads.  K/V tiles -- and, with an explicit mask, the tile's ROWS x KT block of
 // mask values -- stream into a ring of LDS stages with direct-to-LDS loads
 // (global_load_lds, 1 KB per wave instruction for K/V, 256 bytes for the mask),
 // STAGES - 1 tiles ahead of the one being computed, without passing through
@@ -163,38 +162,48 @@ __device__ __forceinline__ int kswz(int r) {
 }
 __device__ __forceinline__ int vswz(int r) { return (r & 3) << 1; }
 
-// Per head size and mask mode: keys per tile, LDS ring stages, waves per SIMD, and
-// the number of wave groups the output dims are split over (DSPLIT).  A stage holds
-// one K and one V tile (KT x D bf16 each) and, with an explicit mask, the tile's
-// 128 x KT fp32 mask block.  With DSPLIT = 2 a workgroup has 8 waves: waves w and
-// w + 4 own the same 32 query rows, both form the full scores and probabilities, and
-// each accumulates half of the output dims -- a 256-dim accumulator per wave would
-// leave room for only one wave per SIMD and nothing to hide LDS and MFMA latency.
+// Per head size and mask mode: keys per tile, LDS ring stages, waves per SIMD, the
+// number of 32-row groups of a workgroup (ROWW) and of wave groups the output dims
+// are split over (DSPLIT).  A stage holds one K and one V tile (KT x D bf16 each)
+// and, with an explicit mask, the tile's 32 ROWW x KT fp32 mask block.
+//  - D = 128: one 256-row workgroup of 8 waves per CU (2 per SIMD) rather than two
+//    of 128 rows: each K/V tile serves twice the rows, and the LDS left over holds a
+//    4-stage ring, so a tile is requested three tiles before it is needed.
+//  - D = 256: DSPLIT = 2, a workgroup of 8 waves where waves w and w + 4 own the same
+//    32 query rows, both form the full scores and probabilities, and each accumulates
+//    half of the output dims -- a 256-dim accumulator per wave would leave room for
+//    only one wave per SIMD and nothing to hide LDS and MFMA latency.
 template <int D, bool EX>
 struct Cfg;
 template <>
 struct Cfg<64, false> {
   static constexpr int KT = 64, STAGES = 4, WAVES = 2, DSPLIT = 1;
+  static constexpr int ROWW = 4;
 };
 template <>
 struct Cfg<64, true> {
   static constexpr int KT = 32, STAGES = 3, WAVES = 2, DSPLIT = 1;
+  static constexpr int ROWW = 4;
 };
 template <>
 struct Cfg<128, false> {
-  static constexpr int KT = 64, STAGES = 2, WAVES = 2, DSPLIT = 1;
+  static constexpr int KT = 64, STAGES = 4, WAVES = 2, DSPLIT = 1;
+  static constexpr int ROWW = 8;
 };
 template <>
 struct Cfg<128, true> {
   static constexpr int KT = 32, STAGES = 2, WAVES = 2, DSPLIT = 1;
+  static constexpr int ROWW = 4;
 };
 template <>
 struct Cfg<256, false> {
   static constexpr int KT = 32, STAGES = 4, WAVES = 2, DSPLIT = 2;
+  static constexpr int ROWW = 4;
 };
 template <>
 struct Cfg<256, true> {
   static constexpr int KT = 32, STAGES = 3, WAVES = 2, DSPLIT = 2;
+  static constexpr int ROWW = 4;
 };
 
 // One wave-wide 4-byte direct-to-LDS load (mask blocks: no alignment beyond 4 bytes).
@@ -207,7 +216,7 @@ __device__ __forceinline__ void dma4(const float *src, float *lds_base) {
 #endif
 }
 
-// Swizzle of the 16-byte chunks of row r of a 128 x 32 fp32 mask block (rows of
+// Swizzle of the 16-byte chunks of row r of a ROWS x 32 fp32 mask block (rows of
 // 128 bytes: rows r and r + 1 share a 256-byte bank line).
 __device__ __forceinline__ int mswz(int r) { return (r >> 1) & 7; }
 
@@ -234,7 +243,7 @@ __device__ __forceinline__ void wait_tiles_after(int n) {
 // (set with EXPLICIT, and for the in-kernel rule under CP_ATTN_FULL_TILES so that both
 // modes see the same key partition).
 template <int D, bool EXPLICIT, bool EXT>
-__global__ void __launch_bounds__((256 * Cfg<D, EXT>::DSPLIT))
+__global__ void __launch_bounds__((64 * Cfg<D, EXT>::ROWW * Cfg<D, EXT>::DSPLIT))
     __attribute__((amdgpu_waves_per_eu(Cfg<D, EXT>::WAVES, Cfg<D, EXT>::WAVES)))
     k_attn_mfma(AttnParams p) {
   static_assert(EXT || !EXPLICIT, "explicit masks use the explicit tiling");
@@ -242,7 +251,9 @@ __global__ void __launch_bounds__((256 * Cfg<D, EXT>::DSPLIT))
   constexpr int KT = CF::KT;
   constexpr int STAGES = CF::STAGES;
   constexpr int DSPLIT = CF::DSPLIT;
-  constexpr int NW = 4 * DSPLIT;     // waves per workgroup
+  constexpr int ROWW = CF::ROWW;    // 32-row groups per workgroup
+  constexpr int ROWS = 32 * ROWW;    // query rows per workgroup
+  constexpr int NW = ROWW * DSPLIT;  // waves per workgroup
   constexpr int CPR = D / 8;         // 16-byte chunks per row
   constexpr int NK = KT * CPR;       // chunks per tile (K or V)
   constexpr int NL = NK / (64 * NW); // direct-to-LDS loads per wave per tile per tensor
@@ -253,25 +264,25 @@ __global__ void __launch_bounds__((256 * Cfg<D, EXT>::DSPLIT))
   constexpr int NDW = NDB / DSPLIT;  // ... accumulated by one wave
   constexpr int NPT = KT / 16;       // k-steps of PV
   constexpr int TILE = KT * D;       // bf16 elements of one K (or V) tile
-  constexpr int MT = EXPLICIT ? 128 * KT * 2 : 0;     // mask block (in 16-bit units)
+  constexpr int MT = EXPLICIT ? ROWS * KT * 2 : 0;    // mask block (in 16-bit units)
   constexpr int STAGE = 2 * TILE + MT;
-  constexpr int NMK = EXPLICIT ? 128 * KT / (64 * NW) : 0;  // mask loads per wave per tile
+  constexpr int NMK = EXPLICIT ? ROWS * KT / (64 * NW) : 0;  // mask loads per wave per tile
   constexpr int ND = 2 * NL + NMK;   // direct-to-LDS loads per wave per tile
-  static_assert(!EXPLICIT || (KT == 32 && (128 * KT) % (64 * NW) == 0), "mask block split");
+  static_assert(!EXPLICIT || (KT == 32 && (ROWS * KT) % (64 * NW) == 0), "mask block split");
   static_assert(NK % (64 * NW) == 0, "tile must split evenly over the waves");
   static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
 
   // ring of STAGES x (K tile, V tile[, mask block])
   __shared__ __attribute__((aligned(1024))) uint16_t ring[STAGES * STAGE];
-  // explicit mask: element offset of the mask row of each of the 128 query rows
-  __shared__ int64_t mtab[EXPLICIT ? 128 : 1];
+  // explicit mask: element offset of the mask row of each of the ROWS query rows
+  __shared__ int64_t mtab[EXPLICIT ? ROWS : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int n = lane & 31;
   const int hh = lane >> 5;
-  const int dgrp = wave / 4;         // which NDW dim blocks this wave accumulates
+  const int dgrp = wave / ROWW;      // which NDW dim blocks this wave accumulates
 
   // XCD-aware order: the hardware deals workgroups round-robin over 8 XCDs;
   // give each XCD a contiguous range of work items.
@@ -285,7 +296,7 @@ __global__ void __launch_bounds__((256 * Cfg<D, EXT>::DSPLIT))
   const int b = bg / p.nKV;
   const int g = bg % p.nKV;
 
-  const int r = (wave & 3) * 32 + n;
+  const int r = (wave % ROWW) * 32 + n;
   const int hl = r / p.qpos;
   const int i_min = qtile * p.qpos;
   const int i = i_min + r % p.qpos;
@@ -314,7 +325,7 @@ __global__ void __launch_bounds__((256 * Cfg<D, EXT>::DSPLIT))
   if constexpr (EXPLICIT) {
     // mask row of query row t (rows past the tile's end read a valid row; their
     // results are discarded), then make the table visible to every wave.
-    if (tid < 128) {
+    if (tid < ROWS) {
       const int hl_t = imin(tid / p.qpos, p.G - 1);
       const int i_t = imin(i_min + tid % p.qpos, p.C - 1);
       mtab[tid] = b * p.mbs + static_cast<int64_t>(g * p.G + hl_t) * p.mhs +
@@ -706,13 +717,13 @@ hipError_t launch_d(const AttnParams &p, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   if (p.mask)
     hipLaunchKernelGGL((k_attn_mfma<D, true, true>), dim3(blocks),
-                       dim3(256 * Cfg<D, true>::DSPLIT), 0, s, p);
+                       dim3(64 * Cfg<D, true>::ROWW * Cfg<D, true>::DSPLIT), 0, s, p);
   else if (p.full_tiles)
     hipLaunchKernelGGL((k_attn_mfma<D, false, true>), dim3(blocks),
-                       dim3(256 * Cfg<D, true>::DSPLIT), 0, s, p);
+                       dim3(64 * Cfg<D, true>::ROWW * Cfg<D, true>::DSPLIT), 0, s, p);
   else
     hipLaunchKernelGGL((k_attn_mfma<D, false, false>), dim3(blocks),
-                       dim3(256 * Cfg<D, false>::DSPLIT), 0, s, p);
+                       dim3(64 * Cfg<D, false>::ROWW * Cfg<D, false>::DSPLIT), 0, s, p);
   return hipGetLastError();
 }
 
@@ -729,6 +740,14 @@ hipError_t launch_attn_mfma(const AttnParams &p, int D, hipStream_t s) {
     default:
       return hipErrorInvalidValue;
   }
+}
+
+int mfma_rows_per_tile(int D, bool explicit_tiling) {
+  if (explicit_tiling)
+    return 32 * (D == 256 ? Cfg<256, true>::ROWW
+                          : (D == 128 ? Cfg<128, true>::ROWW : Cfg<64, true>::ROWW));
+  return 32 * (D == 256 ? Cfg<256, false>::ROWW
+                        : (D == 128 ? Cfg<128, false>::ROWW : Cfg<64, false>::ROWW));
 }
 
 int mfma_keys_per_tile(int D, bool explicit_tiling) {

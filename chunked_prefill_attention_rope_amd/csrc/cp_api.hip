@@ -11,6 +11,7 @@
 
 namespace cp {
 int mfma_keys_per_tile(int D, bool explicit_tiling);
+int mfma_rows_per_tile(int D, bool explicit_tiling);
 
 namespace {
 
@@ -41,12 +42,15 @@ AttnPlan plan_attention(const cp_cache &c, const cp_attn_args &a, bool for_works
   const int G = a.H / c.nKV;
   const bool aligned = aligned16(a.q) && aligned16(a.k_new) && aligned16(a.v_new) &&
                        aligned16(a.out) && aligned16(c.k) && aligned16(c.v);
-  pl.mfma = c.dtype == CP_BF16 && (c.D == 64 || c.D == 128 || c.D == 256) && G <= 128 &&
-            !(a.flags & CP_ATTN_FORCE_GENERIC) && aligned;
+  const bool ext = a.mask != nullptr || (a.flags & CP_ATTN_FULL_TILES);
+  const bool mfma_d = c.D == 64 || c.D == 128 || c.D == 256;
+  const int rows = mfma_d ? mfma_rows_per_tile(c.D, ext) : 0;
+  pl.mfma = c.dtype == CP_BF16 && mfma_d && G <= rows && !(a.flags & CP_ATTN_FORCE_GENERIC) &&
+            aligned;
   int hgroups = 1;
   if (pl.mfma) {
-    pl.qpos = 128 / G;
-    pl.kt = mfma_keys_per_tile(c.D, a.mask != nullptr || (a.flags & CP_ATTN_FULL_TILES));
+    pl.qpos = rows / G;
+    pl.kt = mfma_keys_per_tile(c.D, ext);
   } else {
     const int hb = G < 16 ? G : 16;
     hgroups = (G + hb - 1) / hb;

@@ -155,12 +155,19 @@ __device__ __forceinline__ int wave_max_i(int v) {
   return v;
 }
 
-// Swizzle of the 16-byte chunks of LDS row r.
+// Swizzle of the 16-byte chunks of LDS row r.  K: the 16 rows one ds_read_b128 pass
+// reads (one chunk each) land on distinct banks.  V: a 32-lane pass of the transpose
+// read touches 4 rows x 8 chunks; with rows of 256 bytes or more every row starts at
+// bank 0, so the 4 rows' chunk groups are spread by 4 chunks (D = 64 rows alternate
+// bank halves, so 2 chunks suffice there).
 template <int D>
 __device__ __forceinline__ int kswz(int r) {
   return D == 64 ? ((r >> 1) & 7) : (r & 15);
 }
-__device__ __forceinline__ int vswz(int r) { return (r & 3) << 1; }
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  return D == 64 ? (r & 3) << 1 : (r & 3) << 2;
+}
 
 // Per head size and mask mode: keys per tile, LDS ring stages, waves per SIMD, the
 // number of 32-row groups of a workgroup (ROWW) and of wave groups the output dims
@@ -372,7 +379,7 @@ __global__ void __launch_bounds__((64 * Cfg<D, EXT>::ROWW * Cfg<D, EXT>::DSPLIT)
   for (int e = 0; e < NL; ++e) {
     const int row = (wave * NL + e) * RPI + lane / CPR, phys = lane % CPR;
     koff[e] = (phys ^ kswz<D>(row)) << 3;
-    voff[e] = (phys ^ vswz(row)) << 3;
+    voff[e] = (phys ^ vswz<D>(row)) << 3;
   }
   // source rows (cache slot or chunk row) of this wave's loads of tile u
   auto plan = [&](int u, int *srow, int &first, int &lim) __attribute__((always_inline)) {
@@ -427,7 +434,7 @@ __global__ void __launch_bounds__((64 * Cfg<D, EXT>::ROWW * Cfg<D, EXT>::DSPLIT)
   const int k_sw = kswz<D>(n);  // rows 32 kb + n share n's swizzle
   const int s16 = lane & 15;
   const int v_key = 4 * hh + (s16 >> 2);           // + 16 t (+ 8)
-  const int v_sw = vswz(v_key);                   // (16 t + 8 keeps it)
+  const int v_sw = vswz<D>(v_key);                // (16 t + 8 keeps it)
   const int v_cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // chunk within a 32-dim block
   const int v_el = 4 * (lane & 1);
 

@@ -6,15 +6,14 @@
 // additive per-head mask.  One workgroup = 16 query rows (hb heads of one KV
 // group x qpos chunk rows) x 16 lanes per row; a lane owns D/16 output
 // columns.  K/V tiles of 16 keys are staged in LDS as fp32 and shared by the
-// rows; scores are reduced across the 16 lanes of a row with cross-lane
-// shuffles; the softmax is the online (running max / running sum) form in
+// rows; scores are reduced across the 16 lanes of a row with DPP moves; the softmax is the online (running max / running sum) form in
 // base 2 with scale*log2(e) folded into one FMA.  fp32 accumulation.
 #include "attn_common.h"
 
 namespace cp {
 namespace {
 
-constexpr int KTG = 16;   // keys per tile
+constexpr int KTG = 16;  // keys per tile
 constexpr int ROWS = 16;  // query rows per workgroup
 
 template <typename T>
@@ -30,8 +29,26 @@ __device__ __forceinline__ float ld<uint16_t>(const uint16_t *p, size_t i) {
 __device__ __forceinline__ void st(float *p, size_t i, float v) { p[i] = v; }
 __device__ __forceinline__ void st(uint16_t *p, size_t i, float v) { p[i] = f32_to_bf16_rne(v); }
 
+// One DPP move within rows of 16 lanes (a VALU operand modifier: no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// Sum over the 16 lanes of a row, left in every lane (bitwise the same in each: every
+// step adds a lane's value to its partner's, and the partner does the same in the
+// other order).  quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x140>(v);
+  return v;
+}
+
 template <typename T, int DPT, bool EXPLICIT>
 __global__ void __launch_bounds__(256) k_attn_valu(AttnParams p, int D) {
+  constexpr int NF = KTG * DPT / 16;  // >= KTG * D / 256 tile elements per thread
   extern __shared__ float lds[];
   float *Ks = lds;             // [KTG][D]
   float *Vs = lds + KTG * D;   // [KTG][D]
@@ -98,28 +115,63 @@ __global__ void __launch_bounds__(256) k_attn_valu(AttnParams p, int D) {
   const size_t nbase = (static_cast<size_t>(b) * p.nKV + g) * p.C;
   const int qabs = seen + i;
 
+  // K/V tile u into registers: thread tid holds elements tid + 256 j of the KTG x D
+  // tile (KTG * D / 256 <= NF of them), all loads in flight together
+  float kreg[NF], vreg[NF];
+  auto fetch = [&](int u) __attribute__((always_inline)) {
+    int first;
+    const bool chunk = ts.at(u, KTG, &first);
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+      const int e = tid + 256 * j;
+      const int kk = e / D, d = e - kk * D;
+      const int col = first + kk;
+      float kv = 0.f, vv = 0.f;
+      if (e < KTG * D) {
+        if (chunk) {
+          if (col < p.C) {
+            kv = ld<T>(KN, (nbase + col) * D + d);
+            vv = ld<T>(VN, (nbase + col) * D + d);
+          }
+        } else if (col < gl.L) {
+          const int sl = slot_of(column_position(gl, col), p.cap, p.ring, p.sink);
+          kv = ld<T>(KC, (cbase + sl) * D + d);
+          vv = ld<T>(VC, (cbase + sl) * D + d);
+        }
+      }
+      kreg[j] = kv;
+      vreg[j] = vv;
+    }
+  };
+  // explicit mask row of this lane's query row (a valid row for the rows past the
+  // tile's end, whose results are discarded)
+  const float *mrow = nullptr;
+  if (EXPLICIT)
+    mrow = p.mask + b * p.mbs + head * p.mhs + static_cast<int64_t>(i < p.C ? i : 0) * p.mld;
+  if (u0 < u1) fetch(u0);
   for (int u = u0; u < u1; ++u) {
     int first;
     const bool chunk = ts.at(u, KTG, &first);
-    __syncthreads();
-    for (int e = tid; e < KTG * D; e += 256) {
-      const int kk = e / D, d = e % D;
-      const int col = first + kk;
-      float kv = 0.f, vv = 0.f;
-      if (chunk) {
-        if (col < p.C) {
-          kv = ld<T>(KN, (nbase + col) * D + d);
-          vv = ld<T>(VN, (nbase + col) * D + d);
-        }
-      } else if (col < gl.L) {
-        const int sl = slot_of(column_position(gl, col), p.cap, p.ring, p.sink);
-        kv = ld<T>(KC, (cbase + sl) * D + d);
-        vv = ld<T>(VC, (cbase + sl) * D + d);
+    // the tile's KTG mask values: unconditional loads of clamped columns, all in flight
+    // at once (columns past the valid range become -inf below)
+    float madd[KTG];
+    if (EXPLICIT) {
+      const int lim = chunk ? p.C : gl.L;
+      const int64_t mb = chunk ? static_cast<int64_t>(gl.L) : 0;
+#pragma unroll
+      for (int kk = 0; kk < KTG; ++kk) madd[kk] = mrow[mb + imin(first + kk, lim - 1)];
+    }
+    __syncthreads();  // every row is done with the previous tile
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+      const int e = tid + 256 * j;
+      if (e < KTG * D) {
+        Ks[e] = kreg[j];
+        Vs[e] = vreg[j];
       }
-      Ks[e] = kv;
-      Vs[e] = vv;
     }
     __syncthreads();
+    if (u + 1 < u1) fetch(u + 1);  // next tile's loads fly while this one computes
     const bool visible =
         !EXPLICIT && tile_all_visible(chunk, first, KTG, gl, seen, p.C, i_min, i_last, p.window);
     float t[KTG];
@@ -132,21 +184,12 @@ __global__ void __launch_bounds__(256) k_attn_valu(AttnParams p, int D) {
         const int d = ql + 16 * e;
         if (d < D) part = fmaf(q[e], Ks[kk * D + d], part);
       }
-      part += __shfl_xor(part, 8, 16);
-      part += __shfl_xor(part, 4, 16);
-      part += __shfl_xor(part, 2, 16);
-      part += __shfl_xor(part, 1, 16);
+      part = row16_sum(part);
       const int col = first + kk;
       float add;
       if (EXPLICIT) {
         const bool in = chunk ? col < p.C : col < gl.L;
-        if (!in) {
-          add = -INFINITY;
-        } else {
-          const int64_t mc = chunk ? static_cast<int64_t>(gl.L) + col : col;
-          add = row_ok ? p.mask[b * p.mbs + head * p.mhs + static_cast<int64_t>(i) * p.mld + mc]
-                       : 0.f;
-        }
+        add = in ? madd[kk] : -INFINITY;
       } else if (visible) {
         add = 0.f;
       } else {
@@ -315,6 +358,8 @@ hipError_t launch_valu_t(const AttnParams &p, int D, hipStream_t s) {
 }
 
 }  // namespace
+
+int valu_keys(int) { return KTG; }
 
 hipError_t launch_attn_valu(const AttnParams &p, int D, int dtype, hipStream_t s) {
   const bool ex = p.mask != nullptr;

@@ -12,6 +12,7 @@
 namespace cp {
 int mfma_keys_per_tile(int D, bool explicit_tiling);
 int mfma_rows_per_tile(int D, bool explicit_tiling);
+int valu_keys(int D);
 
 namespace {
 
@@ -55,7 +56,7 @@ AttnPlan plan_attention(const cp_cache &c, const cp_attn_args &a, bool for_works
     const int hb = G < 16 ? G : 16;
     hgroups = (G + hb - 1) / hb;
     pl.qpos = 16 / hb;
-    pl.kt = 16;
+    pl.kt = valu_keys(c.D);
   }
   pl.qtiles = (a.C + pl.qpos - 1) / pl.qpos;
   pl.splits = 1;
@@ -69,11 +70,14 @@ AttnPlan plan_attention(const cp_cache &c, const cp_attn_args &a, bool for_works
   const int forced = static_cast<int>((a.flags >> 8) & 0xffu);
   if (forced > 0) {
     pl.splits = forced > 64 ? 64 : forced;
-  } else if (!(a.flags & CP_ATTN_NO_SPLIT) && base > 0 && base < kNumCU && tiles >= 8) {
-    // Few query tiles: split the keys so that more CUs work, but keep >= 4 key tiles per
-    // split -- each split writes fp32 partials that a second kernel merges.
+  } else if (!(a.flags & CP_ATTN_NO_SPLIT) && base > 0 && base < kNumCU) {
+    // Few query tiles: split the keys so that more CUs work -- each split writes fp32
+    // partials that a second kernel merges.  The matrix-core kernel keeps >= 4 key tiles
+    // per split; the vector-ALU kernel's 16-key tiles each cost a memory round trip that
+    // their arithmetic does not hide, so it goes down to one tile per split.
+    const long per = pl.mfma ? 4 : 1;
     long s = (2 * kNumCU + base - 1) / base;
-    if (s > tiles / 4) s = tiles / 4;
+    if (s > tiles / per) s = tiles / per;
     if (s > 64) s = 64;
     pl.splits = s > 1 ? static_cast<int>(s) : 1;
   }

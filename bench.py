@@ -206,6 +206,63 @@ def cpu_baseline(layers, seconds):
                       f"{os.cpu_count()} host CPUs visible"}
 
 
+# Bandwidth sweep: each workload's per-sequence shape at sizes where the attention can
+# be HBM-bound (c2's shape batched; c4 and the c5 global layer at small chunks).
+SWEEP = ([("c2", dict(B=b, explicit_mask=em)) for em in (True, False) for b in (1, 16, 64, 256)]
+         + [(n, dict(C=c)) for n in ("c4", "c5g") for c in (16, 32, 64)])
+
+
+def launch_latency_us():
+    """Duration of a one-element device kernel per launch in a HIP graph (the floor any
+    launch of the path pays)."""
+    x = torch.zeros(1, device="cuda")
+    ms, _ = time_graph(lambda: [x.add_(1.0) for _ in range(200)], 200)
+    return ms * 1e3 / 200
+
+
+def sweep(out_path):
+    """Time the attention call alone on the SWEEP shapes; print a markdown table (and
+    JSON lines to out_path).  Not the contract line: a separate measurement mode."""
+    from chunked_prefill_attention_rope_amd import cp, path
+    torch.cuda.set_device(0)
+    lat = launch_latency_us()
+    rows = []
+    for name, kw in SWEEP:
+        cfg = I.derived(name, **kw)
+        lay = Layer(cp, path, cfg, 1, 0)
+        d = lay.d
+        cp.rope_qk_chunk(d["q"], d["k"], d["cos"], d["sin"], q_out=lay.bufs.q_rot,
+                         k_out=lay.bufs.k_rot)
+        reps = 20 if name == "c5g" else 100
+        ms, _ = time_graph(lambda: [lay.attn_only(cp) for _ in range(reps)], reps)
+        us = ms * 1e3 / reps
+        nbytes, flops = algorithmic(cfg)
+        row = {"shape": name, "B": cfg.B, "C": cfg.C, "G": cfg.G, "D": cfg.D,
+               "mask": "explicit" if cfg.explicit_mask else "in-kernel",
+               "attn_us": round(us, 3), "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+               "flop_per_byte": round(flops / nbytes, 1),
+               "hbm_gbs": round(nbytes / us / 1e3, 1),
+               "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+               "tflops": round(flops / us / 1e6, 1),
+               "mfma_frac": round(flops / us / 1e6 / BF16_PEAK_TFLOPS, 4),
+               "launch_latency_us": round(lat, 3)}
+        rows.append(row)
+        print(json.dumps(row), file=sys.stderr, flush=True)
+        del lay
+        torch.cuda.empty_cache()
+    print(f"launch latency (one-element kernel in a graph): {lat:.2f} us")
+    print("| shape | B | C | mask | flop/B | attention us | GB/s | % HBM | TFLOP/s | % MFMA |")
+    print("|---|---:|---:|---|---:|---:|---:|---:|---:|---:|")
+    for r in rows:
+        print(f"| {r['shape']} | {r['B']} | {r['C']} | {r['mask']} | {r['flop_per_byte']} | "
+              f"{r['attn_us']} | {r['hbm_gbs']} | {100 * r['hbm_frac']:.1f} | {r['tflops']} | "
+              f"{100 * r['mfma_frac']:.1f} |")
+    if out_path:
+        with open(out_path, "w") as f:
+            for r in rows:
+                f.write(json.dumps(r) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -218,11 +275,17 @@ def main():
     ap.add_argument("--attn-reps", type=int, default=200)
     ap.add_argument("--attn-flags", type=int, default=0,
                     help="CP_ATTN_* flags for the attention call (e.g. a forced split count)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead: the attention alone on the bandwidth-sweep shapes")
+    ap.add_argument("--sweep-out", default=None, help="JSON lines of the sweep")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU: this path has no multi-GPU mode (see DESIGN.md for "
               "how it would shard); use --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        sweep(args.sweep_out)
+        return
 
     from chunked_prefill_attention_rope_amd import cp, path
 

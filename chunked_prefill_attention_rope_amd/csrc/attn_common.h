@@ -31,6 +31,7 @@ struct AttnParams {
   int splits;
   int full_tiles;
   int mask_vec4;  // explicit mask rows may be read 16 bytes at a time
+  int small_rows; // matrix-core kernel: the 64-row configuration
   float sl2e;     // scale * log2(e)
 };
 

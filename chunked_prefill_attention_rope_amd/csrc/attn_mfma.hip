@@ -213,6 +213,19 @@ struct Cfg<256, true> {
   static constexpr int ROWW = 4;
 };
 
+// Small-rows configuration, for chunks whose rows of one KV head fit 64 (C * G <= 64,
+// decode steps included): 64-row workgroups of 32-key tiles in a 2-stage ring, so that
+// several workgroups share a CU and stream independent K/V (the regime is HBM-bound:
+// a standard workgroup would leave most of its rows empty and stream one tile at a
+// time per CU).
+template <int D, bool EX, bool SMALL>
+struct Sel : Cfg<D, EX> {};
+template <int D, bool EX>
+struct Sel<D, EX, true> {
+  static constexpr int KT = 32, STAGES = 2, WAVES = 2, DSPLIT = Cfg<D, EX>::DSPLIT;
+  static constexpr int ROWW = 2;
+};
+
 // One wave-wide 4-byte direct-to-LDS load (mask blocks: no alignment beyond 4 bytes).
 __device__ __forceinline__ void dma4(const float *src, float *lds_base) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -249,12 +262,12 @@ __device__ __forceinline__ void wait_tiles_after(int n) {
 // EXPLICIT: the additive mask comes from memory.  EXT: use the explicit-mask tiling
 // (set with EXPLICIT, and for the in-kernel rule under CP_ATTN_FULL_TILES so that both
 // modes see the same key partition).
-template <int D, bool EXPLICIT, bool EXT>
-__global__ void __launch_bounds__((64 * Cfg<D, EXT>::ROWW * Cfg<D, EXT>::DSPLIT))
-    __attribute__((amdgpu_waves_per_eu(Cfg<D, EXT>::WAVES, Cfg<D, EXT>::WAVES)))
+template <int D, bool EXPLICIT, bool EXT, bool SMALL>
+__global__ void __launch_bounds__((64 * Sel<D, EXT, SMALL>::ROWW * Sel<D, EXT, SMALL>::DSPLIT))
+    __attribute__((amdgpu_waves_per_eu(Sel<D, EXT, SMALL>::WAVES, Sel<D, EXT, SMALL>::WAVES)))
     k_attn_mfma(AttnParams p) {
   static_assert(EXT || !EXPLICIT, "explicit masks use the explicit tiling");
-  using CF = Cfg<D, EXT>;
+  using CF = Sel<D, EXT, SMALL>;
   constexpr int KT = CF::KT;
   constexpr int STAGES = CF::STAGES;
   constexpr int DSPLIT = CF::DSPLIT;
@@ -718,19 +731,31 @@ __global__ void __launch_bounds__((64 * Cfg<D, EXT>::ROWW * Cfg<D, EXT>::DSPLIT)
   }
 }
 
+template <int D, bool EXPLICIT, bool EXT, bool SMALL>
+void launch_one(const AttnParams &p, unsigned blocks, hipStream_t s) {
+  using CF = Sel<D, EXT, SMALL>;
+  hipLaunchKernelGGL((k_attn_mfma<D, EXPLICIT, EXT, SMALL>), dim3(blocks),
+                     dim3(64 * CF::ROWW * CF::DSPLIT), 0, s, p);
+}
+
+template <int D, bool SMALL>
+void launch_mode(const AttnParams &p, unsigned blocks, hipStream_t s) {
+  if (p.mask)
+    launch_one<D, true, true, SMALL>(p, blocks, s);
+  else if (p.full_tiles)
+    launch_one<D, false, true, SMALL>(p, blocks, s);
+  else
+    launch_one<D, false, false, SMALL>(p, blocks, s);
+}
+
 template <int D>
 hipError_t launch_d(const AttnParams &p, hipStream_t s) {
   const unsigned blocks = static_cast<unsigned>(p.qtiles) * p.splits * p.B * p.nKV;
   if (blocks == 0) return hipSuccess;
-  if (p.mask)
-    hipLaunchKernelGGL((k_attn_mfma<D, true, true>), dim3(blocks),
-                       dim3(64 * Cfg<D, true>::ROWW * Cfg<D, true>::DSPLIT), 0, s, p);
-  else if (p.full_tiles)
-    hipLaunchKernelGGL((k_attn_mfma<D, false, true>), dim3(blocks),
-                       dim3(64 * Cfg<D, true>::ROWW * Cfg<D, true>::DSPLIT), 0, s, p);
+  if (p.small_rows)
+    launch_mode<D, true>(p, blocks, s);
   else
-    hipLaunchKernelGGL((k_attn_mfma<D, false, false>), dim3(blocks),
-                       dim3(64 * Cfg<D, false>::ROWW * Cfg<D, false>::DSPLIT), 0, s, p);
+    launch_mode<D, false>(p, blocks, s);
   return hipGetLastError();
 }
 
@@ -749,18 +774,25 @@ hipError_t launch_attn_mfma(const AttnParams &p, int D, hipStream_t s) {
   }
 }
 
-int mfma_rows_per_tile(int D, bool explicit_tiling) {
-  if (explicit_tiling)
-    return 32 * (D == 256 ? Cfg<256, true>::ROWW
-                          : (D == 128 ? Cfg<128, true>::ROWW : Cfg<64, true>::ROWW));
-  return 32 * (D == 256 ? Cfg<256, false>::ROWW
-                        : (D == 128 ? Cfg<128, false>::ROWW : Cfg<64, false>::ROWW));
+template <bool EX, bool SMALL>
+int rows_of(int D) {
+  return 32 * (D == 256 ? Sel<256, EX, SMALL>::ROWW
+                        : (D == 128 ? Sel<128, EX, SMALL>::ROWW : Sel<64, EX, SMALL>::ROWW));
+}
+template <bool EX, bool SMALL>
+int keys_of(int D) {
+  return D == 256 ? Sel<256, EX, SMALL>::KT
+                  : (D == 128 ? Sel<128, EX, SMALL>::KT : Sel<64, EX, SMALL>::KT);
 }
 
-int mfma_keys_per_tile(int D, bool explicit_tiling) {
-  if (explicit_tiling)
-    return D == 256 ? Cfg<256, true>::KT : (D == 128 ? Cfg<128, true>::KT : Cfg<64, true>::KT);
-  return D == 256 ? Cfg<256, false>::KT : (D == 128 ? Cfg<128, false>::KT : Cfg<64, false>::KT);
+int mfma_rows_per_tile(int D, bool explicit_tiling, bool small_rows) {
+  if (small_rows) return explicit_tiling ? rows_of<true, true>(D) : rows_of<false, true>(D);
+  return explicit_tiling ? rows_of<true, false>(D) : rows_of<false, false>(D);
+}
+
+int mfma_keys_per_tile(int D, bool explicit_tiling, bool small_rows) {
+  if (small_rows) return explicit_tiling ? keys_of<true, true>(D) : keys_of<false, true>(D);
+  return explicit_tiling ? keys_of<true, false>(D) : keys_of<false, false>(D);
 }
 
 }  // namespace cp

@@ -10,8 +10,8 @@
 #include "attn_common.h"
 
 namespace cp {
-int mfma_keys_per_tile(int D, bool explicit_tiling);
-int mfma_rows_per_tile(int D, bool explicit_tiling);
+int mfma_keys_per_tile(int D, bool explicit_tiling, bool small_rows);
+int mfma_rows_per_tile(int D, bool explicit_tiling, bool small_rows);
 int valu_keys(int D);
 
 namespace {
@@ -45,13 +45,15 @@ AttnPlan plan_attention(const cp_cache &c, const cp_attn_args &a, bool for_works
                        aligned16(a.out) && aligned16(c.k) && aligned16(c.v);
   const bool ext = a.mask != nullptr || (a.flags & CP_ATTN_FULL_TILES);
   const bool mfma_d = c.D == 64 || c.D == 128 || c.D == 256;
-  const int rows = mfma_d ? mfma_rows_per_tile(c.D, ext) : 0;
+  // all rows of one KV head fit 64: the small-rows configuration
+  pl.small_rows = static_cast<long>(a.C) * G <= 64;
+  const int rows = mfma_d ? mfma_rows_per_tile(c.D, ext, pl.small_rows) : 0;
   pl.mfma = c.dtype == CP_BF16 && mfma_d && G <= rows && !(a.flags & CP_ATTN_FORCE_GENERIC) &&
             aligned;
   int hgroups = 1;
   if (pl.mfma) {
     pl.qpos = rows / G;
-    pl.kt = mfma_keys_per_tile(c.D, ext);
+    pl.kt = mfma_keys_per_tile(c.D, ext, pl.small_rows);
   } else {
     const int hb = G < 16 ? G : 16;
     hgroups = (G + hb - 1) / hb;
@@ -76,7 +78,9 @@ AttnPlan plan_attention(const cp_cache &c, const cp_attn_args &a, bool for_works
     // per split; the vector-ALU kernel's 16-key tiles each cost a memory round trip that
     // their arithmetic does not hide, so it goes down to one tile per split.
     const long per = pl.mfma ? 4 : 1;
-    long s = (2 * kNumCU + base - 1) / base;
+    // several small-rows workgroups share a CU
+    const long target = (pl.mfma && pl.small_rows ? 4 : 2) * kNumCU;
+    long s = (target + base - 1) / base;
     if (s > tiles / per) s = tiles / per;
     if (s > 64) s = 64;
     pl.splits = s > 1 ? static_cast<int>(s) : 1;
@@ -127,6 +131,7 @@ hipError_t launch_attention(const cp_cache &c, const cp_attn_args &a, hipStream_
   p.mask_vec4 = a.mask && aligned16(a.mask) && a.mask_ld % 4 == 0 && a.mask_head_stride % 4 == 0 &&
                 a.mask_batch_stride % 4 == 0;
   p.sl2e = a.scale * kLog2e;
+  p.small_rows = pl.small_rows ? 1 : 0;
   if (pl.splits > 1) {
     const size_t rows = static_cast<size_t>(c.B) * a.H * a.C;
     unsigned char *w = static_cast<unsigned char *>(a.workspace);

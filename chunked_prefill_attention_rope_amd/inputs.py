@@ -101,6 +101,30 @@ def config(name: str, layer: int = 0) -> LayerCfg:
     raise ValueError(f"unknown workload {name}")
 
 
+def derived(name: str, B: Optional[int] = None, C: Optional[int] = None,
+            explicit_mask: Optional[bool] = None) -> LayerCfg:
+    """A workload's per-sequence shape at another batch or chunk size (the bandwidth
+    sweep): c2 at batch B (every sequence 800 cached, 52 of 64 rows real), c4 (its 16
+    seeded past lengths) and the c5 global layer at chunk C (all rows real)."""
+    if name == "c2":
+        cfg = config("c2")
+        nb = B or cfg.B
+        cfg.B, cfg.seen, cfg.n_valid = nb, [800] * nb, [52] * nb
+    elif name == "c4":
+        cfg = config("c4")
+        c = C or cfg.C
+        cfg.C, cfg.cap, cfg.n_valid = c, 4096 + c, [c] * cfg.B
+    elif name == "c5g":
+        cfg = config("c5", 5)
+        c = C or cfg.C
+        cfg.C, cfg.n_valid = c, [c] * cfg.B
+    else:
+        raise ValueError(f"no derived shapes of {name}")
+    if explicit_mask is not None:
+        cfg.explicit_mask = explicit_mask
+    return cfg
+
+
 def rope_tables(cfg: LayerCfg):
     """Caller-side per-position cos/sin tables [Bt, C, D] (fp32).
 

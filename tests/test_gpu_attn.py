@@ -94,7 +94,15 @@ SMALL = [
          window=64, seen=[150], n_valid=[20]),
     dict(name="odd_d40", dtype=I.BF16, B=1, H=4, nKV=1, D=40, C=12, cap=50, seen=[9],
          n_valid=[12]),
+    # C * G <= 64: the matrix-core kernel's small-rows configuration
+    dict(name="small_c16_d128", dtype=I.BF16, B=2, H=8, nKV=2, D=128, C=16, cap=300,
+         seen=[100, 250], n_valid=[16, 9]),
+    dict(name="small_c8_d64_window", dtype=I.BF16, B=2, H=4, nKV=1, D=64, C=8, cap=200,
+         window=40, seen=[150, 3], n_valid=[8, 5]),
+    dict(name="decode_d256_ring", dtype=I.BF16, B=2, H=8, nKV=1, D=256, C=1, cap=96, ring=1,
+         window=96, seen=[50, 400], n_valid=[1, 1]),
 ]
+SMALL_ROWS = SMALL[-3:]
 
 
 @pytest.mark.parametrize("kw", SMALL, ids=lambda c: c["name"])
@@ -114,7 +122,7 @@ def test_attention_matches_oracle(cp, kw, mode, kernel, split):
     assert int(status.item()) == 0
 
 
-@pytest.mark.parametrize("kw", SMALL[:6], ids=lambda c: c["name"])
+@pytest.mark.parametrize("kw", SMALL[:6] + SMALL_ROWS, ids=lambda c: c["name"])
 @pytest.mark.parametrize("kernel", [0, 2])
 def test_explicit_mask_equals_inkernel_bitwise(cp, kw, kernel):
     """On the same key partition with the mask evaluated on every tile (no split,
@@ -162,7 +170,7 @@ def test_select_out_equals_select_row(cp, kw, split):
     np.testing.assert_array_equal(bits(sel2), bits(out2[:, :, cfg.C - 1]))
 
 
-@pytest.mark.parametrize("kw", SMALL[:5], ids=lambda c: c["name"])
+@pytest.mark.parametrize("kw", SMALL[:5] + SMALL_ROWS, ids=lambda c: c["name"])
 def test_run_twice_is_deterministic(cp, kw):
     kw = dict(kw)
     kw.pop("name")

@@ -304,15 +304,27 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SMALL>::ROWW * Sel<D, EXT, S
   const int hh = lane >> 5;
   const int dgrp = wave / ROWW;      // which NDW dim blocks this wave accumulates
 
-  // XCD-aware order: the hardware deals workgroups round-robin over 8 XCDs;
-  // give each XCD a contiguous range of work items.
-  const unsigned nblk = gridDim.x;
-  unsigned wk = blockIdx.x;
-  if (nblk % 8 == 0) wk = (wk % 8) * (nblk / 8) + wk / 8;
-  const int qtile = wk % p.qtiles;
-  wk /= p.qtiles;
-  const int split = wk % p.splits;
-  const int bg = wk / p.splits;
+  // Block order.  The hardware dispatches blocks in order and deals them round-robin
+  // over 8 XCDs.  The query tiles of one (split, sequence, KV head) group read the same
+  // K/V, so they go to one XCD and share its L2; the groups are dealt round-robin over
+  // the XCDs, so that sequences of different lengths spread evenly (each XCD drains
+  // only its own blocks); and the split index varies slowest, so that the first part
+  // of every sequence starts at once and the later parts of long sequences fill the
+  // CUs that short sequences free.
+  const unsigned nbg = static_cast<unsigned>(p.B) * p.nKV;
+  const unsigned groups = static_cast<unsigned>(p.splits) * nbg;
+  unsigned gi, qt;
+  if (groups % 8 == 0) {
+    const unsigned rest = blockIdx.x / 8;
+    qt = rest % p.qtiles;
+    gi = (rest / p.qtiles) * 8 + blockIdx.x % 8;
+  } else {
+    qt = blockIdx.x % p.qtiles;
+    gi = blockIdx.x / p.qtiles;
+  }
+  const int qtile = static_cast<int>(qt);
+  const int split = static_cast<int>(gi / nbg);
+  const int bg = static_cast<int>(gi % nbg);
   const int b = bg / p.nKV;
   const int g = bg % p.nKV;
 

@@ -209,7 +209,10 @@ def cpu_baseline(layers, seconds):
 # Bandwidth sweep: each workload's per-sequence shape at sizes where the attention can
 # be HBM-bound (c2's shape batched; c4 and the c5 global layer at small chunks).
 SWEEP = ([("c2", dict(B=b, explicit_mask=em)) for em in (True, False) for b in (1, 16, 64, 256)]
-         + [(n, dict(C=c)) for n in ("c4", "c5g") for c in (16, 32, 64)])
+         + [(n, dict(C=c)) for n in ("c4", "c5g") for c in (1, 16, 32, 64)])
+
+# Prompt-tail sweep: real tokens of a tail, run as one padded chunk or token by token.
+TAIL_SWEEP = [1, 2, 3, 4, 6, 8, 9, 10, 12, 16, 24, 32, 48, 64, 96, 127]
 
 
 def launch_latency_us():
@@ -263,6 +266,49 @@ def sweep(out_path):
                 f.write(json.dumps(r) + "\n")
 
 
+def tail_sweep(out_path, reps=20):
+    """The [cactus] tail experiment on one layer of c3's shape (sliding ring W512 holding
+    1023 positions, C128, H8/KV1 D256): a tail of n real tokens as one padded chunk step
+    (snapshot, static append of 128 rows, rollback) against n one-token steps (RoPE,
+    attention with C = 1, append of one row).  Each mode is a HIP graph of `reps`
+    back-to-back tails; prints a markdown table and the breakeven."""
+    from chunked_prefill_attention_rope_amd import cp, path
+    torch.cuda.set_device(0)
+    cfg = I.config("c3")
+    t = I.make_layer(cfg, nan_dead=False)
+    d = {k: v.to("cuda") for k, v in t.items()}
+    cache = cp.KVCache(d["kc"], d["vc"], d["seen"], ring=cfg.ring, sink=cfg.sink)
+    q, k, v, cos, sin = d["q"], d["k"], d["v"], d["cos"], d["sin"]
+    W = cfg.window
+    bufs = path.make_buffers(cache, q, k, v, window=W, static_append=True)
+    rows = []
+    for n in TAIL_SWEEP:
+        nv = torch.full((cfg.B,), n, dtype=torch.int32, device="cuda")
+        steps = path.token_steps(cache, q, k, v, cos, sin, n, window=W)
+        ms_p, _ = time_graph(lambda: [path.chunk_step(cache, q, k, v, cos, sin, nv, bufs, window=W,
+                                                      static_append=True)
+                                      for _ in range(reps)], reps)
+        ms_s, _ = time_graph(lambda: [path.scalar_tail(cache, steps, window=W)
+                                      for _ in range(reps)], reps)
+        row = {"n_tail": n, "padded_us": round(ms_p * 1e3 / reps, 2),
+               "scalar_us": round(ms_s * 1e3 / reps, 2),
+               "scalar_us_per_token": round(ms_s * 1e3 / reps / n, 2)}
+        rows.append(row)
+        print(json.dumps(row), file=sys.stderr, flush=True)
+        del steps
+    even = next((r["n_tail"] for r in rows if r["scalar_us"] > r["padded_us"]), None)
+    print("| tail tokens | padded chunk us | token by token us | us per token |")
+    print("|---:|---:|---:|---:|")
+    for r in rows:
+        print(f"| {r['n_tail']} | {r['padded_us']} | {r['scalar_us']} | {r['scalar_us_per_token']} |")
+    print(f"breakeven: padding wins from {even} tail tokens on this GPU "
+          f"(the pages' threshold: pad from {path.PAD_FROM})")
+    if out_path:
+        with open(out_path, "w") as f:
+            for r in rows:
+                f.write(json.dumps(r) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,6 +324,8 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="instead: the attention alone on the bandwidth-sweep shapes")
     ap.add_argument("--sweep-out", default=None, help="JSON lines of the sweep")
+    ap.add_argument("--tail-sweep", action="store_true",
+                    help="instead: padded-chunk vs token-by-token prompt tails (c3's shape)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU: this path has no multi-GPU mode (see DESIGN.md for "
@@ -285,6 +333,9 @@ def main():
         sys.exit(2)
     if args.sweep:
         sweep(args.sweep_out)
+        return
+    if args.tail_sweep:
+        tail_sweep(args.sweep_out)
         return
 
     from chunked_prefill_attention_rope_amd import cp, path

@@ -13,9 +13,16 @@ same launch as its copy).
 (a fixed-shape graph): the ring is protected by the padded-append snapshot and
 rollback ([cactus] "Fix").  Otherwise only the n_valid real rows are appended.
 Every step runs in libcp's kernels; this module only sequences the calls.
+
+The tail of a prompt (fewer real tokens than a chunk) runs either as one padded
+chunk or token by token -- one-token steps, the decode contract of [TICO]
+"Runtime behavior" -- chosen by `pad_tail` ([cactus] "Fix": pad from 9 tokens,
+with a kill switch that forces token by token).
 """
+import dataclasses
+import os
 from dataclasses import dataclass
-from typing import Optional
+from typing import List, Optional
 
 import torch
 
@@ -63,3 +70,77 @@ def chunk_step(cache: cp.KVCache, q, k, v, cos, sin, n_valid, bufs: StepBuffers,
     if static_append:
         cp.kv_rollback_padded_append(cache, bufs.snap)
     return bufs.out, bufs.sel
+
+
+# ------------------------------------------------------------- prompt tails
+
+PAD_FROM = 9  # [cactus] "Fix": tails of up to 8 tokens stay token by token
+KILL_SWITCH = "CP_DISABLE_PREFILL_TAIL_PAD"
+
+
+def pad_tail(n_tail: int, pad_from: int = PAD_FROM) -> bool:
+    """Tail policy: True runs a tail of n_tail real tokens as one padded chunk, False token
+    by token.  The environment variable CP_DISABLE_PREFILL_TAIL_PAD=1 (any value but
+    empty or 0) forces token by token.  `pad_from` is the hardware's breakeven; the
+    default is the pages' (measured on another machine) -- `bench.py --tail-sweep`
+    measures it on this one."""
+    if os.environ.get(KILL_SWITCH, "") not in ("", "0"):
+        return False
+    return n_tail >= pad_from
+
+
+@dataclass
+class TokenSteps:
+    """Per-token inputs of a tail (what a decode loop receives per step) and the
+    one-token step buffers: each token has its own output and selection, the rotated
+    q/k and the workspace are shared."""
+    q: List[torch.Tensor]
+    k: List[torch.Tensor]
+    v: List[torch.Tensor]
+    cos: List[torch.Tensor]
+    sin: List[torch.Tensor]
+    bufs: List[StepBuffers]
+    ones: torch.Tensor
+
+
+def token_steps(cache: cp.KVCache, q, k, v, cos, sin, n_tail: int, window: int = 0) -> TokenSteps:
+    """Split rows [0, n_tail) of a chunk's inputs into one-token steps (token j sits at
+    position seen + j, so it takes row j of the chunk's tables)."""
+    B, H, C, D = q.shape
+    if not 0 < n_tail <= C:
+        raise ValueError("n_tail must be in [1, C]")
+    row = lambda t, j: t[:, :, j:j + 1].contiguous()
+    trow = lambda t, j: t[:, j:j + 1].contiguous()
+    qs = [row(q, j) for j in range(n_tail)]
+    ks = [row(k, j) for j in range(n_tail)]
+    vs = [row(v, j) for j in range(n_tail)]
+    base = make_buffers(cache, qs[0], ks[0], vs[0], window=window)
+    bufs = [dataclasses.replace(base, out=torch.empty_like(qs[0]),
+                                sel=torch.empty_like(base.sel)) for _ in range(n_tail)]
+    return TokenSteps(qs, ks, vs, [trow(cos, j) for j in range(n_tail)],
+                      [trow(sin, j) for j in range(n_tail)], bufs,
+                      torch.ones(B, dtype=torch.int32, device=q.device))
+
+
+def scalar_tail(cache: cp.KVCache, steps: TokenSteps, window: int = 0):
+    """The tail token by token: per token RoPE -> attention over past + 1 key (C = 1)
+    -> append of one row.  Returns the per-token outputs [B, H, 1, D] and the last
+    token's selection."""
+    for j in range(len(steps.q)):
+        chunk_step(cache, steps.q[j], steps.k[j], steps.v[j], steps.cos[j], steps.sin[j],
+                   steps.ones, steps.bufs[j], window=window)
+    return [b.out for b in steps.bufs], steps.bufs[-1].sel
+
+
+def prefill_tail(cache: cp.KVCache, q, k, v, cos, sin, n_valid, n_tail: int,
+                 chunk_bufs: StepBuffers, steps: TokenSteps, mask=None, window: int = 0,
+                 static_append: bool = False, pad_from: int = PAD_FROM):
+    """Run a prompt tail of n_tail real tokens (n_valid holds n_tail per sequence) by the
+    tail policy.  Returns ("padded", out [B, H, C, D], sel) or ("scalar", [out per
+    token], sel)."""
+    if pad_tail(n_tail, pad_from):
+        out, sel = chunk_step(cache, q, k, v, cos, sin, n_valid, chunk_bufs, mask=mask,
+                              window=window, static_append=static_append)
+        return "padded", out, sel
+    outs, sel = scalar_tail(cache, steps, window=window)
+    return "scalar", outs, sel

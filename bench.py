@@ -309,6 +309,66 @@ def tail_sweep(out_path, reps=20):
                 f.write(json.dumps(r) + "\n")
 
 
+# Chunk-size sweep: a whole prompt prefilled in chunks of C on one layer of a workload's
+# shape, from an empty global cache.
+CHUNK_SWEEP_PROMPT = 1023
+CHUNK_SWEEP_SIZES = [16, 32, 64, 128, 256, 512]
+CHUNK_SWEEP_SHAPES = {
+    "c2": dict(B=1, H=4, nKV=1, D=256, base=1e6),   # Gemma-270M-like
+    "c4": dict(B=4, H=32, nKV=8, D=128, base=5e5),  # Llama-8B-like GQA
+}
+
+
+def chunk_sweep(out_path, reps=5):
+    """Prefill a CHUNK_SWEEP_PROMPT-token prompt on one layer in chunks of each size (each
+    rep from an empty cache), then apply the chunk-size selection to the measured
+    per-chunk-step times."""
+    from chunked_prefill_attention_rope_amd import cp, path
+    torch.cuda.set_device(0)
+    P = CHUNK_SWEEP_PROMPT
+    rows = []
+    for name, sh in CHUNK_SWEEP_SHAPES.items():
+        cfg = I.LayerCfg(f"{name}-prompt", I.BF16, sh["B"], sh["H"], sh["nKV"], sh["D"], P,
+                         P + 1, base=sh["base"], seen=[0] * sh["B"], n_valid=[P] * sh["B"],
+                         seed=4242)
+        t = I.make_layer(cfg, nan_dead=False)
+        d = {k: v.to("cuda") for k, v in t.items()}
+        seen_all = d["seen"].repeat(reps, 1).contiguous()
+        caches = [cp.KVCache(d["kc"], d["vc"], seen_all[r]) for r in range(reps)]
+        table = {}
+        for C in CHUNK_SWEEP_SIZES:
+            pc = path.prompt_chunks(caches[0], d["q"], d["k"], d["v"], d["cos"], d["sin"], C)
+            seen_all.zero_()
+            ms, _ = time_graph(lambda: [path.prefill(caches[r], pc) for r in range(reps)], reps)
+            seen_all.zero_()
+            us = ms * 1e3 / reps
+            n = len(pc.q)
+            table[C] = us / n
+            row = {"shape": name, "prompt": P, "C": C, "chunks": n, "prefill_us": round(us, 1),
+                   "us_per_chunk": round(us / n, 2), "tok_per_s": round(P / us * 1e6, 1)}
+            rows.append(row)
+            print(json.dumps(row), file=sys.stderr, flush=True)
+            del pc
+        best = path.choose_chunk(P, table)
+        rows.append({"shape": name, "prompt": P, "chosen_C": best})
+        del caches, d
+        torch.cuda.empty_cache()
+    print("| shape | C | chunks | prompt us | us per chunk | tok/s |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for r in rows:
+        if "C" in r:
+            print(f"| {r['shape']} | {r['C']} | {r['chunks']} | {r['prefill_us']} | "
+                  f"{r['us_per_chunk']} | {r['tok_per_s']} |")
+    for r in rows:
+        if "chosen_C" in r:
+            print(f"chunk-size selection for a {r['prompt']}-token prompt on {r['shape']}: "
+                  f"C = {r['chosen_C']}")
+    if out_path:
+        with open(out_path, "w") as f:
+            for r in rows:
+                f.write(json.dumps(r) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -326,6 +386,8 @@ def main():
     ap.add_argument("--sweep-out", default=None, help="JSON lines of the sweep")
     ap.add_argument("--tail-sweep", action="store_true",
                     help="instead: padded-chunk vs token-by-token prompt tails (c3's shape)")
+    ap.add_argument("--chunk-sweep", action="store_true",
+                    help="instead: a whole prompt in chunks of 16..512 and the chunk selection")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU: this path has no multi-GPU mode (see DESIGN.md for "
@@ -336,6 +398,9 @@ def main():
         return
     if args.tail_sweep:
         tail_sweep(args.sweep_out)
+        return
+    if args.chunk_sweep:
+        chunk_sweep(args.sweep_out)
         return
 
     from chunked_prefill_attention_rope_amd import cp, path

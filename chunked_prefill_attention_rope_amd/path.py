@@ -144,3 +144,70 @@ def prefill_tail(cache: cp.KVCache, q, k, v, cos, sin, n_valid, n_tail: int,
         return "padded", out, sel
     outs, sel = scalar_tail(cache, steps, window=window)
     return "scalar", outs, sel
+
+
+# ------------------------------------------------------------ whole prompts
+
+@dataclass
+class PromptChunks:
+    """A prompt cut into chunks of C rows (the last one padded), with each chunk's
+    inputs contiguous and its step buffers: what a chunked-prefill loop feeds its chunk
+    graph ([SKaiNET] "Change (additive)": one fixed-C graph called per chunk)."""
+    C: int
+    n_valid: List[torch.Tensor]
+    q: List[torch.Tensor]
+    k: List[torch.Tensor]
+    v: List[torch.Tensor]
+    cos: List[torch.Tensor]
+    sin: List[torch.Tensor]
+    bufs: List[StepBuffers]
+
+
+def prompt_chunks(cache: cp.KVCache, q, k, v, cos, sin, C: int, window: int = 0,
+                  static_append: bool = False) -> PromptChunks:
+    """Cut prompt tensors q [B, H, P, D], k, v [B, nKV, P, D], cos/sin [Bt, P, D] (row p at
+    position seen + p) into ceil(P / C) chunks of C rows; the last chunk's missing rows
+    are zero padding."""
+    B, H, P, D = q.shape
+    n = (P + C - 1) // C
+
+    def piece(t, c):
+        lo, hi = c * C, min(P, (c + 1) * C)
+        out = torch.zeros(t.shape[:-2] + (C, t.shape[-1]), dtype=t.dtype, device=t.device)
+        out[..., :hi - lo, :] = t[..., lo:hi, :]
+        return out
+
+    pc = PromptChunks(C, [], [], [], [], [], [], [])
+    for c in range(n):
+        pc.q.append(piece(q, c))
+        pc.k.append(piece(k, c))
+        pc.v.append(piece(v, c))
+        pc.cos.append(piece(cos, c))
+        pc.sin.append(piece(sin, c))
+        pc.n_valid.append(torch.full((B,), min(C, P - c * C), dtype=torch.int32,
+                                     device=q.device))
+    base = make_buffers(cache, pc.q[0], pc.k[0], pc.v[0], window=window,
+                        static_append=static_append)
+    pc.bufs = [dataclasses.replace(base, out=torch.empty_like(pc.q[0]),
+                                   sel=torch.empty_like(base.sel)) for _ in range(n)]
+    return pc
+
+
+def prefill(cache: cp.KVCache, pc: PromptChunks, window: int = 0,
+            static_append: bool = False):
+    """Run a whole prompt chunk after chunk (the cache grows as it goes); returns the last
+    chunk's selection (the prompt's last real row)."""
+    for c in range(len(pc.q)):
+        chunk_step(cache, pc.q[c], pc.k[c], pc.v[c], pc.cos[c], pc.sin[c], pc.n_valid[c],
+                   pc.bufs[c], window=window, static_append=static_append)
+    return pc.bufs[-1].sel
+
+
+def choose_chunk(prompt_len: int, step_us: dict) -> int:
+    """Chunk-size selection: the C of a measured table {C: microseconds per chunk step}
+    that minimises ceil(prompt_len / C) * step_us[C] (a padded last chunk costs a whole
+    step; `bench.py --chunk-sweep` measures the table on this GPU).  Ties go to the
+    smaller C (less padding)."""
+    if prompt_len <= 0 or not step_us:
+        raise ValueError("need a positive prompt length and a non-empty table")
+    return min(sorted(step_us), key=lambda c: ((prompt_len + c - 1) // c) * step_us[c])

@@ -24,3 +24,15 @@ def test_threshold_is_a_parameter(path):
 def test_kill_switch(path, monkeypatch, val, forced):
     monkeypatch.setenv("CP_DISABLE_PREFILL_TAIL_PAD", val)
     assert path.pad_tail(100) is (not forced)
+
+
+def test_choose_chunk_minimises_total_time(path):
+    table = {32: 20.0, 64: 24.0, 128: 30.0, 256: 55.0}
+    # 1023 tokens: 32 chunks x 20 = 640, 16 x 24 = 384, 8 x 30 = 240, 4 x 55 = 220
+    assert path.choose_chunk(1023, table) == 256
+    # 100 tokens: 4 x 20 = 80, 2 x 24 = 48, 1 x 30 = 30, 1 x 55 = 55
+    assert path.choose_chunk(100, table) == 128
+    # ties go to the smaller chunk
+    assert path.choose_chunk(64, {32: 10.0, 64: 20.0}) == 32
+    with pytest.raises(ValueError):
+        path.choose_chunk(0, table)

@@ -22,6 +22,11 @@
  * round-to-nearest-even.  Cache updates are byte copies.
  *
  * Storage dtype codes: 0 = fp32, 1 = bf16 (raw 16-bit patterns).
+ *
+ * A second operator, the gated delta rule of linear-attention layers, follows
+ *   [Kazeia]   "Chantier 4 -- GDN chunkwise prefill" (Kazeia-engine docs),
+ *               sections "Le kernel actuel" and "P1 -- chunk f32": its
+ *               per-token recurrence, evaluated here in fp64 token by token.
  */
 #include <math.h>
 #include <stdint.h>
@@ -522,4 +527,57 @@ int orc_num_threads(void) {
 #else
   return 1;
 #endif
+}
+
+/* ------------------------------------------------------ gated delta rule */
+
+/*
+ * [Kazeia] "Le kernel actuel" / "P1 -- chunk f32": per (sequence, head) a state S of
+ * dk x dv; for every token t, in order:
+ *   S <- g_t S                      (gate decay, g_t = exp(alpha_t))
+ *   sum = S^T k_t                   (the state's prediction of v_t)
+ *   delta = (v_t - sum) * beta_t
+ *   S <- S + k_t delta^T            (rank-1 update)
+ *   out_t = S^T q_t
+ * q, k [B,H,P,dk], v [B,H,P,dv], beta and alpha [B,H,P] (fp32 inputs); s0 [B,H,dk,dv]
+ * fp32 initial state (NULL: zero); out [B,H,P,dv] and s_out [B,H,dk,dv] fp64.  The
+ * arithmetic is fp64 throughout, serial over the tokens, parallel over (b, h).
+ */
+int orc_gdn(const float *q, const float *k, const float *v, const float *beta,
+            const float *alpha, const float *s0, double *out, double *s_out, int B, int H,
+            int P, int dk, int dv) {
+  if (B < 0 || H < 0 || P < 0 || dk < 1 || dv < 1) return ORC_EARG;
+  if ((long)B * H * P > 0 && (!q || !k || !v || !beta || !alpha || !out)) return ORC_EARG;
+  if (!s_out) return ORC_EARG;
+  const long nbh = (long)B * H;
+#pragma omp parallel for schedule(dynamic)
+  for (long bh = 0; bh < nbh; ++bh) {
+    double *S = s_out + bh * dk * dv;
+    for (long e = 0; e < (long)dk * dv; ++e) S[e] = s0 ? (double)s0[bh * dk * dv + e] : 0.0;
+    double *sum = (double *)malloc(sizeof(double) * dv);
+    for (int t = 0; t < P; ++t) {
+      const long row = bh * P + t;
+      const float *kt = k + row * dk, *qt = q + row * dk, *vt = v + row * dv;
+      const double g = exp((double)alpha[row]);
+      const double bt = (double)beta[row];
+      for (long e = 0; e < (long)dk * dv; ++e) S[e] *= g;
+      for (int j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < dk; ++i) acc += S[(long)i * dv + j] * (double)kt[i];
+        sum[j] = acc;
+      }
+      for (int j = 0; j < dv; ++j) {
+        const double delta = ((double)vt[j] - sum[j]) * bt;
+        for (int i = 0; i < dk; ++i) S[(long)i * dv + j] += (double)kt[i] * delta;
+      }
+      double *ot = out + row * dv;
+      for (int j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < dk; ++i) acc += S[(long)i * dv + j] * (double)qt[i];
+        ot[j] = acc;
+      }
+    }
+    free(sum);
+  }
+  return ORC_OK;
 }

@@ -39,9 +39,10 @@ def lib():
                                ctypes.c_long, ip, ip, ip, ip, ip, ip, ip, ip, ip, ctypes.c_float,
                                ip, vp, vp]
         L.orc_select_row.argtypes = [vp, vp, i32p, ip, ip, ip, ip, ip]
+        L.orc_gdn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ip, ip, ip, ip, ip]
         for f in ("orc_rope", "orc_slot", "orc_live_positions", "orc_kv_append",
                   "orc_padded_overevicted", "orc_build_mask", "orc_attn", "orc_select_row",
-                  "orc_num_threads"):
+                  "orc_num_threads", "orc_gdn"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -171,6 +172,23 @@ def select_row(x, idx, off=-1):
     y = np.empty((B, H, D), dtype=np.float64)
     _check(lib().orc_select_row(_ptr(x), _ptr(y), _ptr(idx), int(off), B, H, C, D), "select_row")
     return y
+
+
+def gdn(q, k, v, beta, alpha, s0=None):
+    """Gated delta rule, token by token in fp64 ([Kazeia] "Le kernel actuel").
+    q, k [B,H,P,dk], v [B,H,P,dv], beta, alpha [B,H,P] (alpha = log of the gate),
+    s0 [B,H,dk,dv] or None (zero state).  Returns (out [B,H,P,dv], state [B,H,dk,dv]),
+    both fp64."""
+    q, k, v = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32)
+    beta, alpha = _c(beta, np.float32), _c(alpha, np.float32)
+    s0 = _c(s0, np.float32)
+    B, H, P, dk = q.shape
+    dv = v.shape[3]
+    out = np.zeros((B, H, P, dv), dtype=np.float64)
+    st = np.zeros((B, H, dk, dv), dtype=np.float64)
+    _check(lib().orc_gdn(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(s0),
+                         _ptr(out), _ptr(st), B, H, P, dk, dv), "gdn")
+    return out, st
 
 
 def num_threads():

@@ -369,6 +369,84 @@ def chunk_sweep(out_path, reps=5):
                 f.write(json.dumps(r) + "\n")
 
 
+def gdn_flops(B, H, P, dk, dv):
+    """Algorithmic flops of a gated-delta-rule prefill: per token and head, the three
+    dk x dv matrix-vector products of the recurrence (S^T k, the rank-1 update k delta^T,
+    the read-out S^T q) at 2 flops per multiply-add -- the 3 S^2 multiply-adds per token
+    that [Kazeia] "Le kernel actuel" counts.  The gate's scaling and the chunkwise form's
+    extra intra-chunk products are not counted."""
+    return 6 * B * H * P * dk * dv
+
+
+def gdn_bytes(B, H, P, dk, dv):
+    """Algorithmic HBM bytes: q, k, v, beta, alpha read, out written, state read and
+    written once (fp32)."""
+    return 4 * (B * H * P * (2 * dk + 2 * dv + 2) + 2 * B * H * dk * dv)
+
+
+def gdn_bench(name, reps, cpu_seconds, with_cpu):
+    """The gated-delta-rule chunkwise prefill (cp_gdn_chunk_prefill) on one workload:
+    prompt tokens per second per layer, the call's roofline, the oracle's rate."""
+    from chunked_prefill_attention_rope_amd import cp
+    torch.cuda.set_device(0)
+    cfg = I.gdn_config(name)
+    t = I.make_gdn(cfg)
+    d = {k: v.cuda() for k, v in t.items()}
+    B, H, P, dk, dv = cfg.B, cfg.H, cfg.P, cfg.dk, cfg.dv
+    st = d["state"].clone()
+    out = torch.empty_like(d["v"])
+    ws = torch.empty(cp.gdn_workspace_bytes(B, H, P, dk, dv), dtype=torch.uint8, device="cuda")
+
+    def call():
+        cp.gdn_chunk_prefill(d["q"], d["k"], d["v"], d["beta"], d["alpha"], st, out, ws)
+
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / reps
+    ms, _ = time_graph(lambda: [call() for _ in range(reps)], reps)
+    ms /= reps
+    flops, nbytes = gdn_flops(B, H, P, dk, dv), gdn_bytes(B, H, P, dk, dv)
+    achieved = flops / (ms * 1e-3) / 1e12
+    result = {
+        "metric": "gated-delta-rule prefill tok/s per layer", "value": round(B * P / (ms * 1e-3), 1),
+        "unit": "tok/s", "n_gpus": 1, "steps": reps, "warmup": 5,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{name}: B={B} H={H} P={P} dk={dk} dv={dv}, chunk 64",
+                   "launch": "hip-graph", "eager_ms_per_call": round(eager_ms, 6)},
+        "roofline": {"bound": "alu", "achieved": round(achieved, 4), "peak": FP32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK_TFLOPS, 5),
+                     "traffic": None, "kernel": "cp_gdn_chunk_prefill (prep + scan)",
+                     "avg_launch_us": round(ms * 1e3, 3), "algorithmic_flops": flops,
+                     "algorithmic_bytes": nbytes,
+                     "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5)},
+    }
+    if with_cpu:
+        from oracle import oracle as O
+        args = [t[n].numpy() for n in ("q", "k", "v", "beta", "alpha", "state")]
+        total, reps_c = 0.0, 0
+        while total < cpu_seconds and reps_c < 1000:
+            t0 = time.perf_counter()
+            O.gdn(*args)
+            total += time.perf_counter() - t0
+            reps_c += 1
+        result["cpu_baseline"] = {
+            "value": round(B * P * reps_c / total, 1), "unit": "tok/s",
+            "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"whole workload, token-by-token fp64 recurrence, {reps_c} reps, "
+                      f"{total:.1f} s; {os.cpu_count()} host CPUs visible"}
+    print(f"[bench] {name}: gdn {ms * 1e3:.2f} us/call graph, {eager_ms * 1e3:.2f} eager",
+          file=sys.stderr, flush=True)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -388,11 +466,16 @@ def main():
                     help="instead: padded-chunk vs token-by-token prompt tails (c3's shape)")
     ap.add_argument("--chunk-sweep", action="store_true",
                     help="instead: a whole prompt in chunks of 16..512 and the chunk selection")
+    ap.add_argument("--gdn", default=None, choices=["g0", "g1"],
+                    help="instead: the gated-delta-rule chunkwise prefill on this workload")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU: this path has no multi-GPU mode (see DESIGN.md for "
               "how it would shard); use --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.gdn:
+        gdn_bench(args.gdn, args.attn_reps, args.cpu_seconds, not args.no_cpu_baseline)
+        return
     if args.sweep:
         sweep(args.sweep_out)
         return

@@ -72,6 +72,9 @@ _SIGS = {
     "cp_attn_chunk_with_past": (_i, [_P(CacheDesc), _P(AttnArgs), _vp]),
     "cp_build_mask": (_i, [_vp, ctypes.c_int64, _P(CacheDesc), _vp, _i, _i, _i, _vp]),
     "cp_select_row": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
+    "cp_gdn_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i, _i]),
+    "cp_gdn_chunk_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp,
+                                  ctypes.c_size_t, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -325,6 +328,40 @@ def select_row(x: torch.Tensor, idx: torch.Tensor, offset: int = -1,
     _check(_lib.cp_select_row(_dev(x, "x"), _dev(out, "out"), _opt(idx, "idx", torch.int32),
                               int(offset), B, H, C, D, _dtype_code(x), _stream()),
            "cp_select_row")
+    return out
+
+
+# ------------------------------------------------------- gated delta rule
+
+def gdn_workspace_bytes(B: int, H: int, P: int, dk: int, dv: int) -> int:
+    return int(_lib.cp_gdn_workspace_bytes(int(B), int(H), int(P), int(dk), int(dv)))
+
+
+def gdn_chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+                      alpha: torch.Tensor, state: torch.Tensor,
+                      out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """cp_gdn_chunk_prefill: fp32 q, k [B,H,P,dk], v [B,H,P,dv], beta, alpha [B,H,P];
+    state [B,H,dk,dv] is updated in place to the state after the last token."""
+    B, H, P, dk = q.shape
+    dv = v.shape[3]
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("alpha", alpha),
+                    ("state", state)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or beta.shape != q.shape[:3] \
+            or alpha.shape != q.shape[:3] or state.shape != (B, H, dk, dv):
+        raise ValueError("inconsistent gated-delta-rule shapes")
+    if out is None:
+        out = torch.empty_like(v)
+    if workspace is None:
+        workspace = torch.empty(max(gdn_workspace_bytes(B, H, P, dk, dv), 1), dtype=torch.uint8,
+                                device=q.device)
+    _check(_lib.cp_gdn_chunk_prefill(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(beta, "beta"),
+                                     _dev(alpha, "alpha"), _dev(state, "state"), _dev(out, "out"),
+                                     B, H, P, dk, dv, _dev(workspace, "workspace"),
+                                     workspace.numel() * workspace.element_size(), _stream()),
+           "cp_gdn_chunk_prefill")
     return out
 
 

@@ -323,4 +323,22 @@ int cp_select_row(const void *x, void *y, const int32_t *idx, int offset, int B,
       launch_select(x, y, idx, offset, B, H, C, D, dtype, static_cast<hipStream_t>(stream)));
 }
 
+size_t cp_gdn_workspace_bytes(int B, int H, int P, int dk, int dv) {
+  if (B < 0 || H < 0 || P < 0 || !gdn_dims_supported(dk, dv)) return 0;
+  return gdn_workspace_bytes(B, H, P, dk, dv);
+}
+
+int cp_gdn_chunk_prefill(const float *q, const float *k, const float *v, const float *beta,
+                         const float *alpha, float *state, float *out, int B, int H, int P,
+                         int dk, int dv, void *workspace, size_t workspace_bytes,
+                         cp_stream_t stream) {
+  if (B < 0 || H < 0 || P < 0) return CP_ERR_ARG;
+  if (!gdn_dims_supported(dk, dv) || B > 65535 || H > 65535) return CP_ERR_SHAPE;  // grid y, z
+  if (static_cast<size_t>(B) * H * P == 0) return CP_OK;  // empty: pointers may be NULL
+  if (!q || !k || !v || !beta || !alpha || !state || !out || !workspace) return CP_ERR_ARG;
+  if (workspace_bytes < gdn_workspace_bytes(B, H, P, dk, dv)) return CP_ERR_WORKSPACE;
+  return to_status(launch_gdn(q, k, v, beta, alpha, state, out, B, H, P, dk, dv, workspace,
+                              static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

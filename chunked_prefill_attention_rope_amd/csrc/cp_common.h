@@ -83,6 +83,11 @@ __device__ __forceinline__ int read_nvalid(const int32_t *n_valid, int b, int C,
 
 // --------------------------------------------------------- host launchers
 
+size_t gdn_workspace_bytes(int B, int H, int P, int dk, int dv);
+bool gdn_dims_supported(int dk, int dv);
+hipError_t launch_gdn(const float *q, const float *k, const float *v, const float *beta,
+                      const float *alpha, float *state, float *out, int B, int H, int P, int dk,
+                      int dv, void *ws, hipStream_t s);
 hipError_t launch_rope(const void *x, void *y, const float *cos, const float *sin, int B, int Hx,
                        int C, int D, int Bt, int dtype, hipStream_t s);
 // Two tensors (Q and K of a chunk) rotated by one launch from the same tables.

@@ -101,6 +101,46 @@ def config(name: str, layer: int = 0) -> LayerCfg:
     raise ValueError(f"unknown workload {name}")
 
 
+@dataclass
+class GdnCfg:
+    """A gated-delta-rule prefill workload ([Kazeia] "Chantier 4": head size 64 over 256
+    tokens is the page's kernel test; 128-wide states over a 512-token prompt its pp512
+    benchmark)."""
+    name: str
+    B: int
+    H: int
+    P: int
+    dk: int
+    dv: int
+    seed: int
+
+
+def gdn_config(name: str) -> GdnCfg:
+    if name == "g0":
+        return GdnCfg("g0", 1, 4, 256, 64, 64, 2001)
+    if name == "g1":
+        return GdnCfg("g1", 1, 16, 512, 128, 128, 2002)
+    raise ValueError(f"unknown gated-delta-rule workload {name}")
+
+
+def make_gdn(cfg: GdnCfg, P: Optional[int] = None):
+    """Draws for a gated-delta-rule prefill (fp32, CPU): q and k N(0,1) with unit-norm keys
+    (k / |k|, as the layer normalises them), v N(0,1), beta = sigmoid(N(0,1)), log-gates
+    alpha = -softplus(N(0,1) - 2) (gates between about 0.3 and 1), entry state
+    N(0,1) * 0.1.  Order of draws from Generator(seed): q, k, v, beta, alpha, state."""
+    g = torch.Generator("cpu").manual_seed(cfg.seed)
+    P = cfg.P if P is None else P
+    B, H, dk, dv = cfg.B, cfg.H, cfg.dk, cfg.dv
+    q = torch.randn((B, H, P, dk), generator=g)
+    k = torch.randn((B, H, P, dk), generator=g)
+    k = k / k.norm(dim=-1, keepdim=True)
+    v = torch.randn((B, H, P, dv), generator=g)
+    beta = torch.sigmoid(torch.randn((B, H, P), generator=g))
+    alpha = -torch.nn.functional.softplus(torch.randn((B, H, P), generator=g) - 2)
+    state = torch.randn((B, H, dk, dv), generator=g) * 0.1
+    return dict(q=q, k=k, v=v, beta=beta, alpha=alpha, state=state)
+
+
 def derived(name: str, B: Optional[int] = None, C: Optional[int] = None,
             explicit_mask: Optional[bool] = None) -> LayerCfg:
     """A workload's per-sequence shape at another batch or chunk size (the bandwidth

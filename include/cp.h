@@ -25,6 +25,9 @@
  *             runtime": the KV cache is owned by the runtime, outside the
  *             graph; past tokens packed in the first past_len slots; the
  *             runtime writes the delta K/V into the external cache.
+ *   [Kazeia]  Kazeia-engine docs, "Chantier 4 -- GDN chunkwise prefill":
+ *             the gated delta rule of linear-attention layers and its chunkwise
+ *             form (cp_gdn_chunk_prefill).
  *   [cactus]  cactus PR #716, "Pad the chunked-prefill tail for sliding-window
  *             models", section "Fix" and the review hardening: sliding caches
  *             evict chronologically; a padded append over-evicts up to
@@ -312,6 +315,34 @@ int cp_build_mask(float *mask, int64_t ld, const cp_cache *cache, const int32_t 
  */
 int cp_select_row(const void *x, void *y, const int32_t *idx, int offset, int B, int H, int C,
                   int D, int dtype, cp_stream_t stream);
+
+/* ---- gated delta rule (the linear-attention layers of hybrid models) ---- */
+
+/*
+ * Prefill of P tokens through the gated delta rule ([Kazeia] "Chantier 4 -- GDN
+ * chunkwise prefill", sections "Le kernel actuel" and "P1 -- chunk f32"): per
+ * (sequence, head) a state S of dk x dv; per token, in order,
+ *   S <- exp(alpha_t) S;  delta = (v_t - S^T k_t) beta_t;  S <- S + k_t delta^T;
+ *   out_t = S^T q_t
+ * computed in chunks of 64 tokens ("Chunkwise (delta rule)"), fp32.
+ *
+ *   q, k       fp32 [B, H, P, dk] (as the layer produces them; commonly unit keys)
+ *   v          fp32 [B, H, P, dv]
+ *   beta       fp32 [B, H, P]   write strengths
+ *   alpha      fp32 [B, H, P]   log of the gates (<= 0 for decaying gates)
+ *   state      fp32 [B, H, dk, dv], in/out: the entry state, replaced by the state
+ *              after the last token (the layer's "cache")
+ *   out        fp32 [B, H, P, dv]
+ *   workspace  device scratch of at least cp_gdn_workspace_bytes()
+ * dk and dv each 64 or 128.
+ * Errors: CP_ERR_ARG (null, negative sizes), CP_ERR_SHAPE (dk, dv; B or H above 65535),
+ *         CP_ERR_WORKSPACE, CP_ERR_HIP.  P = 0 is a no-op (state untouched).
+ */
+size_t cp_gdn_workspace_bytes(int B, int H, int P, int dk, int dv);
+int cp_gdn_chunk_prefill(const float *q, const float *k, const float *v, const float *beta,
+                         const float *alpha, float *state, float *out, int B, int H, int P,
+                         int dk, int dv, void *workspace, size_t workspace_bytes,
+                         cp_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -169,3 +169,22 @@ def test_select_and_mask_validation(cp):
     c = _cache(cp)
     assert lib.cp_build_mask(None, 8, ctypes.byref(c), None, 4, 2, 0, None) == cp.ERR_ARG
     assert lib.cp_build_mask(FAKE, 8, ctypes.byref(c), None, 0, 2, 0, None) == cp.ERR_ARG
+
+
+def test_gdn_validation(cp):
+    lib = cp.raw()
+    f = lib.cp_gdn_chunk_prefill
+    ws = cp.gdn_workspace_bytes(1, 2, 100, 64, 64)
+    assert ws == 1 * 2 * 2 * (64 * 64 + 64 * 64 + 64 * 64 + 64) * 4
+    assert cp.gdn_workspace_bytes(1, 2, 100, 96, 64) == 0
+    call = lambda **kw: f(*[kw.get(n, FAKE) for n in ("q", "k", "v", "beta", "alpha", "state", "out")],
+                          kw.get("B", 1), kw.get("H", 2), kw.get("P", 100), kw.get("dk", 64),
+                          kw.get("dv", 64), kw.get("ws", FAKE), kw.get("wsb", ws), None)
+    assert call(dk=96) == cp.ERR_SHAPE
+    assert call(dv=256) == cp.ERR_SHAPE
+    assert call(H=70000) == cp.ERR_SHAPE
+    assert call(P=-1) == cp.ERR_ARG
+    assert call(q=None) == cp.ERR_ARG
+    assert call(ws=None) == cp.ERR_ARG
+    assert call(wsb=ws - 1) == cp.ERR_WORKSPACE
+    assert call(P=0, q=None, ws=None) == cp.OK  # empty prompt: nothing is read

@@ -333,9 +333,12 @@ int cp_gdn_chunk_prefill(const float *q, const float *k, const float *v, const f
                          int dk, int dv, void *workspace, size_t workspace_bytes,
                          cp_stream_t stream) {
   if (B < 0 || H < 0 || P < 0) return CP_ERR_ARG;
-  if (!gdn_dims_supported(dk, dv) || B > 65535 || H > 65535) return CP_ERR_SHAPE;  // grid y, z
+  if (!gdn_dims_supported(dk, dv) || !gdn_grid_fits(B, H, P)) return CP_ERR_SHAPE;
   if (static_cast<size_t>(B) * H * P == 0) return CP_OK;  // empty: pointers may be NULL
   if (!q || !k || !v || !beta || !alpha || !state || !out || !workspace) return CP_ERR_ARG;
+  const uintptr_t vec = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                        reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(workspace);
+  if (vec & 15) return CP_ERR_ARG;  // read and written as 16-byte vectors
   if (workspace_bytes < gdn_workspace_bytes(B, H, P, dk, dv)) return CP_ERR_WORKSPACE;
   return to_status(launch_gdn(q, k, v, beta, alpha, state, out, B, H, P, dk, dv, workspace,
                               static_cast<hipStream_t>(stream)));

@@ -85,6 +85,7 @@ __device__ __forceinline__ int read_nvalid(const int32_t *n_valid, int b, int C,
 
 size_t gdn_workspace_bytes(int B, int H, int P, int dk, int dv);
 bool gdn_dims_supported(int dk, int dv);
+bool gdn_grid_fits(int B, int H, int P);
 hipError_t launch_gdn(const float *q, const float *k, const float *v, const float *beta,
                       const float *alpha, float *state, float *out, int B, int H, int P, int dk,
                       int dv, void *ws, hipStream_t s);

@@ -1,5 +1,5 @@
 // gdn.hip -- gated delta rule prefill in chunks (the linear-attention layer of a
-// hybrid model), fp32.
+// hybrid model), fp32 on the matrix cores.
 //
 // [Kazeia] "Chantier 4 -- GDN chunkwise prefill", sections "Le kernel actuel" and
 // "P1 -- chunk f32": per (sequence, head) a state S of dk x dv; per token the state
@@ -12,202 +12,477 @@
 //   U = T diag(beta) V       W = T diag(beta e^lg) K       D = U - W S0
 //   O = diag(e^lg) Q S0 + (tril(R) * Q K^T) D
 //   S = e^{lg_last} S0 + K^T diag(R[last, :]) D
-// (A, U and W never see the state: they are computed for every chunk at once.)
+// A, T, U and W never see the state, and O of a chunk needs only the chunk's entry
+// state and D: only D and the state update form the serial chain across chunks.
 //
-// Two kernels:
-//  - k_gdn_prep: one workgroup per (sequence, head, chunk).  K and Q of the chunk
-//    in LDS; the gated, masked products A and P = tril(R) * Q K^T; U and W by forward
-//    substitution, one thread per column (rows of a column depend only on earlier
-//    rows of the same column, so the columns need no barriers).  Writes W, U, P and lg
-//    to the workspace.
-//  - k_gdn_scan: one workgroup per (sequence, head, 16 columns of the state): the
-//    columns of S evolve independently, so the state's dv columns are split over
-//    workgroups.  Walks the chunks in order: D, O and the next state, all from LDS.
+// Three kernels, all on v_mfma_f32_16x16x4f32 (fp32 products, fp32 sums):
+//  - k_gdn_prep, one workgroup per (chunk, head, sequence): the Gram products K K^T
+//    and Q K^T of the chunk; T by inverting the four 16x16 diagonal blocks of I + A
+//    (one lane per column) and filling the blocks below them in three rounds
+//    (T_ij = -T_ii sum_k A_ik T_kj); then [U | W] = T [diag(beta) V | diag(beta e^lg) K].
+//    Writes W, U, P = tril(R) * Q K^T, lg and K^T of the chunk to the workspace.
+//  - k_gdn_scan, one workgroup per (16 state columns, head, sequence): the state's
+//    columns evolve independently.  Walks the chunks: each wave computes 16 rows of
+//    D = U - W S, then updates its own row blocks of S (kept in MFMA accumulators,
+//    mirrored to LDS transposed for the next chunk's D).  Stores each chunk's entry
+//    state and D for the output kernel.
+//  - k_gdn_out, one workgroup per (32 output columns of a chunk, head, sequence):
+//    O = diag(e^lg) Q S_c + P D_c.
 // Pad rows of a last partial chunk are zero with beta = 0 and a zero log-gate: their
-// rows of U, W and D are zero and they leave the state untouched.
+// rows of A, U, W and D are zero, they leave the state untouched and are not stored.
+//
+// MFMA 16x16x4 fp32 operand layout (lane l, m = l % 16, g = l / 16): A supplies
+// A[m][g], B supplies B[g][m], and accumulator register r holds C[4g + r][m].  A
+// product's register r is therefore a valid B operand for the k-step whose four
+// contraction indices are {4g + r}, which chains products without a trip through LDS.
+#include <algorithm>
+
 #include "cp_common.h"
 
 namespace cp {
 namespace {
 
-constexpr int CH = 64;   // tokens per chunk
-constexpr int VB = 16;   // state columns per scan workgroup
+constexpr int CH = 64;      // tokens per chunk
+constexpr int VB = 16;      // state columns per scan workgroup
+constexpr int AP = CH + 4;  // LDS row stride of the 64 x 64 tiles
+constexpr int OC = 32;      // output columns per output workgroup
 
-__host__ __device__ constexpr size_t gdn_chunk_floats(int dk, int dv) {
-  return static_cast<size_t>(CH) * dk + static_cast<size_t>(CH) * dv + CH * CH + CH;
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f4 mma(float a, float b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Workgroup L runs on XCD L % 8.  All workgroups of one (sequence, head) -- which read
+// the same chunk products -- go to one XCD, so those reads share its L2: (sequence,
+// head) G takes XCD G % 8, and its `per` workgroups the successive slots there.  The
+// grid has 8 * ceil(BH / 8) * per workgroups; the surplus ones (G >= BH) exit at once.
+__device__ __forceinline__ bool head_slot(int per, int BH, int &G, int &k) {
+  const int L = blockIdx.x, x = L % 8, slot = L / 8;
+  G = x + 8 * (slot / per);
+  k = slot % per;
+  return G < BH;
+}
+
+__device__ __forceinline__ f4 ld4(const float *p) { return *reinterpret_cast<const f4 *>(p); }
+__device__ __forceinline__ void st4(float *p, f4 v) { *reinterpret_cast<f4 *>(p) = v; }
+
+// Workspace of one (sequence, head, chunk), in floats.
 template <int DK, int DV>
-__global__ void __launch_bounds__(256) k_gdn_prep(const float *__restrict__ q,
+struct Chunk {
+  static constexpr size_t W = 0;               // [CH][DK]  T diag(beta e^lg) K
+  static constexpr size_t U = W + CH * DK;     // [CH][DV]  T diag(beta) V
+  static constexpr size_t P = U + CH * DV;     // [CH][CH]  tril(R) * Q K^T (lower blocks)
+  static constexpr size_t LG = P + CH * CH;    // [CH]      cumulated log-gates
+  static constexpr size_t KT = LG + CH;        // [DK][CH]  K^T
+  static constexpr size_t SC = KT + DK * CH;   // [DK][DV]  entry state
+  static constexpr size_t DC = SC + DK * DV;   // [CH][DV]  D
+  static constexpr size_t SIZE = DC + CH * DV;
+};
+
+__host__ __device__ constexpr size_t gdn_chunk_floats(int dk, int dv) {
+  return 2 * static_cast<size_t>(CH) * dk + 2 * static_cast<size_t>(CH) * dv + CH * CH + CH +
+         static_cast<size_t>(dk) * dv;
+}
+static_assert(Chunk<128, 64>::SIZE == gdn_chunk_floats(128, 64), "workspace layout");
+
+constexpr int PREP_THREADS = 512;  // 8 waves: two per SIMD to overlap LDS and MFMA latency
+
+template <int DK, int DV>
+__global__ void __launch_bounds__(PREP_THREADS) k_gdn_prep(const float *__restrict__ q,
                                                   const float *__restrict__ k,
                                                   const float *__restrict__ v,
                                                   const float *__restrict__ beta,
                                                   const float *__restrict__ alpha,
-                                                  float *__restrict__ ws, int H, int P, int nch) {
-  constexpr int NX = DV + DK;  // columns of the substitution: U's, then W's
-  __shared__ float Ks[CH][DK + 1];
-  __shared__ float Qs[CH][DK + 1];
-  __shared__ float As[CH][CH + 1];
-  __shared__ float Xs[CH][NX];
-  __shared__ float lg[CH], bt[CH];
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x;
-  const size_t bh = static_cast<size_t>(b) * H + h;
+                                                  float *__restrict__ ws, int BH, int P, int nch) {
+  using L = Chunk<DK, DV>;
+  constexpr int KP = DK + 4, VP = DV + 4;
+  __shared__ __align__(16) float Ks[CH * KP];
+  __shared__ __align__(16) float Qs[CH * KP];
+  __shared__ __align__(16) float Vs[CH * VP];
+  __shared__ __align__(16) float As[CH * AP];
+  __shared__ __align__(16) float Ts[CH * AP];
+  __shared__ float lg[CH], bt[CH], fk[CH];  // lg, beta, beta e^lg
+  int G, c;
+  if (!head_slot(nch, BH, G, c)) return;  // whole workgroup, before any barrier
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, m = lane & 15, g = lane >> 4;
+  const size_t bh = G;
   const int t0 = c * CH;
   const int n = min(CH, P - t0);
-  for (int e = tid; e < CH * DK; e += 256) {
-    const int t = e / DK, i = e % DK;
-    const bool in = t < n;
-    Ks[t][i] = in ? k[(bh * P + t0 + t) * DK + i] : 0.f;
-    Qs[t][i] = in ? q[(bh * P + t0 + t) * DK + i] : 0.f;
-  }
-  if (tid < CH) {
-    const bool in = tid < n;
-    lg[tid] = in ? alpha[bh * P + t0 + tid] : 0.f;
-    bt[tid] = in ? beta[bh * P + t0 + tid] : 0.f;
-  }
-  __syncthreads();
-  if (tid == 0) {  // inclusive prefix sum of the log-gates (64 terms, fp32)
-    float acc = 0.f;
-    for (int t = 0; t < CH; ++t) {
-      acc += lg[t];
-      lg[t] = acc;
+  float *ck = ws + (bh * nch + c) * L::SIZE;
+
+  const f4 zero = {0.f, 0.f, 0.f, 0.f};
+  {  // the chunk's K, Q and V: every load in flight before the first LDS store
+    constexpr int NK = CH * DK / (4 * PREP_THREADS), NV = CH * DV / (4 * PREP_THREADS);
+    f4 kr[NK], qr[NK], vr[NV];
+#pragma unroll
+    for (int u = 0; u < NK; ++u) {
+      const int e = tid + PREP_THREADS * u, t = e / (DK / 4), i = (e % (DK / 4)) * 4;
+      const size_t src = (bh * P + t0 + t) * DK + i;
+      kr[u] = t < n ? ld4(k + src) : zero;
+      qr[u] = t < n ? ld4(q + src) : zero;
     }
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int e = tid + PREP_THREADS * u, t = e / (DV / 4), j = (e % (DV / 4)) * 4;
+      vr[u] = t < n ? ld4(v + (bh * P + t0 + t) * DV + j) : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < NK; ++u) {
+      const int e = tid + PREP_THREADS * u, t = e / (DK / 4), i = (e % (DK / 4)) * 4;
+      st4(&Ks[t * KP + i], kr[u]);
+      st4(&Qs[t * KP + i], qr[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int e = tid + PREP_THREADS * u, t = e / (DV / 4), j = (e % (DV / 4)) * 4;
+      st4(&Vs[t * VP + j], vr[u]);
+    }
+  }
+  if (w == 0) {  // inclusive prefix sum of the log-gates over the chunk
+    const bool in = lane < n;
+    float a = in ? alpha[bh * P + t0 + lane] : 0.f;
+    for (int off = 1; off < CH; off <<= 1) {
+      const float y = __shfl_up(a, off, 64);
+      if (lane >= off) a += y;
+    }
+    const float be = in ? beta[bh * P + t0 + lane] : 0.f;
+    lg[lane] = a;
+    bt[lane] = be;
+    fk[lane] = be * __expf(a);
+    ck[L::LG + lane] = a;
   }
   __syncthreads();
 
-  float *W = ws + (bh * nch + c) * gdn_chunk_floats(DK, DV);
-  float *U = W + CH * DK;
-  float *Pm = U + CH * DV;
-  float *LG = Pm + CH * CH;
-  // A (strictly lower) into LDS, P = tril(R) * Q K^T into the workspace
-  for (int e = tid; e < CH * CH; e += 256) {
-    const int t = e / CH, s = e % CH;
-    float a = 0.f, pv = 0.f;
-    if (s <= t) {
-      float kk = 0.f, qk = 0.f;
-#pragma unroll 8
-      for (int i = 0; i < DK; ++i) {
-        kk = fmaf(Ks[t][i], Ks[s][i], kk);
-        qk = fmaf(Qs[t][i], Ks[s][i], qk);
+  // Gram tiles on and below the diagonal: 10 tiles of K K^T (-> A) and 10 of Q K^T
+  // (-> P), dealt over the waves.  Contraction index of k-step (kk, j): g * DK/4 + 4 kk + j.
+  for (int p = w; p < 20; p += PREP_THREADS / 64) {
+    const int tl = p % 10;
+    const int tt = (tl >= 1) + (tl >= 3) + (tl >= 6);
+    const int st = tl - tt * (tt + 1) / 2;
+    const float *X = p >= 10 ? Qs : Ks;
+    f4 acc0 = zero, acc1 = zero;
+#pragma unroll
+    for (int kk = 0; kk < DK / 16; kk += 2) {
+      const int i0 = g * (DK / 4) + kk * 4;
+      const f4 a0 = ld4(&X[(tt * 16 + m) * KP + i0]);
+      const f4 b0 = ld4(&Ks[(st * 16 + m) * KP + i0]);
+      const f4 a1 = ld4(&X[(tt * 16 + m) * KP + i0 + 4]);
+      const f4 b1 = ld4(&Ks[(st * 16 + m) * KP + i0 + 4]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc0 = mma(a0[j], b0[j], acc0);
+        acc1 = mma(a1[j], b1[j], acc1);
       }
-      const float r = __expf(lg[t] - lg[s]);
-      pv = r * qk;
-      if (s < t) a = bt[t] * r * kk;
     }
-    As[t][s] = a;
-    Pm[e] = pv;
+    const int s = st * 16 + m;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = tt * 16 + 4 * g + r;
+      const float gram = acc0[r] + acc1[r];
+      const float rr = s <= t ? __expf(lg[t] - lg[s]) : 0.f;
+      if (p < 10)
+        As[t * AP + s] = s < t ? bt[t] * rr * gram : 0.f;
+      else
+        ck[L::P + t * CH + s] = rr * gram;
+    }
   }
-  if (tid < CH) LG[tid] = lg[tid];
+  for (int e = tid; e < DK * CH; e += PREP_THREADS) {  // K^T for the scan's state update
+    const int i = e / CH, t = e % CH;
+    ck[L::KT + e] = Ks[t * KP + i];
+  }
   __syncthreads();
 
-  // right-hand sides: beta V (U's columns), beta e^lg K (W's columns)
-  for (int e = tid; e < CH * NX; e += 256) {
-    const int t = e / NX, col = e % NX;
-    float rhs = 0.f;
-    if (col < DV) {
-      if (t < n) rhs = bt[t] * v[(bh * P + t0 + t) * DV + col];
-    } else {
-      rhs = bt[t] * __expf(lg[t]) * Ks[t][col - DV];
+  // T = (I + A)^-1.  Diagonal blocks: wave w < 4 inverts block w, lane m < 16 one
+  // column (unit lower triangular: forward substitution on e_m).
+  if (w < 4 && g == 0) {
+    const int o = w * 16;
+    float x[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      float acc = t == m ? 1.f : 0.f;
+#pragma unroll
+      for (int s = 0; s < t; ++s) acc = fmaf(-As[(o + t) * AP + o + s], x[s], acc);
+      x[t] = acc;
     }
-    Xs[t][col] = rhs;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) Ts[(o + t) * AP + o + m] = x[t];
   }
   __syncthreads();
-  // forward substitution (I + A) X = rhs in place, one column per thread: row t of a
-  // column needs only the earlier rows of the same column
-  for (int col = tid; col < NX; col += 256) {
-    for (int t = 1; t < CH; ++t) {
-      float acc = Xs[t][col];
-      for (int s = 0; s < t; ++s) acc = fmaf(-As[t][s], Xs[s][col], acc);
-      Xs[t][col] = acc;
+  // Blocks below the diagonal, by distance from it: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj.
+  auto below = [&](int i, int j) {
+    f4 acc = zero;
+    for (int kb = j; kb < i; ++kb) {
+      const f4 a = ld4(&As[(i * 16 + m) * AP + kb * 16 + 4 * g]);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        acc = mma(a[kk], Ts[(kb * 16 + 4 * g + kk) * AP + j * 16 + m], acc);
     }
-  }
+    const f4 a2 = ld4(&Ts[(i * 16 + m) * AP + i * 16 + 4 * g]);
+    f4 t = zero;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) t = mma(a2[kk], acc[kk], t);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Ts[(i * 16 + 4 * g + r) * AP + j * 16 + m] = -t[r];
+  };
+  if (w < 3) below(w + 1, w);
   __syncthreads();
-  for (int e = tid; e < CH * NX; e += 256) {
-    const int t = e / NX, col = e % NX;
-    if (col < DV)
-      U[t * DV + col] = Xs[t][col];
-    else
-      W[t * DK + col - DV] = Xs[t][col];
+  if (w < 2) below(w + 2, w);
+  __syncthreads();
+  if (w == 0) below(3, 0);
+  __syncthreads();
+
+  // [U | W] = T [diag(beta) V | diag(beta e^lg) K]: column tiles dealt over the waves.
+  constexpr int NCT = (DV + DK) / 16;
+  for (int ct = w; ct < NCT; ct += PREP_THREADS / 64) {
+    const bool isv = ct < DV / 16;
+    const float *Y = isv ? Vs + ct * 16 : Ks + (ct - DV / 16) * 16;
+    const int yp = isv ? VP : KP;
+    const float *f = isv ? bt : fk;
+    f4 acc[4] = {zero, zero, zero, zero};
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      float bv[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int s = sb * 16 + 4 * g + kk;
+        bv[kk] = f[s] * Y[s * yp + m];
+      }
+#pragma unroll
+      for (int tt = sb; tt < 4; ++tt) {
+        const f4 a = ld4(&Ts[(tt * 16 + m) * AP + sb * 16 + 4 * g]);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc[tt] = mma(a[kk], bv[kk], acc[tt]);
+      }
+    }
+    float *dst = isv ? ck + L::U + ct * 16 : ck + L::W + (ct - DV / 16) * 16;
+    const int ld = isv ? DV : DK;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(tt * 16 + 4 * g + r) * ld + m] = acc[tt][r];
   }
 }
 
 template <int DK, int DV>
-__global__ void __launch_bounds__(256) k_gdn_scan(const float *__restrict__ q,
-                                                  const float *__restrict__ k,
-                                                  const float *__restrict__ ws,
-                                                  float *__restrict__ state,
-                                                  float *__restrict__ out, int H, int P, int nch) {
-  __shared__ float Ws[CH][DK + 1];
-  __shared__ float Qs[CH][DK + 1];
-  __shared__ float Ks[CH][DK + 1];
-  __shared__ float Pm[CH][CH + 1];
-  __shared__ float Ss[DK][VB + 1];
-  __shared__ float Us[CH][VB + 1];
-  __shared__ float Dl[CH][VB + 1];
-  __shared__ float lg[CH], eg[CH], wl[CH];  // lg, e^lg, e^(lg_last - lg)
-  const int jb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x;
-  const size_t bh = static_cast<size_t>(b) * H + h;
+__global__ void __launch_bounds__(256) k_gdn_scan(float *__restrict__ ws,
+                                                  float *__restrict__ state, int BH, int nch) {
+  using L = Chunk<DK, DV>;
+  constexpr int NIB = DK / 16;  // row blocks of the state
+  constexpr int OWN = NIB / 4;  // row blocks each wave updates
+  constexpr int SP = DK + 4;
+  __shared__ __align__(16) float St[VB * SP];  // S^T of this column block: St[j][i]
+  __shared__ __align__(16) float Dt[VB * AP];  // (diag(R[last, :]) D)^T: Dt[j][t]
+  int G, jb;
+  if (!head_slot(DV / VB, BH, G, jb)) return;  // whole workgroup, before any barrier
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, m = lane & 15, g = lane >> 4;
+  const size_t bh = G;
   const int j0 = jb * VB;
   float *S = state + bh * DK * DV;
-  for (int e = tid; e < DK * VB; e += 256) Ss[e / VB][e % VB] = S[(e / VB) * DV + j0 + e % VB];
+  const f4 zero = {0.f, 0.f, 0.f, 0.f};
 
-  for (int c = 0; c < nch; ++c) {
-    const int t0 = c * CH;
-    const int n = min(CH, P - t0);
-    const float *W = ws + (bh * nch + c) * gdn_chunk_floats(DK, DV);
-    const float *U = W + CH * DK;
-    const float *Pg = U + CH * DV;
-    const float *LG = Pg + CH * CH;
-    __syncthreads();  // the previous chunk is done with the LDS tiles
-    for (int e = tid; e < CH * DK; e += 256) {
-      const int t = e / DK, i = e % DK;
-      const bool in = t < n;
-      Ws[t][i] = W[e];
-      Qs[t][i] = in ? q[(bh * P + t0 + t) * DK + i] : 0.f;
-      Ks[t][i] = in ? k[(bh * P + t0 + t) * DK + i] : 0.f;
+  f4 sacc[OWN];
+#pragma unroll
+  for (int o = 0; o < OWN; ++o) {
+    const int ib = w * OWN + o;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sacc[o][r] = S[(ib * 16 + 4 * g + r) * DV + j0 + m];
+    st4(&St[m * SP + ib * 16 + 4 * g], sacc[o]);
+  }
+  __syncthreads();
+
+  // A operands of a chunk (rows of W, K^T), U and the log-gates, loaded one chunk ahead.
+  // Each workgroup pulls 64 KB of W and K^T per chunk through its CU: issued in one
+  // burst those loads fill the vector-memory queue and stall the wave's MFMAs behind
+  // them, so they are spread over the D products below (four loads per eight MFMAs).
+  struct Ops {
+    f4 w[NIB], kt[OWN * 4], lg;
+    float u[4], lglast;
+  };
+  auto fetch_pair = [&](const float *ck, int ib, Ops &x) {  // four of the 2 NIB large loads
+    x.w[ib] = ld4(&ck[L::W + (w * 16 + m) * DK + ib * 16 + 4 * g]);
+    x.w[ib + 1] = ld4(&ck[L::W + (w * 16 + m) * DK + ib * 16 + 16 + 4 * g]);
+#pragma unroll
+    for (int u = ib; u < ib + 2; ++u)
+      x.kt[u] = ld4(&ck[L::KT + ((w * OWN + u / 4) * 16 + m) * CH + (u % 4) * 16 + 4 * g]);
+  };
+  auto fetch_small = [&](const float *ck, Ops &x) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x.u[r] = ck[L::U + (w * 16 + 4 * g + r) * DV + j0 + m];
+    x.lg = ld4(&ck[L::LG + w * 16 + 4 * g]);
+    x.lglast = ck[L::LG + CH - 1];
+  };
+  auto fetch = [&](int c, Ops &x) {
+    const float *ck = ws + (bh * nch + c) * L::SIZE;
+#pragma unroll
+    for (int ib = 0; ib < NIB; ib += 2) fetch_pair(ck, ib, x);
+    fetch_small(ck, x);
+  };
+  // One chunk: consumes the operands in cu, loads chunk c + 1's into nx.  Two operand
+  // sets alternate roles (the loop below is unrolled by two), so the prefetched
+  // registers are never copied -- a copy would wait for the loads it is meant to hide.
+  auto step = [&](int c, const Ops &cu, Ops &nx) {
+    float *ck = ws + (bh * nch + c) * L::SIZE;
+    const float *cn = ws + (bh * nch + min(c + 1, nch - 1)) * L::SIZE;
+    // entry state of the chunk, for the output kernel
+#pragma unroll
+    for (int o = 0; o < OWN; ++o) {
+      const int ib = w * OWN + o;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ck[L::SC + (ib * 16 + 4 * g + r) * DV + j0 + m] = sacc[o][r];
     }
-    for (int e = tid; e < CH * CH; e += 256) Pm[e / CH][e % CH] = Pg[e];
-    for (int e = tid; e < CH * VB; e += 256) Us[e / VB][e % VB] = U[(e / VB) * DV + j0 + e % VB];
-    if (tid < CH) {
-      const float l = LG[tid];
-      lg[tid] = l;
-      eg[tid] = __expf(l);
-      wl[tid] = __expf(LG[CH - 1] - l);
+    // rows 16w..16w+15 of D = U - W S (contraction over the state's rows)
+    f4 d0 = zero, d1 = zero;
+#pragma unroll
+    for (int ib = 0; ib < NIB; ib += 2) {
+      const f4 b0 = ld4(&St[m * SP + ib * 16 + 4 * g]);
+      const f4 b1 = ld4(&St[m * SP + ib * 16 + 16 + 4 * g]);
+      fetch_pair(cn, ib, nx);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        d0 = mma(cu.w[ib][kk], b0[kk], d0);
+        d1 = mma(cu.w[ib + 1][kk], b1[kk], d1);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the next loads behind these MFMAs
     }
-    __syncthreads();
-    // D = U - W S
-    for (int e = tid; e < CH * VB; e += 256) {
-      const int t = e / VB, j = e % VB;
-      float acc = Us[t][j];
-#pragma unroll 8
-      for (int i = 0; i < DK; ++i) acc = fmaf(-Ws[t][i], Ss[i][j], acc);
-      Dl[t][j] = acc;
+    fetch_small(cn, nx);
+    f4 dw;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = w * 16 + 4 * g + r;
+      const float dd = cu.u[r] - (d0[r] + d1[r]);
+      ck[L::DC + t * DV + j0 + m] = dd;
+      dw[r] = __expf(cu.lglast - cu.lg[r]) * dd;
     }
-    __syncthreads();
-    // O = diag(e^lg) Q S + P D
-    for (int e = tid; e < CH * VB; e += 256) {
-      const int t = e / VB, j = e % VB;
-      if (t >= n) continue;
-      float qs = 0.f, pd = 0.f;
-#pragma unroll 8
-      for (int i = 0; i < DK; ++i) qs = fmaf(Qs[t][i], Ss[i][j], qs);
-      for (int s = 0; s <= t; ++s) pd = fmaf(Pm[t][s], Dl[s][j], pd);
-      out[(bh * P + t0 + t) * DV + j0 + j] = fmaf(eg[t], qs, pd);
+    st4(&Dt[m * AP + w * 16 + 4 * g], dw);
+    __syncthreads();  // Dt complete; every wave is done reading St
+    // S = e^{lg_last} S + K^T diag(R[last, :]) D for this wave's row blocks
+    const float glast = __expf(cu.lglast);
+#pragma unroll
+    for (int o = 0; o < OWN; ++o) {
+      const int ib = w * OWN + o;
+      f4 acc = sacc[o] * glast;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const f4 a = cu.kt[o * 4 + tb];
+        const f4 bb = ld4(&Dt[m * AP + tb * 16 + 4 * g]);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc = mma(a[kk], bb[kk], acc);
+      }
+      sacc[o] = acc;
+      st4(&St[m * SP + ib * 16 + 4 * g], acc);
     }
-    __syncthreads();  // the old state is no longer read
-    // S = e^{lg_last} S + K^T diag(R[last, :]) D
-    const float glast = eg[CH - 1];
-    for (int e = tid; e < DK * VB; e += 256) {
-      const int i = e / VB, j = e % VB;
-      float acc = glast * Ss[i][j];
-      for (int s = 0; s < n; ++s) acc = fmaf(Ks[s][i] * wl[s], Dl[s][j], acc);
-      Ss[i][j] = acc;
+    __syncthreads();  // St holds the next entry state; Dt is free
+  };
+  Ops xa, xb;
+  fetch(0, xa);
+  for (int c = 0; c < nch; c += 2) {
+    step(c, xa, xb);
+    if (c + 1 < nch) step(c + 1, xb, xa);
+  }
+#pragma unroll
+  for (int o = 0; o < OWN; ++o) {
+    const int ib = w * OWN + o;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) S[(ib * 16 + 4 * g + r) * DV + j0 + m] = sacc[o][r];
+  }
+}
+
+template <int DK, int DV>
+__global__ void __launch_bounds__(256) k_gdn_out(const float *__restrict__ q,
+                                                 const float *__restrict__ ws,
+                                                 float *__restrict__ out, int BH, int P, int nch) {
+  using L = Chunk<DK, DV>;
+  constexpr int NJ = DV / OC;  // column blocks of the output
+  constexpr int OP = OC + 4;
+  __shared__ __align__(16) float Ss[DK * OP];  // S_c[:, j0:j0+OC]
+  __shared__ __align__(16) float Ds[CH * OP];  // D_c[:, j0:j0+OC]
+  int G, k;
+  if (!head_slot(nch * NJ, BH, G, k)) return;  // whole workgroup, before any barrier
+  const int c = k / NJ, jh = k % NJ;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, m = lane & 15, g = lane >> 4;
+  const size_t bh = G;
+  const int t0 = c * CH;
+  const int n = min(CH, P - t0);
+  const float *ck = ws + (bh * nch + c) * L::SIZE;
+  const int j0 = jh * OC;
+  const f4 zero = {0.f, 0.f, 0.f, 0.f};
+  // this wave's A operands: rows 16w.. of Q and of P
+  const bool qin = w * 16 + m < n;
+  const float *qr = q + (bh * P + t0 + w * 16 + m) * DK;
+  f4 qa[DK / 16], pa[4];
+#pragma unroll
+  for (int ib = 0; ib < DK / 16; ++ib) qa[ib] = qin ? ld4(qr + ib * 16 + 4 * g) : zero;
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb)
+    pa[sb] = sb <= w ? ld4(&ck[L::P + (w * 16 + m) * CH + sb * 16 + 4 * g]) : zero;
+  const f4 lgr = ld4(&ck[L::LG + w * 16 + 4 * g]);
+  {  // the shared B operands
+    constexpr int Q4 = OC / 4;  // float4s per staged row
+    constexpr int NS = DK * Q4 / 256, ND = CH * Q4 / 256;
+    f4 sr[NS], dr[ND];
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int e = tid + 256 * u;
+      sr[u] = ld4(&ck[L::SC + (e / Q4) * DV + j0 + (e % Q4) * 4]);
+    }
+#pragma unroll
+    for (int u = 0; u < ND; ++u) {
+      const int e = tid + 256 * u;
+      dr[u] = ld4(&ck[L::DC + (e / Q4) * DV + j0 + (e % Q4) * 4]);
+    }
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int e = tid + 256 * u;
+      st4(&Ss[(e / Q4) * OP + (e % Q4) * 4], sr[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < ND; ++u) {
+      const int e = tid + 256 * u;
+      st4(&Ds[(e / Q4) * OP + (e % Q4) * 4], dr[u]);
     }
   }
   __syncthreads();
-  for (int e = tid; e < DK * VB; e += 256) S[(e / VB) * DV + j0 + e % VB] = Ss[e / VB][e % VB];
+  if (w * 16 >= n) return;  // a wave of pad rows only
+  constexpr int NC = OC / 16;  // column tiles per wave
+  f4 acc[NC];
+#pragma unroll
+  for (int ct = 0; ct < NC; ++ct) acc[ct] = zero;
+  // Q S_c for rows 16w.. of the chunk, contraction over the state's rows
+#pragma unroll
+  for (int ib = 0; ib < DK / 16; ++ib) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const float *srow = Ss + (ib * 16 + 4 * g + kk) * OP + m;
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) acc[ct] = mma(qa[ib][kk], srow[ct * 16], acc[ct]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float e = __expf(lgr[r]);
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) acc[ct][r] *= e;
+  }
+  // + P D_c over the chunk's rows up to this wave's (P is zero above the diagonal)
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) {
+    if (sb > w) break;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const float *drow = Ds + (sb * 16 + 4 * g + kk) * OP + m;
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) acc[ct] = mma(pa[sb][kk], drow[ct * 16], acc[ct]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = w * 16 + 4 * g + r;
+    if (t >= n) continue;
+    float *orow = out + (bh * P + t0 + t) * DV + j0 + m;
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) orow[ct * 16] = acc[ct][r];
+  }
 }
 
 template <int DK, int DV>
@@ -215,12 +490,17 @@ hipError_t launch_dims(const float *q, const float *k, const float *v, const flo
                        const float *alpha, float *state, float *out, int B, int H, int P,
                        float *ws, hipStream_t s) {
   const int nch = (P + CH - 1) / CH;
-  hipLaunchKernelGGL((k_gdn_prep<DK, DV>), dim3(nch, H, B), dim3(256), 0, s, q, k, v, beta,
-                     alpha, ws, H, P, nch);
+  const int BH = B * H, slots = 8 * ((BH + 7) / 8);  // grid sizes checked by gdn_grid_fits
+  hipLaunchKernelGGL((k_gdn_prep<DK, DV>), dim3(slots * nch), dim3(PREP_THREADS), 0, s, q, k, v,
+                     beta, alpha, ws, BH, P, nch);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_gdn_scan<DK, DV>), dim3(DV / VB, H, B), dim3(256), 0, s, q, k, ws, state,
-                     out, H, P, nch);
+  hipLaunchKernelGGL((k_gdn_scan<DK, DV>), dim3(slots * (DV / VB)), dim3(256), 0, s, ws, state,
+                     BH, nch);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_gdn_out<DK, DV>), dim3(slots * nch * (DV / OC)), dim3(256), 0, s, q, ws,
+                     out, BH, P, nch);
   return hipGetLastError();
 }
 
@@ -229,6 +509,13 @@ hipError_t launch_dims(const float *q, const float *k, const float *v, const flo
 size_t gdn_workspace_bytes(int B, int H, int P, int dk, int dv) {
   const size_t nch = (static_cast<size_t>(P) + CH - 1) / CH;
   return static_cast<size_t>(B) * H * nch * gdn_chunk_floats(dk, dv) * sizeof(float);
+}
+
+bool gdn_grid_fits(int B, int H, int P) {
+  const size_t slots = 8 * ((static_cast<size_t>(B) * H + 7) / 8);
+  const size_t nch = (static_cast<size_t>(P) + CH - 1) / CH;
+  const size_t per = std::max<size_t>(nch * (128 / OC), 128 / VB);  // the largest of the three grids
+  return slots * per <= 0x7fffffff;
 }
 
 bool gdn_dims_supported(int dk, int dv) {

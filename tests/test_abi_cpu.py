@@ -175,16 +175,18 @@ def test_gdn_validation(cp):
     lib = cp.raw()
     f = lib.cp_gdn_chunk_prefill
     ws = cp.gdn_workspace_bytes(1, 2, 100, 64, 64)
-    assert ws == 1 * 2 * 2 * (64 * 64 + 64 * 64 + 64 * 64 + 64) * 4
+    # per (sequence, head, chunk of 64): W, U, P, lg, K^T, entry state, D (fp32)
+    assert ws == 1 * 2 * 2 * (2 * 64 * 64 + 2 * 64 * 64 + 64 * 64 + 64 + 64 * 64) * 4
     assert cp.gdn_workspace_bytes(1, 2, 100, 96, 64) == 0
     call = lambda **kw: f(*[kw.get(n, FAKE) for n in ("q", "k", "v", "beta", "alpha", "state", "out")],
                           kw.get("B", 1), kw.get("H", 2), kw.get("P", 100), kw.get("dk", 64),
                           kw.get("dv", 64), kw.get("ws", FAKE), kw.get("wsb", ws), None)
     assert call(dk=96) == cp.ERR_SHAPE
     assert call(dv=256) == cp.ERR_SHAPE
-    assert call(H=70000) == cp.ERR_SHAPE
+    assert call(B=65535, H=65535, P=1 << 20) == cp.ERR_SHAPE  # beyond one launch grid
     assert call(P=-1) == cp.ERR_ARG
     assert call(q=None) == cp.ERR_ARG
     assert call(ws=None) == cp.ERR_ARG
+    assert call(q=FAKE + 4) == cp.ERR_ARG  # not 16-byte aligned
     assert call(wsb=ws - 1) == cp.ERR_WORKSPACE
     assert call(P=0, q=None, ws=None) == cp.OK  # empty prompt: nothing is read

@@ -291,3 +291,46 @@ def test_workload_c5_sampled_rows(cp, layer):
     err = rowwise_rel_err(got, ref, m)
     assert err <= TOL[I.BF16], err
     assert int(status.item()) == 0
+
+
+MERGE = [
+    dict(name="decode_d128_long", dtype=I.BF16, B=2, H=8, nKV=2, D=128, C=1, cap=4096,
+         seen=[3000, 1500], n_valid=[1, 1]),
+    dict(name="c4_d64_long", dtype=I.BF16, B=1, H=8, nKV=2, D=64, C=4, cap=3000, seen=[2900],
+         n_valid=[3]),
+    dict(name="decode_d256_window", dtype=I.BF16, B=1, H=8, nKV=1, D=256, C=1, cap=2048,
+         window=1500, seen=[2000], n_valid=[1]),
+]
+
+
+@pytest.mark.parametrize("kw", MERGE, ids=lambda c: c["name"])
+@pytest.mark.parametrize("mode", ["inkernel", "explicit"])
+def test_decode_split_merge(cp, kw, mode):
+    """Decode-sized chunks over a long past, where the planner splits the keys: repeated
+    calls on one workspace give the same bits, match the oracle, and the selection is the
+    merged row."""
+    kw = dict(kw)
+    kw.pop("name")
+    cfg = I.small(**kw)
+    t, cache, status = _setup(cp, cfg)
+    q, k, v = dev(t["q"]), dev(t["k"]), dev(t["v"])
+    nv = dev(t["n_valid"])
+    mask = None
+    if mode == "explicit":
+        mask = cp.build_mask(cache, nv, cfg.H, cfg.C, cfg.mask_ld(), window=cfg.window)
+    window = 0 if mask is not None else cfg.window
+    nb = cp.attn_workspace_bytes(cache, q, k, v, mask=mask, window=window)
+    assert nb > 0  # the planner splits these keys
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    sel = torch.zeros((cfg.B, cfg.H, cfg.D), dtype=q.dtype, device="cuda")
+    outs = []
+    for _ in range(3):
+        outs.append(cp.attn_chunk_with_past(cache, q, k, v, n_valid=nv, mask=mask, window=window,
+                                            scale=cfg.scale, workspace=ws, select_out=sel))
+    torch.cuda.synchronize()
+    ref = _oracle(cfg, t)
+    _check(cfg, outs[0], ref)
+    for o in outs[1:]:
+        assert np.array_equal(bits(o), bits(outs[0]))
+    assert np.array_equal(bits(sel), bits(cp.select_row(outs[0], nv, -1)))
+    assert int(status.item()) == 0

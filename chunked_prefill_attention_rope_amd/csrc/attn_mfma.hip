@@ -336,6 +336,21 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SMALL>::ROWW * Sel<D, EXT, S
   const int head = g * p.G + (row_ok ? hl : 0);
   const int irow = row_ok ? i : 0;
 
+  // Q^T fragments: lane holds q[row n][16 s + 8 hh .. + 7] for every k-step s.  They do
+  // not depend on the cache state, so they are requested first and their latency
+  // overlaps that of `seen` (and they do not queue behind the first tiles' loads).
+  bf16x8 qf[NS];
+  {
+    const uint16_t *Q = static_cast<const uint16_t *>(p.q) +
+                        ((static_cast<size_t>(b) * p.H + head) * p.C + irow) * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row_ok) v = *reinterpret_cast<const u32x4 *>(Q + 16 * s);
+      qf[s] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
   const int seen = p.seen[b];
   const bool lead = tid == 0 && qtile == 0 && split == 0 && g == 0;
   const int nv = read_nvalid(p.n_valid, b, p.C, lead ? p.status : nullptr);
@@ -365,6 +380,21 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SMALL>::ROWW * Sel<D, EXT, S
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
+  }
+  // Mask loads: load j of every tile reads the same rows and chunk positions, so each
+  // lane's row offset and column within the tile are formed once (float P = q * 64 +
+  // lane of the block: row P / 32, physical chunk (P % 32) / 4 holding the row's logical
+  // chunk physical ^ mswz(row)).
+  int64_t mrow[EXPLICIT ? NMK : 1];
+  int mcol[EXPLICIT ? NMK : 1];
+  if constexpr (EXPLICIT) {
+#pragma unroll
+    for (int j = 0; j < NMK; ++j) {
+      const int P = (wave * NMK + j) * 64 + lane;
+      const int row = P >> 5, pp = P & 31;
+      mrow[j] = mtab[row];
+      mcol[j] = 4 * ((pp >> 2) ^ mswz(row)) + (pp & 3);
+    }
   }
 
   f32x16 oacc[NDW];
@@ -432,9 +462,8 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SMALL>::ROWW * Sel<D, EXT, S
     return chunk;
   };
   // load j of a tile into ring stage st: j < NL K rows, j < 2 NL V rows, else 256
-  // bytes of the mask block (float P = q * 64 + lane: row P / 32, physical chunk
-  // (P % 32) / 4 holding the row's logical chunk physical ^ mswz(row), columns
-  // clamped into the valid range -- those past it are masked to -inf)
+  // bytes of the mask block (positions from mrow / mcol above; columns clamped into the
+  // valid range -- those past it are masked to -inf)
   auto dma = [&](int j, bool chunk, const int *srow, int first, int lim, uint16_t *st)
                  __attribute__((always_inline)) {
     if (j < 2 * NL) {
@@ -446,12 +475,11 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SMALL>::ROWW * Sel<D, EXT, S
       else
         dma16((chunk ? VN : VC) + r + voff[e], st + TILE + q * 512);
     } else if constexpr (EXPLICIT) {
-      const int q = wave * NMK + (j - 2 * NL);
-      const int P = q * 64 + lane;
-      const int row = P >> 5, pp = P & 31;
-      const int col = imin(first + 4 * ((pp >> 2) ^ mswz(row)) + (pp & 3), lim - 1);
-      const int64_t mcol = (chunk ? static_cast<int64_t>(gl.L) : 0) + col;
-      dma4(p.mask + mtab[row] + mcol, reinterpret_cast<float *>(st + 2 * TILE) + q * 64);
+      const int jm = j - 2 * NL;
+      const int q = wave * NMK + jm;
+      const int col = imin(first + mcol[jm], lim - 1);
+      dma4(p.mask + mrow[jm] + (chunk ? static_cast<int64_t>(gl.L) : 0) + col,
+           reinterpret_cast<float *>(st + 2 * TILE) + q * 64);
     }
   };
 
@@ -498,19 +526,6 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SMALL>::ROWW * Sel<D, EXT, S
 #pragma unroll
       for (int l = 0; l < ND; ++l) dma(l, ch, srow, f0, l0, st);
     }
-  // Q^T fragments: lane holds q[row n][16 s + 8 hh .. + 7] for every k-step s.  Loaded
-  // after the first tiles' loads are on their way, so that the two latencies overlap.
-  bf16x8 qf[NS];
-  {
-    const uint16_t *Q = static_cast<const uint16_t *>(p.q) +
-                        ((static_cast<size_t>(b) * p.H + head) * p.C + irow) * D + 8 * hh;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row_ok) v = *reinterpret_cast<const u32x4 *>(Q + 16 * s);
-      qf[s] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
 
   for (int u = u0; u < u1; ++u) {
     // tile u has landed in this wave's share of the ring once at most the loads of

@@ -74,10 +74,13 @@ AttnPlan plan_attention(const cp_cache &c, const cp_attn_args &a, bool for_works
     pl.splits = forced > 64 ? 64 : forced;
   } else if (!(a.flags & CP_ATTN_NO_SPLIT) && base > 0 && base < kNumCU) {
     // Few query tiles: split the keys so that more CUs work -- each split writes fp32
-    // partials that a second kernel merges.  The matrix-core kernel keeps >= 4 key tiles
-    // per split; the vector-ALU kernel's 16-key tiles each cost a memory round trip that
-    // their arithmetic does not hide, so it goes down to one tile per split.
-    const long per = pl.mfma ? 4 : 1;
+    // partials that a second kernel merges.  The matrix-core kernel keeps >= 3 key tiles
+    // per split (its ~6 us of prologue and first-tile latency is paid per workgroup; 3
+    // measured best on c2-c4); the vector-ALU kernel's 16-key tiles each cost a memory
+    // round trip that their arithmetic does not hide, so it goes down to one tile per
+    // split.  The tile count is a bound from the capacity (the live length is on the
+    // device), so a split can get one tile less than this.
+    const long per = pl.mfma ? 3 : 1;
     // several small-rows workgroups share a CU
     const long target = (pl.mfma && pl.small_rows ? 4 : 2) * kNumCU;
     long s = (target + base - 1) / base;

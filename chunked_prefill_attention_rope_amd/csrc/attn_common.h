@@ -31,7 +31,7 @@ struct AttnParams {
   int splits;
   int full_tiles;
   int mask_vec4;  // explicit mask rows may be read 16 bytes at a time
-  int small_rows; // matrix-core kernel: the 64-row configuration
+  int small_rows; // matrix-core kernel: 0, the 64-row configuration (1) or its deep ring (2)
   float sl2e;     // scale * log2(e)
 };
 

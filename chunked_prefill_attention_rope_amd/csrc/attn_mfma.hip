@@ -218,12 +218,20 @@ struct Cfg<256, true> {
 // several workgroups share a CU and stream independent K/V (the regime is HBM-bound:
 // a standard workgroup would leave most of its rows empty and stream one tile at a
 // time per CU).
-template <int D, bool EX, bool SMALL>
+//  SM = 1: a 2-stage ring, four workgroups per CU.
+//  SM = 2 (in-kernel mask): a 3-stage ring, three per CU, for splits that stream many
+//  tiles (long decode contexts), where the steady state needs more bytes in flight per
+//  CU than four shallow workgroups keep; short splits prefer more workgroups.
+template <int D, bool EX, int SM>
 struct Sel : Cfg<D, EX> {};
 template <int D, bool EX>
-struct Sel<D, EX, true> {
+struct Sel<D, EX, 1> {
   static constexpr int KT = 32, STAGES = 2, WAVES = 2, DSPLIT = Cfg<D, EX>::DSPLIT;
   static constexpr int ROWW = 2;
+};
+template <int D, bool EX>
+struct Sel<D, EX, 2> : Sel<D, EX, 1> {
+  static constexpr int STAGES = EX ? 2 : 3;
 };
 
 // One wave-wide 4-byte direct-to-LDS load (mask blocks: no alignment beyond 4 bytes).
@@ -262,12 +270,12 @@ __device__ __forceinline__ void wait_tiles_after(int n) {
 // EXPLICIT: the additive mask comes from memory.  EXT: use the explicit-mask tiling
 // (set with EXPLICIT, and for the in-kernel rule under CP_ATTN_FULL_TILES so that both
 // modes see the same key partition).
-template <int D, bool EXPLICIT, bool EXT, bool SMALL>
-__global__ void __launch_bounds__((64 * Sel<D, EXT, SMALL>::ROWW * Sel<D, EXT, SMALL>::DSPLIT))
-    __attribute__((amdgpu_waves_per_eu(Sel<D, EXT, SMALL>::WAVES, Sel<D, EXT, SMALL>::WAVES)))
+template <int D, bool EXPLICIT, bool EXT, int SM>
+__global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>::DSPLIT))
+    __attribute__((amdgpu_waves_per_eu(Sel<D, EXT, SM>::WAVES, Sel<D, EXT, SM>::WAVES)))
     k_attn_mfma(AttnParams p) {
   static_assert(EXT || !EXPLICIT, "explicit masks use the explicit tiling");
-  using CF = Sel<D, EXT, SMALL>;
+  using CF = Sel<D, EXT, SM>;
   constexpr int KT = CF::KT;
   constexpr int STAGES = CF::STAGES;
   constexpr int DSPLIT = CF::DSPLIT;
@@ -758,31 +766,35 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SMALL>::ROWW * Sel<D, EXT, S
   }
 }
 
-template <int D, bool EXPLICIT, bool EXT, bool SMALL>
+template <int D, bool EXPLICIT, bool EXT, int SM>
 void launch_one(const AttnParams &p, unsigned blocks, hipStream_t s) {
-  using CF = Sel<D, EXT, SMALL>;
-  hipLaunchKernelGGL((k_attn_mfma<D, EXPLICIT, EXT, SMALL>), dim3(blocks),
+  using CF = Sel<D, EXT, SM>;
+  hipLaunchKernelGGL((k_attn_mfma<D, EXPLICIT, EXT, SM>), dim3(blocks),
                      dim3(64 * CF::ROWW * CF::DSPLIT), 0, s, p);
 }
 
-template <int D, bool SMALL>
+template <int D, int SM>
 void launch_mode(const AttnParams &p, unsigned blocks, hipStream_t s) {
   if (p.mask)
-    launch_one<D, true, true, SMALL>(p, blocks, s);
+    launch_one<D, true, true, SM>(p, blocks, s);
   else if (p.full_tiles)
-    launch_one<D, false, true, SMALL>(p, blocks, s);
+    launch_one<D, false, true, SM>(p, blocks, s);
   else
-    launch_one<D, false, false, SMALL>(p, blocks, s);
+    launch_one<D, false, false, SM>(p, blocks, s);
 }
 
 template <int D>
 hipError_t launch_d(const AttnParams &p, hipStream_t s) {
   const unsigned blocks = static_cast<unsigned>(p.qtiles) * p.splits * p.B * p.nKV;
   if (blocks == 0) return hipSuccess;
-  if (p.small_rows)
-    launch_mode<D, true>(p, blocks, s);
-  else
-    launch_mode<D, false>(p, blocks, s);
+  if (p.small_rows == 2) {
+    if (p.mask || p.full_tiles) return hipErrorInvalidValue;  // deep ring: in-kernel rule only
+    launch_one<D, false, false, 2>(p, blocks, s);
+  } else if (p.small_rows == 1) {
+    launch_mode<D, 1>(p, blocks, s);
+  } else {
+    launch_mode<D, 0>(p, blocks, s);
+  }
   return hipGetLastError();
 }
 
@@ -801,25 +813,48 @@ hipError_t launch_attn_mfma(const AttnParams &p, int D, hipStream_t s) {
   }
 }
 
-template <bool EX, bool SMALL>
+template <bool EX, int SM>
 int rows_of(int D) {
-  return 32 * (D == 256 ? Sel<256, EX, SMALL>::ROWW
-                        : (D == 128 ? Sel<128, EX, SMALL>::ROWW : Sel<64, EX, SMALL>::ROWW));
+  return 32 * (D == 256 ? Sel<256, EX, SM>::ROWW
+                        : (D == 128 ? Sel<128, EX, SM>::ROWW : Sel<64, EX, SM>::ROWW));
 }
-template <bool EX, bool SMALL>
+template <bool EX, int SM>
 int keys_of(int D) {
-  return D == 256 ? Sel<256, EX, SMALL>::KT
-                  : (D == 128 ? Sel<128, EX, SMALL>::KT : Sel<64, EX, SMALL>::KT);
+  return D == 256 ? Sel<256, EX, SM>::KT
+                  : (D == 128 ? Sel<128, EX, SM>::KT : Sel<64, EX, SM>::KT);
 }
 
-int mfma_rows_per_tile(int D, bool explicit_tiling, bool small_rows) {
-  if (small_rows) return explicit_tiling ? rows_of<true, true>(D) : rows_of<false, true>(D);
-  return explicit_tiling ? rows_of<true, false>(D) : rows_of<false, false>(D);
+// small_rows: 0 standard, 1 small rows, 2 small rows with the deep ring (same tiling)
+int mfma_rows_per_tile(int D, bool explicit_tiling, int small_rows) {
+  if (small_rows) return explicit_tiling ? rows_of<true, 1>(D) : rows_of<false, 1>(D);
+  return explicit_tiling ? rows_of<true, 0>(D) : rows_of<false, 0>(D);
 }
 
-int mfma_keys_per_tile(int D, bool explicit_tiling, bool small_rows) {
-  if (small_rows) return explicit_tiling ? keys_of<true, true>(D) : keys_of<false, true>(D);
-  return explicit_tiling ? keys_of<true, false>(D) : keys_of<false, false>(D);
+// Workgroups of one configuration resident per CU: waves (the kernels ask for two per
+// SIMD) and LDS (ring, plus the explicit mask's row table) both bound it.
+template <int D, bool EX, int SM>
+int wgs_of() {
+  using CF = Sel<D, EX, SM>;
+  constexpr int STAGE = 2 * CF::KT * D + (EX ? 32 * CF::ROWW * CF::KT * 2 : 0);
+  constexpr int lds = CF::STAGES * STAGE * 2 + (EX ? 32 * CF::ROWW * 8 : 0);
+  constexpr int by_waves = 4 * CF::WAVES / (CF::ROWW * CF::DSPLIT);
+  constexpr int by_lds = 160 * 1024 / lds;
+  return by_waves < by_lds ? by_waves : by_lds;
+}
+template <bool EX, int SM>
+int wgs_d(int D) {
+  return D == 256 ? wgs_of<256, EX, SM>() : (D == 128 ? wgs_of<128, EX, SM>() : wgs_of<64, EX, SM>());
+}
+
+int mfma_wgs_per_cu(int D, bool explicit_tiling, int small_rows) {
+  if (small_rows == 2) return wgs_d<false, 2>(D);
+  if (small_rows == 1) return explicit_tiling ? wgs_d<true, 1>(D) : wgs_d<false, 1>(D);
+  return explicit_tiling ? wgs_d<true, 0>(D) : wgs_d<false, 0>(D);
+}
+
+int mfma_keys_per_tile(int D, bool explicit_tiling, int small_rows) {
+  if (small_rows) return explicit_tiling ? keys_of<true, 1>(D) : keys_of<false, 1>(D);
+  return explicit_tiling ? keys_of<true, 0>(D) : keys_of<false, 0>(D);
 }
 
 }  // namespace cp

@@ -10,8 +10,9 @@
 #include "attn_common.h"
 
 namespace cp {
-int mfma_keys_per_tile(int D, bool explicit_tiling, bool small_rows);
-int mfma_rows_per_tile(int D, bool explicit_tiling, bool small_rows);
+int mfma_keys_per_tile(int D, bool explicit_tiling, int small_rows);
+int mfma_rows_per_tile(int D, bool explicit_tiling, int small_rows);
+int mfma_wgs_per_cu(int D, bool explicit_tiling, int small_rows);
 int valu_keys(int D);
 
 namespace {
@@ -46,7 +47,7 @@ AttnPlan plan_attention(const cp_cache &c, const cp_attn_args &a, bool for_works
   const bool ext = a.mask != nullptr || (a.flags & CP_ATTN_FULL_TILES);
   const bool mfma_d = c.D == 64 || c.D == 128 || c.D == 256;
   // all rows of one KV head fit 64: the small-rows configuration
-  pl.small_rows = static_cast<long>(a.C) * G <= 64;
+  pl.small_rows = static_cast<long>(a.C) * G <= 64 ? 1 : 0;
   const int rows = mfma_d ? mfma_rows_per_tile(c.D, ext, pl.small_rows) : 0;
   pl.mfma = c.dtype == CP_BF16 && mfma_d && G <= rows && !(a.flags & CP_ATTN_FORCE_GENERIC) &&
             aligned;
@@ -70,23 +71,33 @@ AttnPlan plan_attention(const cp_cache &c, const cp_attn_args &a, bool for_works
   }
   const long tiles = (keys + pl.kt - 1) / pl.kt;
   const int forced = static_cast<int>((a.flags >> 8) & 0xffu);
-  if (forced > 0) {
-    pl.splits = forced > 64 ? 64 : forced;
-  } else if (!(a.flags & CP_ATTN_NO_SPLIT) && base > 0 && base < kNumCU) {
-    // Few query tiles: split the keys so that more CUs work -- each split writes fp32
-    // partials that a second kernel merges.  The matrix-core kernel keeps >= 3 key tiles
-    // per split (its ~6 us of prologue and first-tile latency is paid per workgroup; 3
-    // measured best on c2-c4); the vector-ALU kernel's 16-key tiles each cost a memory
-    // round trip that their arithmetic does not hide, so it goes down to one tile per
-    // split.  The tile count is a bound from the capacity (the live length is on the
-    // device), so a split can get one tile less than this.
-    const long per = pl.mfma ? 3 : 1;
-    // several small-rows workgroups share a CU
-    const long target = (pl.mfma && pl.small_rows ? 4 : 2) * kNumCU;
-    long s = (target + base - 1) / base;
+  // Few query tiles: split the keys so that more CUs work -- each split writes fp32
+  // partials that a second kernel merges.  The matrix-core kernel keeps >= 3 key tiles
+  // per split (its ~6 us of prologue and first-tile latency is paid per workgroup; 3
+  // measured best on c2-c4); the vector-ALU kernel's 16-key tiles each cost a memory
+  // round trip that their arithmetic does not hide, so it goes down to one tile per
+  // split.  The tile count is a bound from the capacity (the live length is on the
+  // device), so a split can get one tile less than this.
+  const long per = pl.mfma ? 3 : 1;
+  // as many splits as fill the CUs once (rounded down: a partial second round of
+  // workgroups would double the time of the last ones)
+  auto split_for = [&](long wg_per_cu) {
+    long s = wg_per_cu * kNumCU / base;
     if (s > tiles / per) s = tiles / per;
     if (s > 64) s = 64;
-    pl.splits = s > 1 ? static_cast<int>(s) : 1;
+    return s > 1 ? static_cast<int>(s) : 1;
+  };
+  const bool split_ok = !(a.flags & CP_ATTN_NO_SPLIT) && base > 0 && base < kNumCU;
+  if (forced > 0) {
+    pl.splits = forced > 64 ? 64 : forced;
+  } else if (split_ok) {
+    pl.splits = split_for(pl.mfma ? mfma_wgs_per_cu(c.D, ext, pl.small_rows) : 2);
+  }
+  // Small rows whose splits each stream many tiles (long decode contexts): the deep-ring
+  // configuration, three workgroups per CU (in-kernel rule only).
+  if (pl.mfma && pl.small_rows && !ext && tiles / pl.splits >= 24) {
+    pl.small_rows = 2;
+    if (forced == 0 && split_ok) pl.splits = split_for(mfma_wgs_per_cu(c.D, ext, 2));
   }
   if (pl.splits > 1 && !for_workspace &&
       (!a.workspace || a.workspace_bytes < attn_workspace_bytes(c, a, pl)))
@@ -134,7 +145,7 @@ hipError_t launch_attention(const cp_cache &c, const cp_attn_args &a, hipStream_
   p.mask_vec4 = a.mask && aligned16(a.mask) && a.mask_ld % 4 == 0 && a.mask_head_stride % 4 == 0 &&
                 a.mask_batch_stride % 4 == 0;
   p.sl2e = a.scale * kLog2e;
-  p.small_rows = pl.small_rows ? 1 : 0;
+  p.small_rows = pl.small_rows;
   if (pl.splits > 1) {
     const size_t rows = static_cast<size_t>(c.B) * a.H * a.C;
     unsigned char *w = static_cast<unsigned char *>(a.workspace);

@@ -119,7 +119,7 @@ struct AttnPlan {
   int qtiles;     // query tiles per (b, kv head)
   int qpos;       // chunk rows per query tile
   int kt;         // keys per tile
-  bool small_rows;  // matrix-core kernel in its 64-row configuration
+  int small_rows;   // matrix-core kernel: 0, or its 64-row configuration (1; 2 = deep ring)
 };
 
 AttnPlan plan_attention(const cp_cache &c, const cp_attn_args &a, bool for_workspace);

@@ -305,10 +305,12 @@ MERGE = [
 
 @pytest.mark.parametrize("kw", MERGE, ids=lambda c: c["name"])
 @pytest.mark.parametrize("mode", ["inkernel", "explicit"])
-def test_decode_split_merge(cp, kw, mode):
-    """Decode-sized chunks over a long past, where the planner splits the keys: repeated
-    calls on one workspace give the same bits, match the oracle, and the selection is the
-    merged row."""
+@pytest.mark.parametrize("split", ["auto", "four", "none"])
+def test_decode_split_merge(cp, kw, mode, split):
+    """Decode-sized chunks over a long past: repeated calls on one workspace give the same
+    bits, match the oracle, and the selection is the merged row.  Four forced splits (or
+    none) leave each split 24+ tiles, which selects the deep-ring small-rows configuration
+    for the in-kernel rule; the planner's own choice does not."""
     kw = dict(kw)
     kw.pop("name")
     cfg = I.small(**kw)
@@ -319,14 +321,16 @@ def test_decode_split_merge(cp, kw, mode):
     if mode == "explicit":
         mask = cp.build_mask(cache, nv, cfg.H, cfg.C, cfg.mask_ld(), window=cfg.window)
     window = 0 if mask is not None else cfg.window
-    nb = cp.attn_workspace_bytes(cache, q, k, v, mask=mask, window=window)
-    assert nb > 0  # the planner splits these keys
-    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    flags = {"auto": 0, "four": cp.ATTN_SPLITS(4), "none": cp.ATTN_NO_SPLIT}[split]
+    nb = cp.attn_workspace_bytes(cache, q, k, v, mask=mask, window=window, flags=flags)
+    assert (nb > 0) == (split != "none")
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
     sel = torch.zeros((cfg.B, cfg.H, cfg.D), dtype=q.dtype, device="cuda")
     outs = []
     for _ in range(3):
         outs.append(cp.attn_chunk_with_past(cache, q, k, v, n_valid=nv, mask=mask, window=window,
-                                            scale=cfg.scale, workspace=ws, select_out=sel))
+                                            scale=cfg.scale, workspace=ws, select_out=sel,
+                                            flags=flags))
     torch.cuda.synchronize()
     ref = _oracle(cfg, t)
     _check(cfg, outs[0], ref)

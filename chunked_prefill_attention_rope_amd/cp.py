@@ -19,7 +19,7 @@ OK, ERR_ARG, ERR_SHAPE, ERR_DTYPE, ERR_WINDOW, ERR_STATE, ERR_WORKSPACE, ERR_HIP
     0, -1, -2, -3, -4, -5, -6, -7)
 DEV_OVERFLOW, DEV_NVALID, DEV_MASK_LD, DEV_ROLLBACK, DEV_SEEN = 1, 2, 4, 8, 16
 F32, BF16 = 0, 1
-ATTN_NO_SPLIT, ATTN_FORCE_GENERIC, ATTN_FULL_TILES = 1, 2, 4
+ATTN_NO_SPLIT, ATTN_FORCE_GENERIC, ATTN_FULL_TILES, ATTN_ADVANCE_SEEN = 1, 2, 4, 8
 
 
 def ATTN_SPLITS(n: int) -> int:
@@ -65,6 +65,9 @@ _SIGS = {
     "cp_rope_chunk": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "cp_rope_qk_chunk": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "cp_kv_append": (_i, [_P(CacheDesc), _vp, _vp, _i, _vp, _vp]),
+    "cp_kv_advance": (_i, [_P(CacheDesc), _i, _vp, _vp]),
+    "cp_rope_qk_append_chunk": (_i, [_P(CacheDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i,
+                                     _i, _vp, _vp]),
     "cp_snapshot_bytes": (ctypes.c_size_t, [_P(CacheDesc), _i]),
     "cp_kv_snapshot_padded_append": (_i, [_P(CacheDesc), _i, _vp, _P(SnapshotDesc), _vp]),
     "cp_kv_rollback_padded_append": (_i, [_P(CacheDesc), _P(SnapshotDesc), _vp]),
@@ -207,6 +210,37 @@ class KVCache:
     @property
     def D(self):
         return self.desc.D
+
+
+def rope_qk_append_chunk(cache: KVCache, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         cos: torch.Tensor, sin: torch.Tensor,
+                         n_valid: Optional[torch.Tensor] = None,
+                         q_out: Optional[torch.Tensor] = None,
+                         k_out: Optional[torch.Tensor] = None):
+    """cp_rope_qk_append_chunk: rotate q and k, and write rows [0, n_valid[b]) of the
+    rotated k and of v past seen in a global cache (seen is not advanced)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != cache.k.dtype or t.shape[0] != cache.B or t.shape[3] != cache.k.shape[3]:
+            raise ValueError(f"{name} must be [B, heads, C, D] in the cache's dtype")
+    if k.shape != v.shape or k.shape[1] != cache.k.shape[1]:
+        raise ValueError("k and v must be [B, nKV, C, D]")
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    if k_out is None:
+        k_out = torch.empty_like(k)
+    C = k.shape[2]
+    _check(_lib.cp_rope_qk_append_chunk(
+        ctypes.byref(cache.desc), _dev(q, "q"), _dev(q_out, "q_out"), _dev(k, "k"),
+        _dev(k_out, "k_out"), _dev(v, "v"), _opt(cos, "cos", torch.float32),
+        _opt(sin, "sin", torch.float32), q.shape[1], C, cos.shape[0],
+        _opt(n_valid, "n_valid", torch.int32), _stream()), "cp_rope_qk_append_chunk")
+    return q_out, k_out
+
+
+def kv_advance(cache: KVCache, C: int, n_rows: Optional[torch.Tensor] = None) -> None:
+    """cp_kv_advance: seen[b] += n_rows[b] (C when None), as cp_kv_append would."""
+    _check(_lib.cp_kv_advance(ctypes.byref(cache.desc), C, _opt(n_rows, "n_rows", torch.int32),
+                              _stream()), "cp_kv_advance")
 
 
 def kv_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor,

@@ -33,6 +33,8 @@ struct AttnParams {
   int mask_vec4;  // explicit mask rows may be read 16 bytes at a time
   int small_rows; // matrix-core kernel: 0, the 64-row configuration (1) or its deep ring (2)
   float sl2e;     // scale * log2(e)
+  int advance;    // the split merge also advances cache.seen by n_valid (early append)
+  cp_cache cache; // the cache the call reads (for advance)
 };
 
 // Ordered list of the key tiles one query tile needs.  Past tiles cover

@@ -336,6 +336,13 @@ __global__ void __launch_bounds__(256) k_attn_combine(AttnParams p, int D) {
       for (int e = 0; e < VEC; ++e) st(S, e, res[e]);
     }
   }
+  // Early-appended chunk: advance seen.  Every attention workgroup read seen before this
+  // kernel started, and the merge itself never reads it.
+  if (p.advance && blockIdx.x == 0)
+    for (int b = threadIdx.x; b < p.B; b += blockDim.x) {
+      const AppendPlan a = append_plan(p.cache, p.n_valid, b, p.C, false);
+      if (!a.skip) p.cache.seen[b] = a.s0 + a.n;
+    }
 }
 
 template <typename T, bool EXPLICIT>

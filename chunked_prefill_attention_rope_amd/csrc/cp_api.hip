@@ -146,6 +146,9 @@ hipError_t launch_attention(const cp_cache &c, const cp_attn_args &a, hipStream_
                 a.mask_batch_stride % 4 == 0;
   p.sl2e = a.scale * kLog2e;
   p.small_rows = pl.small_rows;
+  p.cache = c;
+  const bool advance = (a.flags & CP_ATTN_ADVANCE_SEEN) != 0;
+  p.advance = advance && pl.splits > 1 ? 1 : 0;
   if (pl.splits > 1) {
     const size_t rows = static_cast<size_t>(c.B) * a.H * a.C;
     unsigned char *w = static_cast<unsigned char *>(a.workspace);
@@ -153,7 +156,8 @@ hipError_t launch_attention(const cp_cache &c, const cp_attn_args &a, hipStream_
     p.wml = reinterpret_cast<float *>(
         w + round256(static_cast<size_t>(pl.splits) * rows * c.D * sizeof(float)));
   }
-  if (static_cast<size_t>(c.B) * a.H * a.C == 0) return hipSuccess;
+  if (static_cast<size_t>(c.B) * a.H * a.C == 0)
+    return advance ? launch_advance_seen(c, a.C, a.n_valid, s) : hipSuccess;
   hipError_t e;
   if (pl.mfma) {
     p.hb = p.G;
@@ -164,8 +168,9 @@ hipError_t launch_attention(const cp_cache &c, const cp_attn_args &a, hipStream_
     p.hgroups = (p.G + p.hb - 1) / p.hb;
     e = launch_attn_valu(p, c.D, c.dtype, s);
   }
-  if (e != hipSuccess || pl.splits == 1) return e;
-  return launch_attn_combine(p, c.D, c.dtype, s);
+  if (e != hipSuccess) return e;
+  if (pl.splits == 1) return advance ? launch_advance_seen(c, a.C, a.n_valid, s) : e;
+  return launch_attn_combine(p, c.D, c.dtype, s);  // also advances seen when asked
 }
 
 }  // namespace cp
@@ -240,6 +245,30 @@ int cp_rope_qk_chunk(const void *q, void *q_out, const void *k, void *k_out, con
                                  static_cast<hipStream_t>(stream)));
   return to_status(launch_rope2(q, q_out, H, k, k_out, has_k ? nKV : 0, cos, sin, B, C, D, Bt,
                                 dtype, static_cast<hipStream_t>(stream)));
+}
+
+int cp_rope_qk_append_chunk(const cp_cache *cache, const void *q, void *q_out, const void *k,
+                            void *k_out, const void *v, const float *cos, const float *sin, int H,
+                            int C, int Bt, const int32_t *n_valid, cp_stream_t stream) {
+  int st = check_cache(cache);
+  if (st != CP_OK) return st;
+  if (cache->ring) return CP_ERR_ARG;  // a ring append may evict rows the attention reads
+  if (H < 0 || C < 0) return CP_ERR_ARG;
+  if (cache->D % 2 != 0 || C > cache->cap) return CP_ERR_SHAPE;
+  if (Bt != 1 && Bt != cache->B) return CP_ERR_ARG;
+  if (static_cast<size_t>(cache->B) * C == 0) return CP_OK;  // empty: pointers may be NULL
+  if (!k || !k_out || !v || !cos || !sin || (H > 0 && (!q || !q_out))) return CP_ERR_ARG;
+  return to_status(launch_rope_qk_append(*cache, q, q_out, H, k, k_out, v, cos, sin, C, Bt,
+                                         n_valid, static_cast<hipStream_t>(stream)));
+}
+
+int cp_kv_advance(const cp_cache *cache, int C, const int32_t *n_rows, cp_stream_t stream) {
+  int st = check_cache(cache);
+  if (st != CP_OK) return st;
+  if (C < 0) return CP_ERR_ARG;
+  if (!cache->ring && C > cache->cap) return CP_ERR_SHAPE;
+  if (C == 0 || cache->B == 0) return CP_OK;
+  return to_status(launch_advance_seen(*cache, C, n_rows, static_cast<hipStream_t>(stream)));
 }
 
 int cp_kv_append(const cp_cache *cache, const void *k_new, const void *v_new, int C,

@@ -81,6 +81,30 @@ __device__ __forceinline__ int read_nvalid(const int32_t *n_valid, int b, int C,
   return nv;
 }
 
+// Where a C-row append lands (device-side checks): rows [0, n) at positions s0..;
+// a sequence with a bad seen, or a global sequence that would overflow, is skipped.
+struct AppendPlan {
+  int s0;     // seen before
+  int n;      // rows appended
+  bool skip;  // sequence not appended (overflow / bad seen)
+};
+
+__device__ __forceinline__ AppendPlan append_plan(const cp_cache &c, const int32_t *n_rows, int b,
+                                                  int C, bool report) {
+  AppendPlan a;
+  a.s0 = c.seen[b];
+  a.n = read_nvalid(n_rows, b, C, report ? c.status : nullptr);
+  a.skip = false;
+  if (a.s0 < 0 || (!c.ring && a.s0 > c.cap)) {
+    a.skip = true;
+    if (report) flag(c.status, CP_DEV_SEEN);
+  } else if (!c.ring && a.s0 + a.n > c.cap) {
+    a.skip = true;
+    if (report) flag(c.status, CP_DEV_OVERFLOW);
+  }
+  return a;
+}
+
 // --------------------------------------------------------- host launchers
 
 size_t gdn_workspace_bytes(int B, int H, int P, int dk, int dv);
@@ -95,6 +119,11 @@ hipError_t launch_rope(const void *x, void *y, const float *cos, const float *si
 hipError_t launch_rope2(const void *x0, void *y0, int H0, const void *x1, void *y1, int H1,
                         const float *cos, const float *sin, int B, int C, int D, int Bt, int dtype,
                         hipStream_t s);
+hipError_t launch_rope_qk_append(const cp_cache &c, const void *q, void *q_out, int H,
+                                 const void *k, void *k_out, const void *v, const float *cos,
+                                 const float *sin, int C, int Bt, const int32_t *n_valid,
+                                 hipStream_t s);
+hipError_t launch_advance_seen(const cp_cache &c, int C, const int32_t *n_rows, hipStream_t s);
 hipError_t launch_kv_append(const cp_cache &c, const void *k_new, const void *v_new, int C,
                             const int32_t *n_rows, hipStream_t s);
 hipError_t launch_snapshot(const cp_cache &c, int C, const int32_t *n_valid, void *buf,

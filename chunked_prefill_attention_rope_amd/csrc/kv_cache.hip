@@ -26,29 +26,6 @@ struct alignas(16) Chunk16 {
   uint32_t w[4];
 };
 
-// Which rows of a C-row append survive in the cache (device-side checks).
-struct AppendPlan {
-  int s0;     // seen before
-  int n;      // rows appended
-  bool skip;  // sequence not appended (overflow / bad seen)
-};
-
-__device__ __forceinline__ AppendPlan append_plan(const cp_cache &c, const int32_t *n_rows, int b,
-                                                  int C, bool report) {
-  AppendPlan a;
-  a.s0 = c.seen[b];
-  a.n = read_nvalid(n_rows, b, C, report ? c.status : nullptr);
-  a.skip = false;
-  if (a.s0 < 0 || (!c.ring && a.s0 > c.cap)) {
-    a.skip = true;
-    if (report) flag(c.status, CP_DEV_SEEN);
-  } else if (!c.ring && a.s0 + a.n > c.cap) {
-    a.skip = true;
-    if (report) flag(c.status, CP_DEV_OVERFLOW);
-  }
-  return a;
-}
-
 // Copy kernel of an append.  Row r of sequence b goes to position s0 + r; in
 // a ring only rows that are still live after the whole append are written
 // (an append longer than the window would otherwise write one slot twice).
@@ -341,6 +318,12 @@ static bool fits32(const cp_cache &c, int C, size_t row_bytes) {
     else                                                                            \
       hipLaunchKernelGGL((K<W, size_t>), dim3(grid), dim3(256), 0, s, __VA_ARGS__);   \
   } while (0)
+
+hipError_t launch_advance_seen(const cp_cache &c, int C, const int32_t *n_rows, hipStream_t s) {
+  if (c.B == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_append_seen, dim3((c.B + 255) / 256), dim3(256), 0, s, c, n_rows, C);
+  return hipGetLastError();
+}
 
 hipError_t launch_kv_append(const cp_cache &c, const void *k_new, const void *v_new, int C,
                             const int32_t *n_rows, hipStream_t s) {

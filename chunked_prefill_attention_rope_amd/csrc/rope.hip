@@ -54,6 +54,19 @@ struct RopeOp {
   int Hx;
 };
 
+// Early append of the second tensor (the keys) into a global cache: the rotated rows,
+// and the same slices of the chunk's value rows, go to slots seen[b] + i for the real
+// rows i < n_valid[b] -- slots the attention of this chunk never reads, since it reads
+// the past below seen and the chunk's own rows from the chunk tensors.  seen is not
+// advanced here.  kc == nullptr: no append.
+template <typename T>
+struct EarlyAppend {
+  cp_cache c;
+  T *kc, *vc;
+  const T *v;
+  const int32_t *n_valid;
+};
+
 // One thread: VEC consecutive pairs (j .. j+VEC-1, j+h2 .. j+h2+VEC-1) of a row,
 // moved with vector loads/stores (VEC > 1 needs 16-byte aligned rows and tables).
 // x and y may alias: every element is read and written by the same thread.  The grid
@@ -62,7 +75,7 @@ struct RopeOp {
 // I: index type -- 32-bit whenever the launch's element count allows (integer division
 // is a software sequence, and a 64-bit one several times longer).
 template <typename T, int VEC, typename I>
-__global__ void __launch_bounds__(128) k_rope(RopeOp<T> a, RopeOp<T> bop,
+__global__ void __launch_bounds__(128) k_rope(RopeOp<T> a, RopeOp<T> bop, EarlyAppend<T> app,
                                               const float *__restrict__ cosb,
                                               const float *__restrict__ sinb, int B, int C, int D,
                                               int Bt) {
@@ -98,6 +111,19 @@ __global__ void __launch_bounds__(128) k_rope(RopeOp<T> a, RopeOp<T> bop,
     }
     *reinterpret_cast<Pack<T, VEC> *>(op.y + xo + j0) = ylo;
     *reinterpret_cast<Pack<T, VEC> *>(op.y + xo + j0 + h2) = yhi;
+    if (second && app.kc) {
+      const int g = static_cast<int>(bh - static_cast<I>(b) * op.Hx);
+      const AppendPlan pl = append_plan(app.c, app.n_valid, b, C, g == 0 && i == 0 && j0 == 0);
+      if (!pl.skip && i < pl.n) {
+        const size_t dst = ((static_cast<size_t>(b) * op.Hx + g) * app.c.cap + pl.s0 + i) * D;
+        *reinterpret_cast<Pack<T, VEC> *>(app.kc + dst + j0) = ylo;
+        *reinterpret_cast<Pack<T, VEC> *>(app.kc + dst + j0 + h2) = yhi;
+        *reinterpret_cast<Pack<T, VEC> *>(app.vc + dst + j0) =
+            *reinterpret_cast<const Pack<T, VEC> *>(app.v + xo + j0);
+        *reinterpret_cast<Pack<T, VEC> *>(app.vc + dst + j0 + h2) =
+            *reinterpret_cast<const Pack<T, VEC> *>(app.v + xo + j0 + h2);
+      }
+    }
   }
 }
 
@@ -106,7 +132,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 template <typename T>
 hipError_t launch_t(const void *x0, void *y0, int H0, const void *x1, void *y1, int H1,
                     const float *cos, const float *sin, int B, int C, int D, int Bt,
-                    hipStream_t s) {
+                    hipStream_t s, const EarlyAppend<T> &app = EarlyAppend<T>{}) {
   const int h2 = D / 2;
   const size_t rows = static_cast<size_t>(B) * (H0 + H1) * C;
   if (rows == 0) return hipSuccess;
@@ -121,21 +147,22 @@ hipError_t launch_t(const void *x0, void *y0, int H0, const void *x1, void *y1, 
   constexpr int V16 = 16 / sizeof(T);  // elements per 16 bytes
   bool al = aligned16(x0) && aligned16(y0) && aligned16(cos) && aligned16(sin);
   if (H1 > 0) al = al && aligned16(x1) && aligned16(y1);
+  if (app.kc) al = al && aligned16(app.kc) && aligned16(app.vc) && aligned16(app.v);
   const bool i32 = rows * h2 < (size_t(1) << 31);
   if (al && h2 % V16 == 0) {
     if (i32)
       hipLaunchKernelGGL((k_rope<T, V16, uint32_t>), dim3(grid_for(V16)), dim3(128), 0, s, a, b,
-                         cos, sin, B, C, D, Bt);
+                         app, cos, sin, B, C, D, Bt);
     else
       hipLaunchKernelGGL((k_rope<T, V16, size_t>), dim3(grid_for(V16)), dim3(128), 0, s, a, b,
-                         cos, sin, B, C, D, Bt);
+                         app, cos, sin, B, C, D, Bt);
   } else {
     if (i32)
-      hipLaunchKernelGGL((k_rope<T, 1, uint32_t>), dim3(grid_for(1)), dim3(128), 0, s, a, b, cos,
-                         sin, B, C, D, Bt);
+      hipLaunchKernelGGL((k_rope<T, 1, uint32_t>), dim3(grid_for(1)), dim3(128), 0, s, a, b, app,
+                         cos, sin, B, C, D, Bt);
     else
-      hipLaunchKernelGGL((k_rope<T, 1, size_t>), dim3(grid_for(1)), dim3(128), 0, s, a, b, cos,
-                         sin, B, C, D, Bt);
+      hipLaunchKernelGGL((k_rope<T, 1, size_t>), dim3(grid_for(1)), dim3(128), 0, s, a, b, app,
+                         cos, sin, B, C, D, Bt);
   }
   return hipGetLastError();
 }
@@ -145,6 +172,20 @@ hipError_t launch_t(const void *x0, void *y0, int H0, const void *x1, void *y1, 
 hipError_t launch_rope(const void *x, void *y, const float *cos, const float *sin, int B, int Hx,
                        int C, int D, int Bt, int dtype, hipStream_t s) {
   return launch_rope2(x, y, Hx, nullptr, nullptr, 0, cos, sin, B, C, D, Bt, dtype, s);
+}
+
+hipError_t launch_rope_qk_append(const cp_cache &c, const void *q, void *q_out, int H,
+                                 const void *k, void *k_out, const void *v, const float *cos,
+                                 const float *sin, int C, int Bt, const int32_t *n_valid,
+                                 hipStream_t s) {
+  if (c.dtype == CP_BF16) {
+    const EarlyAppend<uint16_t> app{c, static_cast<uint16_t *>(c.k), static_cast<uint16_t *>(c.v),
+                                    static_cast<const uint16_t *>(v), n_valid};
+    return launch_t<uint16_t>(q, q_out, H, k, k_out, c.nKV, cos, sin, c.B, C, c.D, Bt, s, app);
+  }
+  const EarlyAppend<float> app{c, static_cast<float *>(c.k), static_cast<float *>(c.v),
+                               static_cast<const float *>(v), n_valid};
+  return launch_t<float>(q, q_out, H, k, k_out, c.nKV, cos, sin, c.B, C, c.D, Bt, s, app);
 }
 
 hipError_t launch_rope2(const void *x0, void *y0, int H0, const void *x1, void *y1, int H1,

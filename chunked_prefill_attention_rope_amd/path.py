@@ -59,7 +59,20 @@ def make_buffers(cache: cp.KVCache, q: torch.Tensor, k: torch.Tensor, v: torch.T
 def chunk_step(cache: cp.KVCache, q, k, v, cos, sin, n_valid, bufs: StepBuffers,
                mask: Optional[torch.Tensor] = None, window: int = 0,
                static_append: bool = False, flags: int = 0):
-    """Run the whole hot path of one layer for one chunk; returns (out, selected row)."""
+    """Run the whole hot path of one layer for one chunk; returns (out, selected row).
+
+    A global cache takes the fused form: the RoPE launch also writes the chunk's K/V
+    rows past seen (slots this chunk's attention does not read), and the attention call
+    advances seen afterwards -- the same cache bytes and outputs as RoPE, attention,
+    append in sequence, without the append's launches.  A ring cache (whose append
+    evicts rows the attention still reads) keeps that sequence."""
+    if not cache.ring and not static_append:
+        cp.rope_qk_append_chunk(cache, q, k, v, cos, sin, n_valid, q_out=bufs.q_rot,
+                                k_out=bufs.k_rot)
+        cp.attn_chunk_with_past(cache, bufs.q_rot, bufs.k_rot, v, n_valid=n_valid, mask=mask,
+                                window=window, out=bufs.out, workspace=bufs.workspace,
+                                flags=flags | cp.ATTN_ADVANCE_SEEN, select_out=bufs.sel)
+        return bufs.out, bufs.sel
     cp.rope_qk_chunk(q, k, cos, sin, q_out=bufs.q_rot, k_out=bufs.k_rot)
     if static_append:
         cp.kv_snapshot_padded_append(cache, q.shape[2], n_valid, bufs.snap)

@@ -9,7 +9,10 @@
  *   -> cp_select_row
  *
  * or, with fewer launches, cp_rope_qk_chunk -> [snapshot] -> cp_attn_chunk_with_past
- * with select_out set -> cp_kv_append -> [rollback].
+ * with select_out set -> cp_kv_append -> [rollback];
+ * or, for a global cache, cp_rope_qk_append_chunk (which also writes the chunk's
+ * K/V rows past seen) -> cp_attn_chunk_with_past with CP_ATTN_ADVANCE_SEEN and
+ * select_out set: two calls, two to three launches.
  *
  * Sources:
  *   [SKaiNET] SKaiNET-transformers PR #417, "functiongemma: chunk prefill-with-
@@ -195,6 +198,10 @@ typedef struct cp_attn_args {
 /* Force the number of key splits to n (1..64; needs the workspace for n) instead of
    the planner's choice.  Placed in bits 8..15 of flags. */
 #define CP_ATTN_SPLITS(n) (((uint32_t)(n) & 0xffu) << 8)
+/* After reading the cache, advance seen[b] by n_valid[b] as cp_kv_advance does (for a
+   chunk whose rows cp_rope_qk_append_chunk already wrote): inside the split merge when
+   the keys are split, else by one small launch after the attention. */
+#define CP_ATTN_ADVANCE_SEEN 8u
 
 /* ---- introspection ---- */
 
@@ -237,6 +244,25 @@ int cp_rope_qk_chunk(const void *q, void *q_out, const void *k, void *k_out, con
                      const float *sin, int B, int H, int nKV, int C, int D, int Bt, int dtype,
                      cp_stream_t stream);
 
+/*
+ * cp_rope_qk_chunk plus the append of the chunk into a GLOBAL cache, in one launch:
+ * q -> q_out [B, H, C, D], k -> k_out [B, nKV, C, D] (B, nKV, D, dtype from the
+ * cache), and rows [0, n_valid[b]) of k_out and of v [B, nKV, C, D] are written to
+ * slots seen[b], seen[b] + 1, ... -- bytes identical to cp_kv_append(k_out, v).
+ * seen is NOT advanced: the attention of the same chunk reads the past below seen
+ * and the chunk's rows from k_out / v, so it never sees these slots; advance seen
+ * afterwards with CP_ATTN_ADVANCE_SEEN on the attention call, or cp_kv_advance.
+ * n_valid NULL appends all C rows.  Same device checks as cp_kv_append
+ * (CP_DEV_OVERFLOW, CP_DEV_SEEN, CP_DEV_NVALID); a skipped sequence is also
+ * skipped by the advance.
+ * Errors: CP_ERR_ARG (ring cache: a ring append may evict rows the attention
+ *         reads; null, negative sizes, Bt not 1 or B), CP_ERR_SHAPE (D odd,
+ *         C > cap), CP_ERR_DTYPE.
+ */
+int cp_rope_qk_append_chunk(const cp_cache *cache, const void *q, void *q_out, const void *k,
+                            void *k_out, const void *v, const float *cos, const float *sin, int H,
+                            int C, int Bt, const int32_t *n_valid, cp_stream_t stream);
+
 /* ---- KV cache ---- */
 
 /*
@@ -253,6 +279,14 @@ int cp_rope_qk_chunk(const void *q, void *q_out, const void *k, void *k_out, con
  */
 int cp_kv_append(const cp_cache *cache, const void *k_new, const void *v_new, int C,
                  const int32_t *n_rows, cp_stream_t stream);
+
+/*
+ * The seen update of cp_kv_append alone: seen[b] += n_rows[b] (all C rows for
+ * NULL), skipping the sequences cp_kv_append would skip, without setting
+ * status bits (cp_rope_qk_append_chunk reported them when it wrote the rows).
+ * Errors: as cp_kv_append.
+ */
+int cp_kv_advance(const cp_cache *cache, int C, const int32_t *n_rows, cp_stream_t stream);
 
 /* Bytes a snapshot of a C-row padded append of `cache` needs (0 on bad args). */
 size_t cp_snapshot_bytes(const cp_cache *cache, int C);

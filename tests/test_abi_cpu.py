@@ -190,3 +190,24 @@ def test_gdn_validation(cp):
     assert call(q=FAKE + 4) == cp.ERR_ARG  # not 16-byte aligned
     assert call(wsb=ws - 1) == cp.ERR_WORKSPACE
     assert call(P=0, q=None, ws=None) == cp.OK  # empty prompt: nothing is read
+
+
+def test_rope_qk_append_and_advance_validation(cp):
+    lib = cp.raw()
+    f = lib.cp_rope_qk_append_chunk
+    c = _cache(cp)
+    call = lambda cache=c, **kw: f(ctypes.byref(cache), *[kw.get(n, FAKE) for n in
+                                   ("q", "q_out", "k", "k_out", "v", "cos", "sin")],
+                                   kw.get("H", 8), kw.get("C", 16), kw.get("Bt", 1), None, None)
+    assert call(cache=_cache(cp, ring=1)) == cp.ERR_ARG  # ring appends evict
+    assert call(cache=_cache(cp, D=63)) == cp.ERR_SHAPE
+    assert call(C=10 ** 6) == cp.ERR_SHAPE
+    assert call(Bt=3) == cp.ERR_ARG
+    assert call(k=None) == cp.ERR_ARG
+    assert call(v=None) == cp.ERR_ARG
+    assert call(H=-1) == cp.ERR_ARG
+    assert call(C=0, k=None, v=None) == cp.OK
+    g = lib.cp_kv_advance
+    assert g(ctypes.byref(c), -1, None, None) == cp.ERR_ARG
+    assert g(ctypes.byref(c), 10 ** 6, None, None) == cp.ERR_SHAPE
+    assert g(ctypes.byref(c), 0, None, None) == cp.OK

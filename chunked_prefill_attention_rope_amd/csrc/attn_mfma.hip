@@ -224,14 +224,19 @@ struct Cfg<256, true> {
 //  CU than four shallow workgroups keep; short splits prefer more workgroups.
 template <int D, bool EX, int SM>
 struct Sel : Cfg<D, EX> {};
+//  At D = 256 the explicit-mask and deep-ring forms need more than the 256 registers
+//  of two waves per SIMD (about 310-340), so they are declared one wave per SIMD: the
+//  split planner then counts one workgroup per CU for them, as the hardware runs them.
 template <int D, bool EX>
 struct Sel<D, EX, 1> {
-  static constexpr int KT = 32, STAGES = 2, WAVES = 2, DSPLIT = Cfg<D, EX>::DSPLIT;
+  static constexpr int KT = 32, STAGES = 2, WAVES = D == 256 && EX ? 1 : 2,
+                       DSPLIT = Cfg<D, EX>::DSPLIT;
   static constexpr int ROWW = 2;
 };
 template <int D, bool EX>
 struct Sel<D, EX, 2> : Sel<D, EX, 1> {
   static constexpr int STAGES = EX ? 2 : 3;
+  static constexpr int WAVES = D == 256 ? 1 : 2;
 };
 
 // One wave-wide 4-byte direct-to-LDS load (mask blocks: no alignment beyond 4 bytes).

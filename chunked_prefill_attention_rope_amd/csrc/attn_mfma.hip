@@ -90,10 +90,25 @@ __device__ __forceinline__ uint32_t lds_addr(const void *ptr) {
 // ds_read_b64_tr_b16 issued as inline asm: the builtin makes the compiler drain all
 // in-flight direct-to-LDS loads before it, which would serialise the K/V ring.  The
 // result registers are only valid after lds_wait() below has been passed through them.
-__device__ __forceinline__ u32x2 tr_read(uint32_t addr) {
+// The constant byte offset OFF rides in the instruction's 16-bit offset field instead
+// of costing an address add.
+template <int OFF>
+__device__ __forceinline__ u32x2 tr_read_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "DS offset field is 16 bits");
   u32x2 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
   return r;
+}
+
+// Transpose reads of rows 16t and 16t + 8 (t = T .. NPT-1) of a V tile with D
+// columns, as consecutive operand pairs.
+template <int D, int T, int NPT>
+__device__ __forceinline__ void tr_read_rows(uint32_t va, u32x2 *w) {
+  if constexpr (T < NPT) {
+    w[2 * T] = tr_read_at<2 * (16 * T * D)>(va);
+    w[2 * T + 1] = tr_read_at<2 * ((16 * T + 8) * D)>(va);
+    tr_read_rows<D, T + 1, NPT>(va, w);
+  }
 }
 
 // Lanes l and l ^ 32 hold the two halves of one query row's keys: combine them with
@@ -522,11 +537,7 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
   // V^T operand reads of one 32-dim block (2 * NPT transpose reads)
   auto v_reads = [&](uint32_t vbase, int db, u32x2 *w) __attribute__((always_inline)) {
     const uint32_t va = vbase + 2 * ((((4 * (dgrp * NDW + db) + v_cl) ^ v_sw) << 3) + v_el);
-#pragma unroll
-    for (int t = 0; t < NPT; ++t) {
-      w[2 * t] = tr_read(va + 2 * (16 * t * D));
-      w[2 * t + 1] = tr_read(va + 2 * ((16 * t + 8) * D));
-    }
+    tr_read_rows<D, 0, NPT>(va, w);
   };
 
   // tile u lives in stage u % STAGES of a ring of (K, V) tiles (a key split starts

@@ -111,6 +111,36 @@ __device__ __forceinline__ void tr_read_rows(uint32_t va, u32x2 *w) {
   }
 }
 
+// K operand read: 16 bytes at a constant byte offset OFF from addr, issued as inline
+// asm for the same reason as the transpose reads (the compiler would otherwise wait for
+// every LDS read before the MFMA right after it, exposing the full LDS latency on each
+// k-step); its results are valid only after k_wait() has been passed through them.
+template <int OFF>
+__device__ __forceinline__ u32x4 k_read_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "DS offset field is 16 bits");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+// the K fragments of key blocks KB .. NKB-1 (32 rows of D bf16 apart) at one k-step
+template <int D, int KB, int NKB>
+__device__ __forceinline__ void k_read_blocks(uint32_t addr, u32x4 *f) {
+  if constexpr (KB < NKB) {
+    f[KB] = k_read_at<2 * 32 * KB * D>(addr);
+    k_read_blocks<D, KB + 1, NKB>(addr, f);
+  }
+}
+// s_waitcnt lgkmcnt(N) that marks the NKB fragments f[] as written by it; the N LDS
+// reads issued after them may stay in flight
+template <int N, int NKB>
+__device__ __forceinline__ void k_wait(u32x4 *f) {
+  static_assert(N >= 0 && N < 16 && (NKB == 1 || NKB == 2), "lgkmcnt range");
+  if constexpr (NKB == 1)
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(f[0]) : "i"(N));
+  else
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(f[0]), "+v"(f[1]) : "i"(N));
+}
+
 // Lanes l and l ^ 32 hold the two halves of one query row's keys: combine them with
 // one v_permlane32_swap (no LDS round trip).  Both lanes get the same value.
 __device__ __forceinline__ float pair_max(float v) {
@@ -499,9 +529,9 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
       const int q = wave * NL + e;
       const size_t r = static_cast<size_t>(srow[e]) * D;
       if (j < NL)
-        dma16((chunk ? KN : KC) + r + koff[e], st + q * 512);
+        dma16((chunk ? KN + r : KC + r) + koff[e], st + q * 512);
       else
-        dma16((chunk ? VN : VC) + r + voff[e], st + TILE + q * 512);
+        dma16((chunk ? VN + r : VC + r) + voff[e], st + TILE + q * 512);
     } else if constexpr (EXPLICIT) {
       const int jm = j - 2 * NL;
       const int q = wave * NMK + jm;
@@ -540,67 +570,47 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
     tr_read_rows<D, 0, NPT>(va, w);
   };
 
-  // tile u lives in stage u % STAGES of a ring of (K, V) tiles (a key split starts
-  // at u0 > 0)
-  for (int j = 0; j < STAGES - 1; ++j)
-    if (u0 + j < u1) {
-      int srow[NL], f0, l0;
-      const bool ch = plan(u0 + j, srow, f0, l0);
-      uint16_t *st = ring + ((u0 + j) % STAGES) * STAGE;
-#pragma unroll
-      for (int l = 0; l < ND; ++l) dma(l, ch, srow, f0, l0, st);
-    }
-
-  for (int u = u0; u < u1; ++u) {
-    // tile u has landed in this wave's share of the ring once at most the loads of
-    // the tiles issued after it are outstanding; the barrier makes that true for all
-    // waves and also guarantees every wave has finished reading the stage refilled
-    wait_tiles_after<ND, STAGES>(imin(u1 - 1, u + STAGES - 2) - u);
-    __builtin_amdgcn_s_barrier();
-    const uint16_t *Ks = ring + (u % STAGES) * STAGE;
-    const uint16_t *Vs = Ks + TILE;
-
-    // the tile STAGES - 1 ahead is loaded while this one's QK^T runs
-    const int w_pf = u + STAGES - 1;
-    const bool pf = w_pf < u1;
-    int srow[NL], pfirst = 0, plim = 1;
-    bool pch = false;
-#pragma unroll
-    for (int e = 0; e < NL; ++e) srow[e] = 0;
-    if (pf) pch = plan(w_pf, srow, pfirst, plim);
-    uint16_t *pst = ring + (w_pf % STAGES) * STAGE;
-
-    // ---- S^T = K Q^T, K fragments read one k-step ahead, loads spread over the steps
-    f32x16 sacc[NKB];
+  // ---- the pieces of one tile
+  // S^T = K Q^T for the tile in Ks, K fragments read one k-step ahead; hook(s) runs
+  // after k-step s (the caller's direct-to-LDS loads, spread over the steps)
+  auto qk_tile = [&](const uint16_t *Ks, f32x16 *sacc, auto &&hook) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
-    u32x4 kf[2][NKB];
+    // K fragments of KP k-steps in flight; lane: key row 32 kb + n, 16-byte chunk
+    // 2 s + hh of the row, stored at chunk (2 s + hh) ^ k_sw = 2 s ^ (hh ^ k_sw)
+    constexpr int KP = NS < 3 ? NS : 3;
+    const uint32_t kbase = lds_addr(Ks) + 2 * (n * D);
+    const int kx = hh ^ k_sw;
+    u32x4 kf[KP][NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-      kf[0][kb] = *reinterpret_cast<const u32x4 *>(&Ks[(32 * kb + n) * D + ((hh ^ k_sw) << 3)]);
+    for (int s = 0; s + 1 < KP; ++s) k_read_blocks<D, 0, NKB>(kbase + 16 * ((2 * s) ^ kx), kf[s]);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      if (s + 1 < NS) {
-        const int off = ((2 * (s + 1) + hh) ^ k_sw) << 3;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          kf[(s + 1) & 1][kb] = *reinterpret_cast<const u32x4 *>(&Ks[(32 * kb + n) * D + off]);
-      }
+      if (s + KP - 1 < NS)
+        k_read_blocks<D, 0, NKB>(kbase + 16 * ((2 * (s + KP - 1)) ^ kx), kf[(s + KP - 1) % KP]);
+      // reads issued after step s's: those of the steps still ahead
+      const int later = (NS - 1 - s < KP - 1 ? NS - 1 - s : KP - 1) * NKB;
+      u32x4 *cur = kf[s % KP];
+      if (later >= 2 * NKB)
+        k_wait<2 * NKB, NKB>(cur);
+      else if (later >= NKB)
+        k_wait<NKB, NKB>(cur);
+      else
+        k_wait<0, NKB>(cur);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        sacc[kb] = mfma(__builtin_bit_cast(bf16x8, kf[s & 1][kb]), qf[s], sacc[kb]);
-#pragma unroll
-      for (int j = s * ND / NS; j < (s + 1) * ND / NS; ++j)
-        if (pf) dma(j, pch, srow, pfirst, plim, pst);
+        sacc[kb] = mfma(__builtin_bit_cast(bf16x8, cur[kb]), qf[s], sacc[kb]);
+      hook(s);
     }
+  };
 
-    // V^T reads of the first dim block go out before the softmax needs the ALUs
-    const uint32_t vbase = lds_addr(Vs) + 2 * (v_key * D);
-    u32x2 wv[2][2 * NPT];
-    v_reads(vbase, 0, wv[0]);
-
+  // Masking and online softmax of tile u: turns the scores in sacc into the bf16
+  // probabilities pb, rescaling the running output when the row maximum rises.
+  // (Mask blocks, for an explicit mask, are read from the tile's ring stage Ms.)
+  auto softmax_tile = [&](int u, f32x16 *sacc, const float *Mst, bf16x8 *pb)
+                          __attribute__((always_inline)) {
     int first;
     const bool chunk = ts.at(u, KT, &first);
     // ---- tile classification (wave-uniform): does every real row of this wave
@@ -634,7 +644,7 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
       mt *= p.sl2e;
     } else if constexpr (EXPLICIT) {
       // mask block of this stage, row r of this lane; keys past the valid range -inf
-      const float *Ms = reinterpret_cast<const float *>(Ks + 2 * TILE) + r * KT;
+      const float *Ms = Mst + r * KT;
       const int xl = lim - first - 4 * hh;
       const int msw = mswz(r);
 #pragma unroll
@@ -697,8 +707,6 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
     // k = 1 on masked ones (fma(t, 1, -m) rounds exactly as t - m)
     const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
     const float kx = visible ? p.sl2e : 1.f;
-
-    bf16x8 pb[NPT];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -715,9 +723,12 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
         pb[2 * kb + half] = __builtin_bit_cast(bf16x8, w);
       }
     }
+  };
 
-    // ---- O^T += V^T P^T: the reads of dim block db + 1 are in flight while block db
-    // multiplies
+  // O^T += V^T P^T for the V tile at LDS byte address vbase; the reads of dim block 0
+  // are already in wv[0], those of block db + 1 are in flight while block db multiplies
+  auto pv_tile = [&](uint32_t vbase, const bf16x8 *pb, u32x2 (*wv)[2 * NPT])
+                     __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < NDW; ++db) {
       u32x2 *cur = wv[db & 1];
@@ -733,6 +744,52 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
         oacc[db] = mfma(__builtin_bit_cast(bf16x8, a), pb[t], oacc[db]);
       }
     }
+  };
+
+  // tile u lives in stage u % STAGES of a ring of (K, V) tiles (a key split starts
+  // at u0 > 0)
+  for (int j = 0; j < STAGES - 1; ++j)
+    if (u0 + j < u1) {
+      int srow[NL], f0, l0;
+      const bool ch = plan(u0 + j, srow, f0, l0);
+      uint16_t *st = ring + ((u0 + j) % STAGES) * STAGE;
+#pragma unroll
+      for (int l = 0; l < ND; ++l) dma(l, ch, srow, f0, l0, st);
+    }
+
+  for (int u = u0; u < u1; ++u) {
+    // tile u has landed in this wave's share of the ring once at most the loads of
+    // the tiles issued after it are outstanding; the barrier makes that true for all
+    // waves and also guarantees every wave has finished reading the stage refilled
+    wait_tiles_after<ND, STAGES>(imin(u1 - 1, u + STAGES - 2) - u);
+    __builtin_amdgcn_s_barrier();
+    const uint16_t *Ks = ring + (u % STAGES) * STAGE;
+    const uint16_t *Vs = Ks + TILE;
+
+    // the tile STAGES - 1 ahead is loaded while this one's QK^T runs
+    const int w_pf = u + STAGES - 1;
+    const bool pf = w_pf < u1;
+    int srow[NL], pfirst = 0, plim = 1;
+    bool pch = false;
+#pragma unroll
+    for (int e = 0; e < NL; ++e) srow[e] = 0;
+    if (pf) pch = plan(w_pf, srow, pfirst, plim);
+    uint16_t *pst = ring + (w_pf % STAGES) * STAGE;
+
+    f32x16 sacc[NKB];
+    qk_tile(Ks, sacc, [&](int s) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = s * ND / NS; j < (s + 1) * ND / NS; ++j)
+        if (pf) dma(j, pch, srow, pfirst, plim, pst);
+    });
+
+    // V^T reads of the first dim block go out before the softmax needs the ALUs
+    const uint32_t vbase = lds_addr(Vs) + 2 * (v_key * D);
+    u32x2 wv[2][2 * NPT];
+    v_reads(vbase, 0, wv[0]);
+    bf16x8 pb[NPT];
+    softmax_tile(u, sacc, reinterpret_cast<const float *>(Ks + 2 * TILE), pb);
+    pv_tile(vbase, pb, wv);
   }
 
   const float l_tot = pair_sum(l_run);

@@ -260,7 +260,7 @@ __global__ void __launch_bounds__(256) k_attn_valu(AttnParams p, int D) {
 // I: index type (32-bit when the element count allows; see the RoPE kernel).
 template <typename T, int VEC, typename I>
 __global__ void __launch_bounds__(256) k_attn_combine(AttnParams p, int D) {
-  constexpr int SB = 8;
+  constexpr int SB = 16;  // splits fetched per round (one round for up to 16 splits)
   const size_t rows = static_cast<size_t>(p.B) * p.H * p.C;
   const I per_row = D / VEC;
   const I total = static_cast<I>(rows) * per_row;
@@ -273,6 +273,37 @@ __global__ void __launch_bounds__(256) k_attn_combine(AttnParams p, int D) {
     const I bh = row_i / static_cast<I>(p.C);
     const int i = static_cast<int>(row_i - bh * p.C);
     const int b = static_cast<int>(bh / static_cast<I>(p.H));
+    // partials of splits s0 .. s0 + SB - 1 (pad rows have none written: their values
+    // are read but not used)
+    float mv[SB], lv[SB], ov[SB][VEC];
+    auto fetch = [&](int s0) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        mv[j] = -INFINITY;
+        lv[j] = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) ov[j][e] = 0.f;
+        if (s0 + j < p.splits) {
+          const size_t sr = (s0 + j) * rows + row;
+          const float2 ml = *reinterpret_cast<const float2 *>(p.wml + sr * 2);
+          mv[j] = ml.x;
+          lv[j] = ml.y;
+          const float *src = p.wo + sr * D + d0;
+          if constexpr (VEC == 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(src);
+            ov[j][0] = v.x;
+            ov[j][1] = v.y;
+            ov[j][2] = v.z;
+            ov[j][3] = v.w;
+          } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) ov[j][e] = src[e];
+          }
+        }
+      }
+    };
+    // the first round goes out together with the n_valid read, not after it
+    fetch(0);
     const int nv = read_nvalid(p.n_valid, b, p.C, nullptr);
     float res[VEC];
 #pragma unroll
@@ -282,31 +313,7 @@ __global__ void __launch_bounds__(256) k_attn_combine(AttnParams p, int D) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) o[e] = 0.f;
       for (int s0 = 0; s0 < p.splits; s0 += SB) {
-        float mv[SB], lv[SB], ov[SB][VEC];
-#pragma unroll
-        for (int j = 0; j < SB; ++j) {
-          mv[j] = -INFINITY;
-          lv[j] = 0.f;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) ov[j][e] = 0.f;
-          if (s0 + j < p.splits) {
-            const size_t sr = (s0 + j) * rows + row;
-            const float2 ml = *reinterpret_cast<const float2 *>(p.wml + sr * 2);
-            mv[j] = ml.x;
-            lv[j] = ml.y;
-            const float *src = p.wo + sr * D + d0;
-            if constexpr (VEC == 4) {
-              const float4 v = *reinterpret_cast<const float4 *>(src);
-              ov[j][0] = v.x;
-              ov[j][1] = v.y;
-              ov[j][2] = v.z;
-              ov[j][3] = v.w;
-            } else {
-#pragma unroll
-              for (int e = 0; e < VEC; ++e) ov[j][e] = src[e];
-            }
-          }
-        }
+        if (s0 > 0) fetch(s0);
         float Mn = M;
 #pragma unroll
         for (int j = 0; j < SB; ++j) Mn = fmaxf(Mn, mv[j]);

@@ -92,8 +92,14 @@ struct AppendPlan {
 __device__ __forceinline__ AppendPlan append_plan(const cp_cache &c, const int32_t *n_rows, int b,
                                                   int C, bool report) {
   AppendPlan a;
+  // both counters are requested before either is checked (one round trip)
   a.s0 = c.seen[b];
-  a.n = read_nvalid(n_rows, b, C, report ? c.status : nullptr);
+  int n = n_rows ? n_rows[b] : C;
+  if (n < 0 || n > C) {
+    if (report) flag(c.status, CP_DEV_NVALID);
+    n = n < 0 ? 0 : C;
+  }
+  a.n = n;
   a.skip = false;
   if (a.s0 < 0 || (!c.ring && a.s0 > c.cap)) {
     a.skip = true;

@@ -35,6 +35,23 @@ struct alignas(sizeof(T) * N) Pack {
   T v[N];
 };
 
+// A plain register type of B bytes, for rows that are only copied (an aggregate held
+// across other work is kept in memory by the compiler).
+template <int B>
+struct RawOf;
+template <>
+struct RawOf<16> {
+  typedef unsigned type __attribute__((ext_vector_type(4)));
+};
+template <>
+struct RawOf<4> {
+  typedef unsigned type;
+};
+template <>
+struct RawOf<2> {
+  typedef unsigned short type;
+};
+
 __device__ __forceinline__ float rot_lo(float lo, float hi, float c, float s) {
   const double a = static_cast<double>(lo) * static_cast<double>(c);
   const double b = static_cast<double>(hi) * static_cast<double>(s);
@@ -89,19 +106,36 @@ __global__ void __launch_bounds__(128) k_rope(RopeOp<T> a, RopeOp<T> bop, EarlyA
     I row = t / per_row;
     const int j0 = static_cast<int>(t - row * per_row) * VEC;
     const bool second = row >= rows_a;
-    const RopeOp<T> &op = second ? bop : a;
+    // the tensor's fields selected by value (a reference to one of the two argument
+    // structs would make the compiler load the struct through a pointer first)
+    const T *opx = second ? bop.x : a.x;
+    T *opy = second ? bop.y : a.y;
+    const int opH = second ? bop.Hx : a.Hx;
     if (second) row -= rows_a;
     const I bh = row / static_cast<I>(C);
     const int i = static_cast<int>(row - bh * C);
-    const int b = static_cast<int>(bh / static_cast<I>(op.Hx));
+    const int b = static_cast<int>(bh / static_cast<I>(opH));
     const size_t xo = static_cast<size_t>(row) * D;
     const size_t to = (static_cast<size_t>(Bt == 1 ? 0 : b) * C + i) * D;
-    const Pack<T, VEC> lo = *reinterpret_cast<const Pack<T, VEC> *>(op.x + xo + j0);
-    const Pack<T, VEC> hi = *reinterpret_cast<const Pack<T, VEC> *>(op.x + xo + j0 + h2);
+    const Pack<T, VEC> lo = *reinterpret_cast<const Pack<T, VEC> *>(opx + xo + j0);
+    const Pack<T, VEC> hi = *reinterpret_cast<const Pack<T, VEC> *>(opx + xo + j0 + h2);
     const Pack<float, VEC> cl = *reinterpret_cast<const Pack<float, VEC> *>(cosb + to + j0);
     const Pack<float, VEC> sl = *reinterpret_cast<const Pack<float, VEC> *>(sinb + to + j0);
     const Pack<float, VEC> ch = *reinterpret_cast<const Pack<float, VEC> *>(cosb + to + j0 + h2);
     const Pack<float, VEC> sh = *reinterpret_cast<const Pack<float, VEC> *>(sinb + to + j0 + h2);
+    // early append of a K row: the append plan (seen, n_valid) and the V row are read
+    // along with the row itself, not after the rotation (one round trip, not three)
+    // (other rows read their own row again instead: no conditionally filled aggregate)
+    const bool app_row = second && app.kc;
+    using Raw = typename RawOf<sizeof(T) * VEC>::type;
+    const T *vsrc = (app_row ? app.v : opx) + xo;
+    const Raw vlo = *reinterpret_cast<const Raw *>(vsrc + j0);
+    const Raw vhi = *reinterpret_cast<const Raw *>(vsrc + j0 + h2);
+    AppendPlan pl{0, 0, true};
+    if (app_row) {
+      const int g = static_cast<int>(bh - static_cast<I>(b) * opH);
+      pl = append_plan(app.c, app.n_valid, b, C, g == 0 && i == 0 && j0 == 0);
+    }
     Pack<T, VEC> ylo, yhi;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
@@ -109,20 +143,15 @@ __global__ void __launch_bounds__(128) k_rope(RopeOp<T> a, RopeOp<T> bop, EarlyA
       ylo.v[e] = Elem<T>::put(rot_lo(xa, xc, cl.v[e], sl.v[e]));
       yhi.v[e] = Elem<T>::put(rot_hi(xa, xc, ch.v[e], sh.v[e]));
     }
-    *reinterpret_cast<Pack<T, VEC> *>(op.y + xo + j0) = ylo;
-    *reinterpret_cast<Pack<T, VEC> *>(op.y + xo + j0 + h2) = yhi;
-    if (second && app.kc) {
-      const int g = static_cast<int>(bh - static_cast<I>(b) * op.Hx);
-      const AppendPlan pl = append_plan(app.c, app.n_valid, b, C, g == 0 && i == 0 && j0 == 0);
-      if (!pl.skip && i < pl.n) {
-        const size_t dst = ((static_cast<size_t>(b) * op.Hx + g) * app.c.cap + pl.s0 + i) * D;
-        *reinterpret_cast<Pack<T, VEC> *>(app.kc + dst + j0) = ylo;
-        *reinterpret_cast<Pack<T, VEC> *>(app.kc + dst + j0 + h2) = yhi;
-        *reinterpret_cast<Pack<T, VEC> *>(app.vc + dst + j0) =
-            *reinterpret_cast<const Pack<T, VEC> *>(app.v + xo + j0);
-        *reinterpret_cast<Pack<T, VEC> *>(app.vc + dst + j0 + h2) =
-            *reinterpret_cast<const Pack<T, VEC> *>(app.v + xo + j0 + h2);
-      }
+    *reinterpret_cast<Pack<T, VEC> *>(opy + xo + j0) = ylo;
+    *reinterpret_cast<Pack<T, VEC> *>(opy + xo + j0 + h2) = yhi;
+    if (app_row && !pl.skip && i < pl.n) {
+      const int g = static_cast<int>(bh - static_cast<I>(b) * opH);
+      const size_t dst = ((static_cast<size_t>(b) * opH + g) * app.c.cap + pl.s0 + i) * D;
+      *reinterpret_cast<Pack<T, VEC> *>(app.kc + dst + j0) = ylo;
+      *reinterpret_cast<Pack<T, VEC> *>(app.kc + dst + j0 + h2) = yhi;
+      *reinterpret_cast<Raw *>(app.vc + dst + j0) = vlo;
+      *reinterpret_cast<Raw *>(app.vc + dst + j0 + h2) = vhi;
     }
   }
 }

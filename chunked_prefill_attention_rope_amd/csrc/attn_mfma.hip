@@ -409,9 +409,15 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
     }
   }
 
+  // seen and n_valid are both requested before either is used (scalar loads complete
+  // out of order, so the first use waits for every one in flight: one round trip)
   const int seen = p.seen[b];
+  int nv = p.n_valid ? p.n_valid[b] : p.C;
   const bool lead = tid == 0 && qtile == 0 && split == 0 && g == 0;
-  const int nv = read_nvalid(p.n_valid, b, p.C, lead ? p.status : nullptr);
+  if (nv < 0 || nv > p.C) {
+    if (lead) flag(p.status, CP_DEV_NVALID);
+    nv = nv < 0 ? 0 : p.C;
+  }
   bool bad = seen < 0 || (!p.ring && seen > p.cap);
   if (bad && lead) flag(p.status, CP_DEV_SEEN);
   const Live gl = live_geometry(bad ? 0 : seen, p.cap, p.ring, p.sink);
@@ -467,9 +473,12 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
   if (any_real) {
     ts = make_tiles(gl, seen, p.C, KT, i_min, i_last, EXPLICIT ? 0 : p.window, p.sink,
                     EXPLICIT || p.full_tiles);
-    const int cnt = ts.count();
-    u0 = static_cast<int>((static_cast<long>(cnt) * split) / p.splits);
-    u1 = static_cast<int>((static_cast<long>(cnt) * (split + 1)) / p.splits);
+    // near-equal split ranges, the first cnt % splits one tile longer (one 32-bit
+    // division: a 64-bit one is a long software sequence ahead of the first load)
+    const unsigned cnt = static_cast<unsigned>(ts.count()), ns = static_cast<unsigned>(p.splits);
+    const unsigned q = cnt / ns, rm = cnt - q * ns, us = static_cast<unsigned>(split);
+    u0 = static_cast<int>(us * q + (us < rm ? us : rm));
+    u1 = u0 + static_cast<int>(q + (us < rm ? 1u : 0u));
   }
 
   const uint16_t *KC = static_cast<const uint16_t *>(p.kc) +

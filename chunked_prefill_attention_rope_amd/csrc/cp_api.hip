@@ -72,13 +72,15 @@ AttnPlan plan_attention(const cp_cache &c, const cp_attn_args &a, bool for_works
   const long tiles = (keys + pl.kt - 1) / pl.kt;
   const int forced = static_cast<int>((a.flags >> 8) & 0xffu);
   // Few query tiles: split the keys so that more CUs work -- each split writes fp32
-  // partials that a second kernel merges.  The matrix-core kernel keeps >= 3 key tiles
-  // per split (its ~6 us of prologue and first-tile latency is paid per workgroup; 3
-  // measured best on c2-c4); the vector-ALU kernel's 16-key tiles each cost a memory
-  // round trip that their arithmetic does not hide, so it goes down to one tile per
-  // split.  The tile count is a bound from the capacity (the live length is on the
-  // device), so a split can get one tile less than this.
-  const long per = pl.mfma ? 3 : 1;
+  // partials that a second kernel merges.  The matrix-core kernel keeps >= 2 key tiles
+  // per split (its prologue and first-tile latency is paid per workgroup; with the
+  // merge reading all splits in one round, 2 measured best: the 864-key D = 256 chunk
+  // step 18.75 -> 18.50 us, the 640-key ring step 22.05 -> 20.59 us against 3); the
+  // vector-ALU kernel's 16-key tiles each cost a memory round trip that their
+  // arithmetic does not hide, so it goes down to one tile per split.  The tile count is
+  // a bound from the capacity (the live length is on the device), so a split can get
+  // one tile less than this.
+  const long per = pl.mfma ? 2 : 1;
   // as many splits as fill the CUs once (rounded down: a partial second round of
   // workgroups would double the time of the last ones)
   auto split_for = [&](long wg_per_cu) {

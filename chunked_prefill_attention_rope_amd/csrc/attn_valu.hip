@@ -258,9 +258,11 @@ __global__ void __launch_bounds__(256) k_attn_valu(AttnParams p, int D) {
 // and folded into a running maximum, so a row costs ceil(splits / SB) memory round
 // trips instead of one per split.
 // I: index type (32-bit when the element count allows; see the RoPE kernel).
-template <typename T, int VEC, typename I>
+// SB: splits fetched per round -- 32 when there are more than 16 splits (one round
+// for up to 32), else 16 (the narrower kernel keeps more waves resident for merges of
+// many rows).
+template <typename T, int VEC, typename I, int SB>
 __global__ void __launch_bounds__(256) k_attn_combine(AttnParams p, int D) {
-  constexpr int SB = 16;  // splits fetched per round (one round for up to 16 splits)
   const size_t rows = static_cast<size_t>(p.B) * p.H * p.C;
   const I per_row = D / VEC;
   const I total = static_cast<I>(rows) * per_row;
@@ -389,12 +391,22 @@ hipError_t launch_attn_combine(const AttnParams &p, int D, int dtype, hipStream_
   size_t blocks = (total / (v4 ? 4 : 1) + 255) / 256;
   if (blocks > 16384) blocks = 16384;
   const bool i32 = total < (size_t(1) << 31);
-#define CP_COMBINE(T, V)                                                                         \
-  do {                                                                                           \
-    if (i32)                                                                                     \
-      hipLaunchKernelGGL((k_attn_combine<T, V, uint32_t>), dim3(blocks), dim3(256), 0, s, p, D); \
-    else                                                                                         \
-      hipLaunchKernelGGL((k_attn_combine<T, V, size_t>), dim3(blocks), dim3(256), 0, s, p, D);   \
+  const bool wide = p.splits > 16;
+#define CP_COMBINE_SB(T, V, SB)                                                              \
+  do {                                                                                       \
+    if (i32)                                                                                 \
+      hipLaunchKernelGGL((k_attn_combine<T, V, uint32_t, SB>), dim3(blocks), dim3(256), 0, s, \
+                         p, D);                                                              \
+    else                                                                                     \
+      hipLaunchKernelGGL((k_attn_combine<T, V, size_t, SB>), dim3(blocks), dim3(256), 0, s,   \
+                         p, D);                                                              \
+  } while (0)
+#define CP_COMBINE(T, V)          \
+  do {                            \
+    if (wide)                     \
+      CP_COMBINE_SB(T, V, 32);    \
+    else                          \
+      CP_COMBINE_SB(T, V, 16);    \
   } while (0)
   if (dtype == CP_BF16) {
     if (v4)
@@ -408,6 +420,7 @@ hipError_t launch_attn_combine(const AttnParams &p, int D, int dtype, hipStream_
       CP_COMBINE(float, 1);
   }
 #undef CP_COMBINE
+#undef CP_COMBINE_SB
   return hipGetLastError();
 }
 

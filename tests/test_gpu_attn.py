@@ -338,3 +338,32 @@ def test_decode_split_merge(cp, kw, mode, split):
         assert np.array_equal(bits(o), bits(outs[0]))
     assert np.array_equal(bits(sel), bits(cp.select_row(outs[0], nv, -1)))
     assert int(status.item()) == 0
+
+
+@pytest.mark.parametrize("splits", [16, 17, 33, 64])
+@pytest.mark.parametrize("mode", ["inkernel", "explicit"])
+def test_merge_rounds(cp, splits, mode):
+    """Forced key splits on either side of the merge's per-round widths (16 splits per
+    round up to 16, 32 above; 33 and 64 take two rounds): the merged output matches the
+    oracle, repeats bit for bit, and the selection is the merged row.  Some splits of 64
+    get no tile at all (their partials carry an empty maximum)."""
+    cfg = I.small(dtype=I.BF16, B=2, H=8, nKV=2, D=128, C=16, cap=2304, seen=[2100, 700],
+                  n_valid=[16, 9])
+    t, cache, status = _setup(cp, cfg)
+    q, k, v = dev(t["q"]), dev(t["k"]), dev(t["v"])
+    nv = dev(t["n_valid"])
+    mask = None
+    if mode == "explicit":
+        mask = cp.build_mask(cache, nv, cfg.H, cfg.C, cfg.mask_ld(), window=cfg.window)
+    flags = cp.ATTN_SPLITS(splits)
+    nb = cp.attn_workspace_bytes(cache, q, k, v, mask=mask, flags=flags)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    sel = torch.zeros((cfg.B, cfg.H, cfg.D), dtype=q.dtype, device="cuda")
+    outs = [cp.attn_chunk_with_past(cache, q, k, v, n_valid=nv, mask=mask, scale=cfg.scale,
+                                    workspace=ws, select_out=sel, flags=flags)
+            for _ in range(2)]
+    torch.cuda.synchronize()
+    _check(cfg, outs[0], _oracle(cfg, t))
+    assert np.array_equal(bits(outs[1]), bits(outs[0]))
+    assert np.array_equal(bits(sel), bits(cp.select_row(outs[0], nv, -1)))
+    assert int(status.item()) == 0

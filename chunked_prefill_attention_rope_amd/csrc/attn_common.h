@@ -30,7 +30,6 @@ struct AttnParams {
   int qtiles;  // query tiles per (b, kv head, head group)
   int splits;
   int full_tiles;
-  int mask_vec4;  // explicit mask rows may be read 16 bytes at a time
   int small_rows; // matrix-core kernel: 0, the 64-row configuration (1) or its deep ring (2)
   float sl2e;     // scale * log2(e)
   int advance;    // the split merge also advances cache.seen by n_valid (early append)

@@ -144,8 +144,6 @@ hipError_t launch_attention(const cp_cache &c, const cp_attn_args &a, hipStream_
   p.qtiles = pl.qtiles;
   p.splits = pl.splits;
   p.full_tiles = (a.flags & CP_ATTN_FULL_TILES) ? 1 : 0;
-  p.mask_vec4 = a.mask && aligned16(a.mask) && a.mask_ld % 4 == 0 && a.mask_head_stride % 4 == 0 &&
-                a.mask_batch_stride % 4 == 0;
   p.sl2e = a.scale * kLog2e;
   p.small_rows = pl.small_rows;
   p.cache = c;

@@ -46,6 +46,8 @@
 // Pipelining inside a tile: K fragments are read one k-step ahead of the MFMAs,
 // and the V^T transpose reads of dim block db + 1 are in flight while block db
 // multiplies (the reads of block 0 overlap the softmax arithmetic).
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace cp {
@@ -755,9 +757,18 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
     }
   };
 
+  // Staggered stages (in-kernel rule, 8 waves as two per SIMD): waves 4..7 run a tile's
+  // stages as [O update of the previous tile, S, softmax] and waves 0..3 as [S, softmax,
+  // O update], so after each barrier one wave's softmax meets the other's matrix
+  // products on every SIMD.  V of tile u - 1 is then still read after the barrier of
+  // tile u, so the ring loads STAGES - 2 tiles ahead instead of STAGES - 1.
+  constexpr bool STAG = !EXPLICIT && NW == 8 && CF::WAVES == 2 && SM == 0 && STAGES >= 3;
+  constexpr int PD = STAG ? STAGES - 2 : STAGES - 1;  // tiles loaded ahead
+  const bool lagging = STAG && __builtin_amdgcn_readfirstlane(wave) >= 4;
+
   // tile u lives in stage u % STAGES of a ring of (K, V) tiles (a key split starts
   // at u0 > 0)
-  for (int j = 0; j < STAGES - 1; ++j)
+  for (int j = 0; j < PD; ++j)
     if (u0 + j < u1) {
       int srow[NL], f0, l0;
       const bool ch = plan(u0 + j, srow, f0, l0);
@@ -766,40 +777,69 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
       for (int l = 0; l < ND; ++l) dma(l, ch, srow, f0, l0, st);
     }
 
-  for (int u = u0; u < u1; ++u) {
-    // tile u has landed in this wave's share of the ring once at most the loads of
-    // the tiles issued after it are outstanding; the barrier makes that true for all
-    // waves and also guarantees every wave has finished reading the stage refilled
-    wait_tiles_after<ND, STAGES>(imin(u1 - 1, u + STAGES - 2) - u);
-    __builtin_amdgcn_s_barrier();
-    const uint16_t *Ks = ring + (u % STAGES) * STAGE;
-    const uint16_t *Vs = Ks + TILE;
+  // the tile loop, specialized for the leading and the lagging order (one copy each, so
+  // neither carries the other's registers)
+  auto tile_loop = [&](auto lag_tag) __attribute__((always_inline)) {
+    constexpr bool LAG = decltype(lag_tag)::value;
+    bf16x8 pb_lag[NPT];  // LAG waves: probabilities of the tile before
+  #pragma unroll
+    for (int t = 0; t < NPT; ++t) pb_lag[t] = bf16x8{};
+    for (int u = u0; u < u1; ++u) {
+      // tile u has landed in this wave's share of the ring once at most the loads of
+      // the tiles issued after it are outstanding; the barrier makes that true for all
+      // waves and also guarantees every wave has finished reading the stage refilled
+      wait_tiles_after<ND, STAGES>(imin(u1 - 1, u + PD - 1) - u);
+      __builtin_amdgcn_s_barrier();
+      const uint16_t *Ks = ring + (u % STAGES) * STAGE;
+      const uint16_t *Vs = Ks + TILE;
 
-    // the tile STAGES - 1 ahead is loaded while this one's QK^T runs
-    const int w_pf = u + STAGES - 1;
-    const bool pf = w_pf < u1;
-    int srow[NL], pfirst = 0, plim = 1;
-    bool pch = false;
-#pragma unroll
-    for (int e = 0; e < NL; ++e) srow[e] = 0;
-    if (pf) pch = plan(w_pf, srow, pfirst, plim);
-    uint16_t *pst = ring + (w_pf % STAGES) * STAGE;
+      if (LAG && u > u0) {  // the previous tile's O update (its V still in the ring)
+        const uint32_t vb = lds_addr(ring + ((u - 1) % STAGES) * STAGE + TILE) + 2 * (v_key * D);
+        u32x2 wv[2][2 * NPT];
+        v_reads(vb, 0, wv[0]);
+        pv_tile(vb, pb_lag, wv);
+      }
 
-    f32x16 sacc[NKB];
-    qk_tile(Ks, sacc, [&](int s) __attribute__((always_inline)) {
-#pragma unroll
-      for (int j = s * ND / NS; j < (s + 1) * ND / NS; ++j)
-        if (pf) dma(j, pch, srow, pfirst, plim, pst);
-    });
+      // the tile PD ahead is loaded while this one's QK^T runs
+      const int w_pf = u + PD;
+      const bool pf = w_pf < u1;
+      int srow[NL], pfirst = 0, plim = 1;
+      bool pch = false;
+  #pragma unroll
+      for (int e = 0; e < NL; ++e) srow[e] = 0;
+      if (pf) pch = plan(w_pf, srow, pfirst, plim);
+      uint16_t *pst = ring + (w_pf % STAGES) * STAGE;
 
-    // V^T reads of the first dim block go out before the softmax needs the ALUs
-    const uint32_t vbase = lds_addr(Vs) + 2 * (v_key * D);
-    u32x2 wv[2][2 * NPT];
-    v_reads(vbase, 0, wv[0]);
-    bf16x8 pb[NPT];
-    softmax_tile(u, sacc, reinterpret_cast<const float *>(Ks + 2 * TILE), pb);
-    pv_tile(vbase, pb, wv);
-  }
+      f32x16 sacc[NKB];
+      qk_tile(Ks, sacc, [&](int s) __attribute__((always_inline)) {
+  #pragma unroll
+        for (int j = s * ND / NS; j < (s + 1) * ND / NS; ++j)
+          if (pf) dma(j, pch, srow, pfirst, plim, pst);
+      });
+
+      if (LAG) {
+        softmax_tile(u, sacc, reinterpret_cast<const float *>(Ks + 2 * TILE), pb_lag);
+      } else {
+        // V^T reads of the first dim block go out before the softmax needs the ALUs
+        const uint32_t vbase = lds_addr(Vs) + 2 * (v_key * D);
+        u32x2 wv[2][2 * NPT];
+        v_reads(vbase, 0, wv[0]);
+        bf16x8 pb[NPT];
+        softmax_tile(u, sacc, reinterpret_cast<const float *>(Ks + 2 * TILE), pb);
+        pv_tile(vbase, pb, wv);
+      }
+    }
+    if (LAG && u1 > u0) {  // the last tile's O update (no load refills the ring now)
+      const uint32_t vb = lds_addr(ring + ((u1 - 1) % STAGES) * STAGE + TILE) + 2 * (v_key * D);
+      u32x2 wv[2][2 * NPT];
+      v_reads(vb, 0, wv[0]);
+      pv_tile(vb, pb_lag, wv);
+    }
+  };
+  if (lagging)
+    tile_loop(std::integral_constant<bool, true>{});
+  else
+    tile_loop(std::integral_constant<bool, false>{});
 
   const float l_tot = pair_sum(l_run);
   if (!row_ok) return;

@@ -14,7 +14,6 @@ namespace cp {
 namespace {
 
 constexpr int KTG = 16;  // keys per tile
-constexpr int ROWS = 16;  // query rows per workgroup
 
 template <typename T>
 __device__ __forceinline__ float ld(const T *p, size_t i);

@@ -16,11 +16,11 @@
 // state and D: only D and the state update form the serial chain across chunks.
 //
 // Three kernels, all on v_mfma_f32_16x16x4f32 (fp32 products, fp32 sums):
-//  - k_gdn_prep, one workgroup per (chunk, head, sequence): the Gram products K K^T
-//    and Q K^T of the chunk; T by inverting the four 16x16 diagonal blocks of I + A
+//  - k_gdn_prep, two workgroups per (chunk, head, sequence): one forms the Gram
+//    product K K^T, T by inverting the four 16x16 diagonal blocks of I + A
 //    (one lane per column) and filling the blocks below them in three rounds
-//    (T_ij = -T_ii sum_k A_ik T_kj); then [U | W] = T [diag(beta) V | diag(beta e^lg) K].
-//    Writes W, U, P = tril(R) * Q K^T, lg and K^T of the chunk to the workspace.
+//    (T_ij = -T_ii sum_k A_ik T_kj); then [U | W] = T [diag(beta) V | diag(beta e^lg) K],
+//    and writes W, U and lg; the other forms P = tril(R) * Q K^T and writes it with K^T.
 //  - k_gdn_scan, one workgroup per (16 state columns, head, sequence): the state's
 //    columns evolve independently.  Walks the chunks: each wave computes 16 rows of
 //    D = U - W S, then updates its own row blocks of S (kept in MFMA accumulators,
@@ -103,8 +103,12 @@ __global__ void __launch_bounds__(PREP_THREADS) k_gdn_prep(const float *__restri
   __shared__ __align__(16) float As[CH * AP];
   __shared__ __align__(16) float Ts[CH * AP];
   __shared__ float lg[CH], bt[CH], fk[CH];  // lg, beta, beta e^lg
-  int G, c;
-  if (!head_slot(nch, BH, G, c)) return;  // whole workgroup, before any barrier
+  // Two workgroups per chunk: role 0 forms A = K K^T, T and [U | W]; role 1 the output's
+  // P = tril(R) * Q K^T and K^T.  They write disjoint parts of the chunk's workspace.
+  int G, cr;
+  if (!head_slot(2 * nch, BH, G, cr)) return;  // whole workgroup, before any barrier
+  const int role = cr >= nch ? 1 : 0;
+  const int c = cr - role * nch;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, m = lane & 15, g = lane >> 4;
   const size_t bh = G;
   const int t0 = c * CH;
@@ -112,7 +116,8 @@ __global__ void __launch_bounds__(PREP_THREADS) k_gdn_prep(const float *__restri
   float *ck = ws + (bh * nch + c) * L::SIZE;
 
   const f4 zero = {0.f, 0.f, 0.f, 0.f};
-  {  // the chunk's K, Q and V: every load in flight before the first LDS store
+  {  // the chunk's K and V (role 0) or K and Q (role 1): every load in flight before the
+     // first LDS store
     constexpr int NK = CH * DK / (4 * PREP_THREADS), NV = CH * DV / (4 * PREP_THREADS);
     f4 kr[NK], qr[NK], vr[NV];
 #pragma unroll
@@ -120,23 +125,25 @@ __global__ void __launch_bounds__(PREP_THREADS) k_gdn_prep(const float *__restri
       const int e = tid + PREP_THREADS * u, t = e / (DK / 4), i = (e % (DK / 4)) * 4;
       const size_t src = (bh * P + t0 + t) * DK + i;
       kr[u] = t < n ? ld4(k + src) : zero;
-      qr[u] = t < n ? ld4(q + src) : zero;
+      qr[u] = t < n && role == 1 ? ld4(q + src) : zero;
     }
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int e = tid + PREP_THREADS * u, t = e / (DV / 4), j = (e % (DV / 4)) * 4;
-      vr[u] = t < n ? ld4(v + (bh * P + t0 + t) * DV + j) : zero;
+      vr[u] = t < n && role == 0 ? ld4(v + (bh * P + t0 + t) * DV + j) : zero;
     }
 #pragma unroll
     for (int u = 0; u < NK; ++u) {
       const int e = tid + PREP_THREADS * u, t = e / (DK / 4), i = (e % (DK / 4)) * 4;
       st4(&Ks[t * KP + i], kr[u]);
-      st4(&Qs[t * KP + i], qr[u]);
+      if (role == 1) st4(&Qs[t * KP + i], qr[u]);
     }
+    if (role == 0) {
 #pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int e = tid + PREP_THREADS * u, t = e / (DV / 4), j = (e % (DV / 4)) * 4;
-      st4(&Vs[t * VP + j], vr[u]);
+      for (int u = 0; u < NV; ++u) {
+        const int e = tid + PREP_THREADS * u, t = e / (DV / 4), j = (e % (DV / 4)) * 4;
+        st4(&Vs[t * VP + j], vr[u]);
+      }
     }
   }
   if (w == 0) {  // inclusive prefix sum of the log-gates over the chunk
@@ -150,13 +157,14 @@ __global__ void __launch_bounds__(PREP_THREADS) k_gdn_prep(const float *__restri
     lg[lane] = a;
     bt[lane] = be;
     fk[lane] = be * __expf(a);
-    ck[L::LG + lane] = a;
+    if (role == 0) ck[L::LG + lane] = a;
   }
   __syncthreads();
 
-  // Gram tiles on and below the diagonal: 10 tiles of K K^T (-> A) and 10 of Q K^T
-  // (-> P), dealt over the waves.  Contraction index of k-step (kk, j): g * DK/4 + 4 kk + j.
-  for (int p = w; p < 20; p += PREP_THREADS / 64) {
+  // Gram tiles on and below the diagonal: the 10 tiles of K K^T (-> A, role 0) or of
+  // Q K^T (-> P, role 1), dealt over the waves.  Contraction index of k-step (kk, j):
+  // g * DK/4 + 4 kk + j.
+  for (int p = w + 10 * role; p < 10 + 10 * role; p += PREP_THREADS / 64) {
     const int tl = p % 10;
     const int tt = (tl >= 1) + (tl >= 3) + (tl >= 6);
     const int st = tl - tt * (tt + 1) / 2;
@@ -187,9 +195,12 @@ __global__ void __launch_bounds__(PREP_THREADS) k_gdn_prep(const float *__restri
         ck[L::P + t * CH + s] = rr * gram;
     }
   }
-  for (int e = tid; e < DK * CH; e += PREP_THREADS) {  // K^T for the scan's state update
-    const int i = e / CH, t = e % CH;
-    ck[L::KT + e] = Ks[t * KP + i];
+  if (role == 1) {
+    for (int e = tid; e < DK * CH; e += PREP_THREADS) {  // K^T for the scan's state update
+      const int i = e / CH, t = e % CH;
+      ck[L::KT + e] = Ks[t * KP + i];
+    }
+    return;  // (the whole workgroup: role 1 passes no further barrier)
   }
   __syncthreads();
 
@@ -491,8 +502,8 @@ hipError_t launch_dims(const float *q, const float *k, const float *v, const flo
                        float *ws, hipStream_t s) {
   const int nch = (P + CH - 1) / CH;
   const int BH = B * H, slots = 8 * ((BH + 7) / 8);  // grid sizes checked by gdn_grid_fits
-  hipLaunchKernelGGL((k_gdn_prep<DK, DV>), dim3(slots * nch), dim3(PREP_THREADS), 0, s, q, k, v,
-                     beta, alpha, ws, BH, P, nch);
+  hipLaunchKernelGGL((k_gdn_prep<DK, DV>), dim3(slots * 2 * nch), dim3(PREP_THREADS), 0, s, q,
+                     k, v, beta, alpha, ws, BH, P, nch);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_gdn_scan<DK, DV>), dim3(slots * (DV / VB)), dim3(256), 0, s, ws, state,

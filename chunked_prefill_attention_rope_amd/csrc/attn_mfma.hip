@@ -865,23 +865,27 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
       }
     }
   } else if (i < nv) {  // partials of real rows only: the merge writes pad rows as zeros
-    const size_t rows = static_cast<size_t>(p.B) * p.H * p.C;
-    float *WO = p.wo + (split * rows + orow) * D;
+    // fragment order (p.frag_rows == ROWS): the accumulators leave as they sit in the
+    // lanes, each store instruction 1 KB of consecutive bytes (in row order every one
+    // would touch 32 rows)
+    const size_t nu = static_cast<size_t>(p.B) * p.nKV * p.qtiles * ROWW;
+    const size_t u = (static_cast<size_t>(bg) * p.qtiles + qtile) * ROWW + wave % ROWW;
+    const size_t grp = static_cast<size_t>(split) * nu + u;
+    float *WO = p.wo + grp * (D / 32) * 1024 + 4 * lane;
 #pragma unroll
     for (int db = 0; db < NDW; ++db) {
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const int d = 32 * (dgrp * NDW + db) + 8 * rq + 4 * hh;
         float4 w;
         w.x = real ? oacc[db][4 * rq + 0] : 0.f;
         w.y = real ? oacc[db][4 * rq + 1] : 0.f;
         w.z = real ? oacc[db][4 * rq + 2] : 0.f;
         w.w = real ? oacc[db][4 * rq + 3] : 0.f;
-        *reinterpret_cast<float4 *>(WO + d) = w;
+        *reinterpret_cast<float4 *>(WO + (dgrp * NDW + db) * 1024 + rq * 256) = w;
       }
     }
     if (hh == 0 && dgrp == 0) {
-      float *ML = p.wml + (split * rows + orow) * 2;
+      float *ML = p.wml + (grp * 32 + n) * 2;
       ML[0] = real ? m_run : -INFINITY;
       ML[1] = real ? l_tot : 0.f;
     }
@@ -889,35 +893,36 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
 }
 
 template <int D, bool EXPLICIT, bool EXT, int SM>
-void launch_one(const AttnParams &p, unsigned blocks, hipStream_t s) {
+hipError_t launch_one(const AttnParams &p, unsigned blocks, hipStream_t s) {
   using CF = Sel<D, EXT, SM>;
+  // split partials go out in the fragment order of this configuration's query tile
+  if (p.splits > 1 && p.frag_rows != 32 * CF::ROWW) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_attn_mfma<D, EXPLICIT, EXT, SM>), dim3(blocks),
                      dim3(64 * CF::ROWW * CF::DSPLIT), 0, s, p);
+  return hipSuccess;
 }
 
 template <int D, int SM>
-void launch_mode(const AttnParams &p, unsigned blocks, hipStream_t s) {
-  if (p.mask)
-    launch_one<D, true, true, SM>(p, blocks, s);
-  else if (p.full_tiles)
-    launch_one<D, false, true, SM>(p, blocks, s);
-  else
-    launch_one<D, false, false, SM>(p, blocks, s);
+hipError_t launch_mode(const AttnParams &p, unsigned blocks, hipStream_t s) {
+  if (p.mask) return launch_one<D, true, true, SM>(p, blocks, s);
+  if (p.full_tiles) return launch_one<D, false, true, SM>(p, blocks, s);
+  return launch_one<D, false, false, SM>(p, blocks, s);
 }
 
 template <int D>
 hipError_t launch_d(const AttnParams &p, hipStream_t s) {
   const unsigned blocks = static_cast<unsigned>(p.qtiles) * p.splits * p.B * p.nKV;
   if (blocks == 0) return hipSuccess;
+  hipError_t e;
   if (p.small_rows == 2) {
     if (p.mask || p.full_tiles) return hipErrorInvalidValue;  // deep ring: in-kernel rule only
-    launch_one<D, false, false, 2>(p, blocks, s);
+    e = launch_one<D, false, false, 2>(p, blocks, s);
   } else if (p.small_rows == 1) {
-    launch_mode<D, 1>(p, blocks, s);
+    e = launch_mode<D, 1>(p, blocks, s);
   } else {
-    launch_mode<D, 0>(p, blocks, s);
+    e = launch_mode<D, 0>(p, blocks, s);
   }
-  return hipGetLastError();
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 }  // namespace

@@ -256,26 +256,57 @@ __global__ void __launch_bounds__(256) k_attn_valu(AttnParams p, int D) {
 // partials are fetched SB splits at a time (independent loads in flight together)
 // and folded into a running maximum, so a row costs ceil(splits / SB) memory round
 // trips instead of one per split.
-// I: index type (32-bit when the element count allows; see the RoPE kernel).
+// I: index type (32-bit when every partial's offset allows; see the RoPE kernel).
 // SB: splits fetched per round -- 32 when there are more than 16 splits (one round
 // for up to 32), else 16 (the narrower kernel keeps more waves resident for merges of
 // many rows).
-template <typename T, int VEC, typename I, int SB>
+// FRAG: the partials are in the matrix-core kernel's fragment order (AttnParams::wo),
+// D a power of two.  Thread t takes the 4 floats at 4 t of each split, so that a
+// wave's partial reads are 1 KB of consecutive bytes (the reads are SB times the
+// writes; the bf16 output rows are written 16 bytes per row and instruction).
+template <typename T, int VEC, typename I, int SB, bool FRAG>
 __global__ void __launch_bounds__(256) k_attn_combine(AttnParams p, int D) {
+  static_assert(!FRAG || VEC == 4, "fragment order: 4 floats per thread");
   const size_t rows = static_cast<size_t>(p.B) * p.H * p.C;
+  // rows of one split's partials (fragment order: every row of every query tile)
+  const size_t prow = FRAG ? static_cast<size_t>(p.B) * p.nKV * p.qtiles * p.frag_rows : rows;
   const I per_row = D / VEC;
-  const I total = static_cast<I>(rows) * per_row;
+  const I total = static_cast<I>(prow) * per_row;
+  // one split's partials apart (element offsets: with a 32-bit I, every offset in the
+  // workspace fits 32 bits, so a load is one scalar base plus a 32-bit vector offset
+  // instead of a 64-bit address per split kept live across the loop)
+  const I o_str = static_cast<I>(prow) * D, m_str = static_cast<I>(prow) * 2;
+  const int lg_blk = FRAG ? __builtin_ctz(static_cast<unsigned>(D)) - 5 : 0;  // log2(D / 32)
   T *O = static_cast<T *>(p.out);
   for (I t = blockIdx.x * static_cast<I>(blockDim.x) + threadIdx.x; t < total;
        t += static_cast<I>(gridDim.x) * blockDim.x) {
-    const I row_i = t / per_row;
-    const size_t row = row_i;
-    const int d0 = static_cast<int>(t - row_i * per_row) * VEC;
-    const I bh = row_i / static_cast<I>(p.C);
-    const int i = static_cast<int>(row_i - bh * p.C);
-    const int b = static_cast<int>(bh / static_cast<I>(p.H));
-    // partials of splits s0 .. s0 + SB - 1 (pad rows have none written: their values
-    // are read but not used)
+    // The split count and strides pass through an empty asm each iteration: loop
+    // invariants to the compiler, which would otherwise compute the SB per-split
+    // conditions and offsets once ahead of the loop and keep them (spilled) across it
+    // -- several hundred instructions ahead of the first load, for a loop that
+    // normally runs once.
+    int nsp = p.splits;
+    I os = o_str, ms = m_str;
+    asm volatile("" : "+s"(nsp), "+s"(os), "+s"(ms));
+    // partial offsets first (shifts only), so that the loads go out before the
+    // divisions that place the row
+    I u = 0;      // fragment order: 32-row group
+    int n = 0;    // fragment order: row within the group
+    I o_at, ml_at;  // offsets of this thread's values in one split's O and (m, l)
+    I row_i = 0;  // row-major: output row
+    if constexpr (FRAG) {
+      // float4 j * 64 + 32 h + n of a block: row n, columns 8 j + 4 h .. + 3
+      n = static_cast<int>(t & 31);
+      u = (t >> 8) >> lg_blk;
+      o_at = t * 4;
+      ml_at = (u * 32 + static_cast<I>(n)) * 2;
+    } else {
+      row_i = t / per_row;
+      o_at = row_i * D + (t - row_i * per_row) * VEC;
+      ml_at = row_i * 2;
+    }
+    // partials of splits s0 .. s0 + SB - 1 (pad rows, and the spare rows of a query
+    // tile, have none written: their values are read but not used)
     float mv[SB], lv[SB], ov[SB][VEC];
     auto fetch = [&](int s0) __attribute__((always_inline)) {
 #pragma unroll
@@ -284,12 +315,12 @@ __global__ void __launch_bounds__(256) k_attn_combine(AttnParams p, int D) {
         lv[j] = 0.f;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) ov[j][e] = 0.f;
-        if (s0 + j < p.splits) {
-          const size_t sr = (s0 + j) * rows + row;
-          const float2 ml = *reinterpret_cast<const float2 *>(p.wml + sr * 2);
+        if (s0 + j < nsp) {
+          const I sj = static_cast<I>(s0 + j);
+          const float2 ml = *reinterpret_cast<const float2 *>(p.wml + (sj * ms + ml_at));
           mv[j] = ml.x;
           lv[j] = ml.y;
-          const float *src = p.wo + sr * D + d0;
+          const float *src = p.wo + (sj * os + o_at);
           if constexpr (VEC == 4) {
             const float4 v = *reinterpret_cast<const float4 *>(src);
             ov[j][0] = v.x;
@@ -305,6 +336,31 @@ __global__ void __launch_bounds__(256) k_attn_combine(AttnParams p, int D) {
     };
     // the first round goes out together with the n_valid read, not after it
     fetch(0);
+    size_t row;  // output row (b * H + head) * C + i
+    int d0, i, b;
+    I bh;        // b * H + head
+    if constexpr (FRAG) {
+      const int rw = p.frag_rows >> 5;
+      const I tq = u / static_cast<I>(rw);  // query tile, over (b, kv head)
+      const int r = static_cast<int>(u - tq * rw) * 32 + n;
+      const I bg = tq / static_cast<I>(p.qtiles);
+      const int qt = static_cast<int>(tq - bg * p.qtiles);
+      b = static_cast<int>(bg / static_cast<I>(p.nKV));
+      const int g = static_cast<int>(bg - static_cast<I>(b) * p.nKV);
+      const int hl = r / p.qpos;
+      i = qt * p.qpos + (r - hl * p.qpos);
+      if (hl >= p.G || i >= p.C) continue;  // a spare row of the tile: no output row
+      bh = static_cast<I>(b) * p.H + g * p.G + hl;
+      row = static_cast<size_t>(bh) * p.C + i;
+      d0 = 32 * static_cast<int>((t >> 8) & ((1u << lg_blk) - 1)) +
+           8 * static_cast<int>((t >> 6) & 3) + 4 * static_cast<int>((t >> 5) & 1);
+    } else {
+      row = row_i;
+      d0 = static_cast<int>(t - row_i * per_row) * VEC;
+      bh = row_i / static_cast<I>(p.C);
+      i = static_cast<int>(row_i - bh * p.C);
+      b = static_cast<int>(bh / static_cast<I>(p.H));
+    }
     const int nv = read_nvalid(p.n_valid, b, p.C, nullptr);
     float res[VEC];
 #pragma unroll
@@ -313,7 +369,7 @@ __global__ void __launch_bounds__(256) k_attn_combine(AttnParams p, int D) {
       float M = -INFINITY, l = 0.f, o[VEC];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) o[e] = 0.f;
-      for (int s0 = 0; s0 < p.splits; s0 += SB) {
+      for (int s0 = 0; s0 < nsp; s0 += SB) {
         if (s0 > 0) fetch(s0);
         float Mn = M;
 #pragma unroll
@@ -384,39 +440,49 @@ hipError_t launch_attn_valu(const AttnParams &p, int D, int dtype, hipStream_t s
 }
 
 hipError_t launch_attn_combine(const AttnParams &p, int D, int dtype, hipStream_t s) {
-  const size_t total = static_cast<size_t>(p.B) * p.H * p.C * D;
-  if (total == 0) return hipSuccess;
+  if (static_cast<size_t>(p.B) * p.H * p.C * D == 0) return hipSuccess;
+  // fragment order: the bf16 matrix-core kernel's partials (D a power of two >= 32)
+  const bool frag = p.frag_rows > 0;
+  if (frag && (dtype != CP_BF16 || D < 32 || (D & (D - 1)) != 0 || p.frag_rows % 32 != 0))
+    return hipErrorInvalidValue;
+  const size_t prow = frag ? static_cast<size_t>(p.B) * p.nKV * p.qtiles * p.frag_rows
+                           : static_cast<size_t>(p.B) * p.H * p.C;
+  const size_t total = prow * D;  // partial elements of one split
   const bool v4 = D % 4 == 0;
-  size_t blocks = (total / (v4 ? 4 : 1) + 255) / 256;
+  const unsigned bs = 64;  // threads per workgroup: the rows spread over more CUs
+  size_t blocks = (total / (v4 ? 4 : 1) + bs - 1) / bs;
   if (blocks > 16384) blocks = 16384;
-  const bool i32 = total < (size_t(1) << 31);
+  // 32-bit offsets when the whole workspace's byte offsets fit 32 bits
+  const bool i32 = total * static_cast<size_t>(p.splits) < (size_t(1) << 30);
   const bool wide = p.splits > 16;
-#define CP_COMBINE_SB(T, V, SB)                                                              \
+#define CP_COMBINE_SB(T, V, SB, F)                                                           \
   do {                                                                                       \
     if (i32)                                                                                 \
-      hipLaunchKernelGGL((k_attn_combine<T, V, uint32_t, SB>), dim3(blocks), dim3(256), 0, s, \
-                         p, D);                                                              \
+      hipLaunchKernelGGL((k_attn_combine<T, V, uint32_t, SB, F>), dim3(blocks), dim3(bs), 0, \
+                         s, p, D);                                                           \
     else                                                                                     \
-      hipLaunchKernelGGL((k_attn_combine<T, V, size_t, SB>), dim3(blocks), dim3(256), 0, s,   \
-                         p, D);                                                              \
+      hipLaunchKernelGGL((k_attn_combine<T, V, size_t, SB, F>), dim3(blocks), dim3(bs), 0,    \
+                         s, p, D);                                                           \
   } while (0)
-#define CP_COMBINE(T, V)          \
-  do {                            \
-    if (wide)                     \
-      CP_COMBINE_SB(T, V, 32);    \
-    else                          \
-      CP_COMBINE_SB(T, V, 16);    \
+#define CP_COMBINE(T, V, F)          \
+  do {                               \
+    if (wide)                        \
+      CP_COMBINE_SB(T, V, 32, F);    \
+    else                             \
+      CP_COMBINE_SB(T, V, 16, F);    \
   } while (0)
-  if (dtype == CP_BF16) {
+  if (frag) {
+    CP_COMBINE(uint16_t, 4, true);
+  } else if (dtype == CP_BF16) {
     if (v4)
-      CP_COMBINE(uint16_t, 4);
+      CP_COMBINE(uint16_t, 4, false);
     else
-      CP_COMBINE(uint16_t, 1);
+      CP_COMBINE(uint16_t, 1, false);
   } else {
     if (v4)
-      CP_COMBINE(float, 4);
+      CP_COMBINE(float, 4, false);
     else
-      CP_COMBINE(float, 1);
+      CP_COMBINE(float, 1, false);
   }
 #undef CP_COMBINE
 #undef CP_COMBINE_SB

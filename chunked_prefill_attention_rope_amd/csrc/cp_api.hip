@@ -53,6 +53,7 @@ AttnPlan plan_attention(const cp_cache &c, const cp_attn_args &a, bool for_works
             aligned;
   int hgroups = 1;
   if (pl.mfma) {
+    pl.rows = rows;
     pl.qpos = rows / G;
     pl.kt = mfma_keys_per_tile(c.D, ext, pl.small_rows);
   } else {
@@ -107,9 +108,17 @@ AttnPlan plan_attention(const cp_cache &c, const cp_attn_args &a, bool for_works
   return pl;
 }
 
+// Rows of the split partials: the chunk rows, or for the matrix-core kernel every row
+// of every query tile (fragment order, which includes the last tile's rows past C and,
+// when G does not divide a tile's rows, its spare rows).
+static size_t partial_rows(const cp_cache &c, const cp_attn_args &a, const AttnPlan &p) {
+  if (p.mfma) return static_cast<size_t>(c.B) * c.nKV * p.qtiles * p.rows;
+  return static_cast<size_t>(c.B) * a.H * a.C;
+}
+
 size_t attn_workspace_bytes(const cp_cache &c, const cp_attn_args &a, const AttnPlan &p) {
   if (p.splits <= 1) return 0;
-  const size_t rows = static_cast<size_t>(c.B) * a.H * a.C;
+  const size_t rows = partial_rows(c, a, p);
   return round256(static_cast<size_t>(p.splits) * rows * c.D * sizeof(float)) +
          round256(static_cast<size_t>(p.splits) * rows * 2 * sizeof(float));
 }
@@ -149,8 +158,9 @@ hipError_t launch_attention(const cp_cache &c, const cp_attn_args &a, hipStream_
   p.cache = c;
   const bool advance = (a.flags & CP_ATTN_ADVANCE_SEEN) != 0;
   p.advance = advance && pl.splits > 1 ? 1 : 0;
+  p.frag_rows = pl.mfma ? pl.rows : 0;
   if (pl.splits > 1) {
-    const size_t rows = static_cast<size_t>(c.B) * a.H * a.C;
+    const size_t rows = partial_rows(c, a, pl);
     unsigned char *w = static_cast<unsigned char *>(a.workspace);
     p.wo = reinterpret_cast<float *>(w);
     p.wml = reinterpret_cast<float *>(

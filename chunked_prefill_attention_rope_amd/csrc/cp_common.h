@@ -155,6 +155,8 @@ struct AttnPlan {
   int qpos;       // chunk rows per query tile
   int kt;         // keys per tile
   int small_rows;   // matrix-core kernel: 0, or its 64-row configuration (1; 2 = deep ring)
+  int rows;         // matrix-core kernel: query rows per query tile (its split partials
+                    // are stored in that tile's fragment order)
 };
 
 AttnPlan plan_attention(const cp_cache &c, const cp_attn_args &a, bool for_workspace);

@@ -340,6 +340,45 @@ def test_decode_split_merge(cp, kw, mode, split):
     assert int(status.item()) == 0
 
 
+@pytest.mark.parametrize("shape", [
+    # (H, nKV, D, C, seen, n_valid): the matrix-core query tile holds 128 or 256 rows;
+    # G = 3 or 5 leaves spare rows at its end, and C is not a multiple of the tile's
+    # chunk rows, so the last query tile is ragged
+    (6, 2, 64, 45, [300, 77], [45, 31]),
+    (5, 1, 256, 40, [260, 129], [33, 40]),
+    (6, 2, 128, 100, [350, 12], [100, 57]),
+])
+@pytest.mark.parametrize("splits", [5, 19])
+@pytest.mark.parametrize("mode", ["inkernel", "explicit"])
+def test_merge_fragment_rows(cp, shape, splits, mode):
+    """The matrix-core kernel's split partials, in accumulator fragment order, on query
+    tiles with spare rows (G does not divide the tile's rows) and a ragged last tile, two
+    sequences, two KV heads: every real row matches the oracle, pad rows are zeros, the
+    selection is the merged row, and a repeat is bit-identical."""
+    H, nKV, D, C, seen, n_valid = shape
+    cfg = I.small(dtype=I.BF16, B=2, H=H, nKV=nKV, D=D, C=C, cap=512, seen=seen,
+                  n_valid=n_valid)
+    t, cache, status = _setup(cp, cfg)
+    q, k, v = dev(t["q"]), dev(t["k"]), dev(t["v"])
+    nv = dev(t["n_valid"])
+    mask = None
+    if mode == "explicit":
+        mask = cp.build_mask(cache, nv, cfg.H, cfg.C, cfg.mask_ld(), window=cfg.window)
+    flags = cp.ATTN_SPLITS(splits)
+    nb = cp.attn_workspace_bytes(cache, q, k, v, mask=mask, flags=flags)
+    assert nb > 0
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    sel = torch.zeros((cfg.B, cfg.H, cfg.D), dtype=q.dtype, device="cuda")
+    outs = [cp.attn_chunk_with_past(cache, q, k, v, n_valid=nv, mask=mask, scale=cfg.scale,
+                                    workspace=ws, select_out=sel, flags=flags)
+            for _ in range(2)]
+    torch.cuda.synchronize()
+    _check(cfg, outs[0], _oracle(cfg, t))
+    assert np.array_equal(bits(outs[1]), bits(outs[0]))
+    assert np.array_equal(bits(sel), bits(cp.select_row(outs[0], nv, -1)))
+    assert int(status.item()) == 0
+
+
 @pytest.mark.parametrize("splits", [16, 17, 33, 64])
 @pytest.mark.parametrize("mode", ["inkernel", "explicit"])
 def test_merge_rounds(cp, splits, mode):

@@ -48,6 +48,21 @@ struct AttnParams {
   cp_cache cache; // the cache the call reads (for advance)
 };
 
+// Requests every 64-byte line of a kernel's argument block in one batch, so that the
+// later reads of its fields hit the scalar cache.  Left to itself the compiler reads
+// the fields lazily, a line or two at a time, and waits for each batch before the
+// next: several memory round trips in a row ahead of the first dependent load.
+template <typename P>
+__device__ __forceinline__ void request_args(const P &p) {
+  constexpr int kLines = static_cast<int>((sizeof(P) + 63) / 64);
+  static_assert(kLines >= 1 && kLines <= 6, "argument block of at most six lines");
+  const int32_t *w = reinterpret_cast<const int32_t *>(&p);
+  int32_t v[6];
+#pragma unroll
+  for (int k = 0; k < 6; ++k) v[k] = w[16 * (k < kLines ? k : kLines - 1)];
+  asm volatile("" ::"s"(v[0]), "s"(v[1]), "s"(v[2]), "s"(v[3]), "s"(v[4]), "s"(v[5]));
+}
+
 // Ordered list of the key tiles one query tile needs.  Past tiles cover
 // columns [t*kt, t*kt + kt) of the live past, chunk tiles rows [t*kt, ...).
 // With the in-kernel mask, tiles no real row of the query tile attends

@@ -47,6 +47,7 @@ __device__ __forceinline__ float row16_sum(float v) {
 
 template <typename T, int DPT, bool EXPLICIT>
 __global__ void __launch_bounds__(256) k_attn_valu(AttnParams p, int D) {
+  request_args(p);
   constexpr int NF = KTG * DPT / 16;  // >= KTG * D / 256 tile elements per thread
   extern __shared__ float lds[];
   float *Ks = lds;             // [KTG][D]
@@ -72,9 +73,26 @@ __global__ void __launch_bounds__(256) k_attn_valu(AttnParams p, int D) {
   const bool row_ok = r < p.hb * p.qpos && hl < p.G && i < p.C;
   const int head = g * p.G + (hl < p.G ? hl : 0);
 
+  // the query row does not depend on the cache state: requested first, so that its
+  // latency overlaps that of seen
+  float q[DPT], acc[DPT];
+  const T *Q = static_cast<const T *>(p.q);
+  const size_t qoff = ((static_cast<size_t>(b) * p.H + head) * p.C + (i < p.C ? i : 0)) * D;
+#pragma unroll
+  for (int e = 0; e < DPT; ++e) {
+    const int d = ql + 16 * e;
+    q[e] = (row_ok && d < D) ? ld<T>(Q, qoff + d) : 0.f;
+    acc[e] = 0.f;
+  }
+  // seen and n_valid are both requested before either is used (scalar loads complete
+  // out of order, so the first use waits for every one in flight: one round trip)
   const int seen = p.seen[b];
+  int nv = p.n_valid ? p.n_valid[b] : p.C;
   const bool lead = tid == 0 && qtile == 0 && hgrp == 0 && split == 0 && g == 0;
-  const int nv = read_nvalid(p.n_valid, b, p.C, lead ? p.status : nullptr);
+  if (nv < 0 || nv > p.C) {
+    if (lead) flag(p.status, CP_DEV_NVALID);
+    nv = nv < 0 ? 0 : p.C;
+  }
   bool bad = seen < 0 || (!p.ring && seen > p.cap);
   if (bad && lead) flag(p.status, CP_DEV_SEEN);
   const Live gl = live_geometry(bad ? 0 : seen, p.cap, p.ring, p.sink);
@@ -86,15 +104,6 @@ __global__ void __launch_bounds__(256) k_attn_valu(AttnParams p, int D) {
   const int i_last = imin(i_end, nv) - 1;
   const bool any_real = !bad && i_last >= i_min;
 
-  float q[DPT], acc[DPT];
-  const T *Q = static_cast<const T *>(p.q);
-  const size_t qoff = ((static_cast<size_t>(b) * p.H + head) * p.C + (i < p.C ? i : 0)) * D;
-#pragma unroll
-  for (int e = 0; e < DPT; ++e) {
-    const int d = ql + 16 * e;
-    q[e] = (row_ok && d < D) ? ld<T>(Q, qoff + d) : 0.f;
-    acc[e] = 0.f;
-  }
   float m_run = -INFINITY, l_run = 0.f;
 
   TileSeq ts{};
@@ -102,9 +111,12 @@ __global__ void __launch_bounds__(256) k_attn_valu(AttnParams p, int D) {
   if (any_real) {
     ts = make_tiles(gl, seen, p.C, KTG, i_min, i_last, EXPLICIT ? 0 : p.window, p.sink,
                     EXPLICIT || p.full_tiles);
-    const int n = ts.count();
-    u0 = static_cast<int>((static_cast<long>(n) * split) / p.splits);
-    u1 = static_cast<int>((static_cast<long>(n) * (split + 1)) / p.splits);
+    // near-equal split ranges, the first cnt % splits one tile longer (one 32-bit
+    // division: a 64-bit one is a long software sequence ahead of the first load)
+    const unsigned cnt = static_cast<unsigned>(ts.count()), ns = static_cast<unsigned>(p.splits);
+    const unsigned qn = cnt / ns, rm = cnt - qn * ns, us = static_cast<unsigned>(split);
+    u0 = static_cast<int>(us * qn + (us < rm ? us : rm));
+    u1 = u0 + static_cast<int>(qn + (us < rm ? 1u : 0u));
   }
   const T *KC = static_cast<const T *>(p.kc);
   const T *VC = static_cast<const T *>(p.vc);

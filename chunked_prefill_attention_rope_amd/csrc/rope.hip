@@ -30,6 +30,10 @@ struct Elem<uint16_t> {
   static __device__ __forceinline__ uint16_t put(float v) { return f32_to_bf16_rne(v); }
 };
 
+// Threads per workgroup: 64 while that keeps the grid within one workgroup per CU
+// (a chunk's rows spread over more CUs), else 128.
+constexpr int kRopeThreads = 128;
+
 template <typename T, int N>
 struct alignas(sizeof(T) * N) Pack {
   T v[N];
@@ -92,7 +96,7 @@ struct EarlyAppend {
 // I: index type -- 32-bit whenever the launch's element count allows (integer division
 // is a software sequence, and a 64-bit one several times longer).
 template <typename T, int VEC, typename I>
-__global__ void __launch_bounds__(128) k_rope(RopeOp<T> a, RopeOp<T> bop, EarlyAppend<T> app,
+__global__ void __launch_bounds__(kRopeThreads) k_rope(RopeOp<T> a, RopeOp<T> bop, EarlyAppend<T> app,
                                               const float *__restrict__ cosb,
                                               const float *__restrict__ sinb, int B, int C, int D,
                                               int Bt) {
@@ -165,33 +169,33 @@ hipError_t launch_t(const void *x0, void *y0, int H0, const void *x1, void *y1, 
   const int h2 = D / 2;
   const size_t rows = static_cast<size_t>(B) * (H0 + H1) * C;
   if (rows == 0) return hipSuccess;
-  auto grid_for = [&](int vec) {
-    size_t total = rows * (h2 / vec);
-    size_t blocks = (total + 127) / 128;
-    if (blocks > 65535 * 4) blocks = 65535 * 4;
-    return static_cast<unsigned>(blocks);
-  };
   const RopeOp<T> a{static_cast<const T *>(x0), static_cast<T *>(y0), H0};
   const RopeOp<T> b{static_cast<const T *>(x1), static_cast<T *>(y1), H1};
   constexpr int V16 = 16 / sizeof(T);  // elements per 16 bytes
   bool al = aligned16(x0) && aligned16(y0) && aligned16(cos) && aligned16(sin);
   if (H1 > 0) al = al && aligned16(x1) && aligned16(y1);
   if (app.kc) al = al && aligned16(app.kc) && aligned16(app.vc) && aligned16(app.v);
+  const bool vec = al && h2 % V16 == 0;
+  const size_t total = rows * (h2 / (vec ? V16 : 1));  // threads
+  const unsigned bs = total <= 64 * 256 ? 64 : kRopeThreads;
+  size_t nb = (total + bs - 1) / bs;
+  if (nb > 65535 * 4) nb = 65535 * 4;
+  const dim3 grid(static_cast<unsigned>(nb)), block(bs);
   const bool i32 = rows * h2 < (size_t(1) << 31);
-  if (al && h2 % V16 == 0) {
+  if (vec) {
     if (i32)
-      hipLaunchKernelGGL((k_rope<T, V16, uint32_t>), dim3(grid_for(V16)), dim3(128), 0, s, a, b,
-                         app, cos, sin, B, C, D, Bt);
+      hipLaunchKernelGGL((k_rope<T, V16, uint32_t>), grid, block, 0, s, a, b, app, cos, sin, B, C,
+                         D, Bt);
     else
-      hipLaunchKernelGGL((k_rope<T, V16, size_t>), dim3(grid_for(V16)), dim3(128), 0, s, a, b,
-                         app, cos, sin, B, C, D, Bt);
+      hipLaunchKernelGGL((k_rope<T, V16, size_t>), grid, block, 0, s, a, b, app, cos, sin, B, C, D,
+                         Bt);
   } else {
     if (i32)
-      hipLaunchKernelGGL((k_rope<T, 1, uint32_t>), dim3(grid_for(1)), dim3(128), 0, s, a, b, app,
-                         cos, sin, B, C, D, Bt);
+      hipLaunchKernelGGL((k_rope<T, 1, uint32_t>), grid, block, 0, s, a, b, app, cos, sin, B, C, D,
+                         Bt);
     else
-      hipLaunchKernelGGL((k_rope<T, 1, size_t>), dim3(grid_for(1)), dim3(128), 0, s, a, b, app,
-                         cos, sin, B, C, D, Bt);
+      hipLaunchKernelGGL((k_rope<T, 1, size_t>), grid, block, 0, s, a, b, app, cos, sin, B, C, D,
+                         Bt);
   }
   return hipGetLastError();
 }

@@ -302,7 +302,7 @@ def tail_sweep(out_path, reps=20):
     for r in rows:
         print(f"| {r['n_tail']} | {r['padded_us']} | {r['scalar_us']} | {r['scalar_us_per_token']} |")
     print(f"breakeven: padding wins from {even} tail tokens on this GPU "
-          f"(the pages' threshold: pad from {path.PAD_FROM})")
+          f"(the pages' threshold: pad from {path.PAGES_PAD_FROM}; the default here: {path.PAD_FROM})")
     if out_path:
         with open(out_path, "w") as f:
             for r in rows:
@@ -452,7 +452,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="c5", choices=sorted(WORKLOADS))
     ap.add_argument("--eager", action="store_true", help="time eager launches, not a graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -540,7 +540,10 @@ def main():
         mode = "hip-graph"
         del g
 
-    value = tokens_per_layer * nl / (ms_per_step * 1e-3) / nl  # tok/s per layer
+    # tok/s per layer: the real tokens one layer takes per step over the mean time of one
+    # layer's hot path (step time / layers); the whole stack passes value / nl tokens/s
+    value = tokens_per_layer * nl / (ms_per_step * 1e-3)
+    stack_tok_s = tokens_per_layer / (ms_per_step * 1e-3)
 
     # dominant kernel: the attention call, timed alone (graph of back-to-back launches)
     lay_dom = max(layers, key=lambda l: algorithmic(l.cfg)[1])
@@ -574,6 +577,8 @@ def main():
         "dtype": "f32" if cfg0.dtype == I.F32 else "bf16", "data": "synthetic",
         "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}",
                    "layers_per_step": nl, "real_tokens_per_layer": tokens_per_layer,
+                   "value_is": "real tokens per layer x layers per step / step time",
+                   "stack_tok_per_s": round(stack_tok_s, 1),
                    "launch": mode, "eager_ms_per_step": round(eager_ms, 6),
                    "attn_flags": args.attn_flags},
         "roofline": roof,

@@ -37,9 +37,12 @@ struct Live {
 __device__ __forceinline__ Live live_geometry(int seen, int cap, int ring, int sink) {
   Live g;
   if (!ring) {
+    // every position is live in its own slot; the first `sink` of them are the sink
+    // rows (attended regardless of the window), so the tile lists visit them even when
+    // the window starts far later.  Column c is still position c (lo == ns).
     g.L = seen;
-    g.ns = 0;
-    g.lo = 0;
+    g.ns = seen < sink ? seen : sink;
+    g.lo = g.ns;
     return g;
   }
   const int R = cap - sink;

@@ -16,8 +16,8 @@ Every step runs in libcp's kernels; this module only sequences the calls.
 
 The tail of a prompt (fewer real tokens than a chunk) runs either as one padded
 chunk or token by token -- one-token steps, the decode contract of [TICO]
-"Runtime behavior" -- chosen by `pad_tail` ([cactus] "Fix": pad from 9 tokens,
-with a kill switch that forces token by token).
+"Runtime behavior" -- chosen by `pad_tail` ([cactus] "Fix": pad from the measured
+breakeven, with a kill switch that forces token by token).
 """
 import dataclasses
 import os
@@ -87,16 +87,21 @@ def chunk_step(cache: cp.KVCache, q, k, v, cos, sin, n_valid, bufs: StepBuffers,
 
 # ------------------------------------------------------------- prompt tails
 
-PAD_FROM = 9  # [cactus] "Fix": tails of up to 8 tokens stay token by token
+# Smallest tail that runs as one padded chunk.  [cactus] "Fix" and its review sweep
+# table: on an Apple M4 Pro the padded chunk won from 9 tail tokens (PAGES_PAD_FROM).
+# The same sweep on MI355X (`bench.py --tail-sweep`, a 512-window ring holding 1023
+# positions, C 128, H8/KV1 D256) measured a one-token step at ~20.5 us and a padded
+# 128-row chunk at ~31.5 us, so padding wins from 2 tail tokens there.
+PAGES_PAD_FROM = 9
+PAD_FROM = 2
 KILL_SWITCH = "CP_DISABLE_PREFILL_TAIL_PAD"
 
 
 def pad_tail(n_tail: int, pad_from: int = PAD_FROM) -> bool:
     """Tail policy: True runs a tail of n_tail real tokens as one padded chunk, False token
     by token.  The environment variable CP_DISABLE_PREFILL_TAIL_PAD=1 (any value but
-    empty or 0) forces token by token.  `pad_from` is the hardware's breakeven; the
-    default is the pages' (measured on another machine) -- `bench.py --tail-sweep`
-    measures it on this one."""
+    empty or 0) forces token by token.  `pad_from` is the hardware's breakeven: the
+    default is the one measured on MI355X; PAGES_PAD_FROM is the pages' own."""
     if os.environ.get(KILL_SWITCH, "") not in ("", "0"):
         return False
     return n_tail >= pad_from

@@ -104,8 +104,10 @@ typedef void *cp_stream_t; /* hipStream_t */
  *           Live rows: global [0, seen); ring the sink rows below
  *           min(sink, seen) and positions [max(sink, seen - (cap - sink)), seen).
  *   status  device int32 or NULL: sticky CP_DEV_* error bits.
- *   sink    pinned rows of a ring (0 for none); they are never evicted and are
- *           attended regardless of the window.
+ *   sink    pinned rows (0 for none): positions below sink are attended
+ *           regardless of the window.  A ring never evicts them; a global cache
+ *           never evicts anything, so there it only widens what a windowed
+ *           attention reads.
  */
 typedef struct cp_cache {
   void *k;
@@ -324,8 +326,11 @@ size_t cp_attn_workspace_bytes(const cp_cache *cache, const cp_attn_args *args);
  * Grouped-query attention of the chunk over the live past plus the C chunk
  * keys, softmax(scale * q.k + mask) v, fp32 accumulation (bf16 matrix
  * cores for CP_BF16).  See cp_attn_args.
- * Errors: CP_ERR_ARG, CP_ERR_SHAPE (H % nKV, D not in {64, 128, 256} for
- *         bf16 or D > 256, C < 0), CP_ERR_DTYPE, CP_ERR_HIP.
+ * Kernels: bf16 with D in {64, 128, 256} (and 16-byte aligned tensors) runs on
+ * the matrix cores; fp32, and bf16 with any other D up to 256, on the vector-ALU
+ * kernel.
+ * Errors: CP_ERR_ARG, CP_ERR_SHAPE (H % nKV, D > 256, C > cap for a global
+ *         cache), CP_ERR_DTYPE, CP_ERR_HIP.
  */
 int cp_attn_chunk_with_past(const cp_cache *cache, const cp_attn_args *args, cp_stream_t stream);
 

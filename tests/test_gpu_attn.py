@@ -94,6 +94,12 @@ SMALL = [
          window=64, seen=[150], n_valid=[20]),
     dict(name="odd_d40", dtype=I.BF16, B=1, H=4, nKV=1, D=40, C=12, cap=50, seen=[9],
          n_valid=[12]),
+    # a global cache with sink rows and a window that starts far past them: the sink
+    # tiles must still be visited (sequence 1: the chunk's own first rows are sinks)
+    dict(name="global_sink_window", dtype=I.BF16, B=2, H=4, nKV=1, D=128, C=32, cap=600,
+         sink=4, window=64, seen=[500, 2], n_valid=[32, 20]),
+    dict(name="global_sink_window_d256", dtype=I.BF16, B=1, H=8, nKV=1, D=256, C=24, cap=400,
+         sink=2, window=40, seen=[300], n_valid=[21]),
     # C * G <= 64: the matrix-core kernel's small-rows configuration
     dict(name="small_c16_d128", dtype=I.BF16, B=2, H=8, nKV=2, D=128, C=16, cap=300,
          seen=[100, 250], n_valid=[16, 9]),
@@ -122,7 +128,7 @@ def test_attention_matches_oracle(cp, kw, mode, kernel, split):
     assert int(status.item()) == 0
 
 
-@pytest.mark.parametrize("kw", SMALL[:6] + SMALL_ROWS, ids=lambda c: c["name"])
+@pytest.mark.parametrize("kw", SMALL[:6] + SMALL[10:12] + SMALL_ROWS, ids=lambda c: c["name"])
 @pytest.mark.parametrize("kernel", [0, 2])
 def test_explicit_mask_equals_inkernel_bitwise(cp, kw, kernel):
     """On the same key partition with the mask evaluated on every tile (no split,
@@ -275,22 +281,51 @@ def test_workload_c4_full(cp):
     assert int(status.item()) == 0
 
 
-@pytest.mark.parametrize("layer", [0, 5])
-def test_workload_c5_sampled_rows(cp, layer):
-    """Long context (32768 past, C = 512): rows sampled across the chunk, every head."""
+# Chunk rows of the long-context workload checked one by one against the oracle: every
+# 8th row, and both sides of every 64-row boundary (a D = 128 query tile holds the 4 heads
+# of a KV head times 64 chunk rows), of the 32-row accumulator groups at 31/32, and the
+# first and last rows.
+C5_ROWS = sorted(set(range(0, 512, 8)) | {1, 31, 32, 255, 256, 510, 511}
+                 | {64 * t - 1 for t in range(1, 9)} | {64 * t for t in range(8)})
+
+
+@pytest.mark.parametrize("layer", [0, 3, 5])
+def test_workload_c5_path_rows(cp, layer):
+    """Long context (B = 4, 32768 past, C = 512, H32/KV8 D128): one layer's whole step
+    in the launch sequence the benchmark times (RoPE of Q and K, attention, append; for
+    the global layer RoPE with the early append and the attention advancing seen).  Every
+    sequence and head on C5_ROWS against the oracle; the selection is the last row; the
+    cache ends byte-identical to the oracle's append on its live slots."""
+    from chunked_prefill_attention_rope_amd import path
     cfg = I.config("c5", layer)
     t, cache, status = _setup(cp, cfg, nan_dead=(layer == 5))
-    out, _ = _run(cp, cfg, t, cache)
-    rows = [0, 1, 31, 32, 255, 300, 510, 511]
-    ref = O.attn(_np(t["q"][:1]), _np(t["k"][:1]), _np(t["v"][:1]), _np(t["kc"][:1]),
-                 _np(t["vc"][:1]), _np(t["seen"][:1]), _np(t["n_valid"][:1]), None, cfg.ring,
-                 cfg.sink, cfg.window, cfg.scale, rows=rows)
-    got = to_f64(out)[:1]
+    d = {n: dev(t[n]) for n in ("q", "k", "v", "cos", "sin", "n_valid")}
+    bufs = path.make_buffers(cache, d["q"], d["k"], d["v"], window=cfg.window)
+    out, sel = path.chunk_step(cache, d["q"], d["k"], d["v"], d["cos"], d["sin"], d["n_valid"],
+                               bufs, window=cfg.window)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    qr = O.rope(_np(t["q"]), _np(t["cos"]), _np(t["sin"]))
+    kr = O.rope(_np(t["k"]), _np(t["cos"]), _np(t["sin"]))
+    np.testing.assert_array_equal(bits(bufs.k_rot), kr.view(np.uint8).reshape(bits(bufs.k_rot).shape))
+    ref = O.attn(qr, kr, _np(t["v"]), _np(t["kc"]), _np(t["vc"]), _np(t["seen"]),
+                 _np(t["n_valid"]), None, cfg.ring, cfg.sink, cfg.window, cfg.scale,
+                 rows=C5_ROWS)
+    got = to_f64(out)
     m = np.zeros(got.shape[:3], dtype=bool)
-    m[:, :, rows] = True
+    m[:, :, C5_ROWS] = True
+    assert m.sum() == cfg.B * cfg.H * len(C5_ROWS)
     err = rowwise_rel_err(got, ref, m)
     assert err <= TOL[I.BF16], err
-    assert int(status.item()) == 0
+    np.testing.assert_array_equal(bits(sel), bits(out[:, :, cfg.C - 1]))
+    ko, vo, so, live = O.kv_append(_np(t["kc"]), _np(t["vc"]), _np(t["seen"]), kr, _np(t["v"]),
+                                   _np(t["n_valid"]), cfg.ring, cfg.sink)
+    assert cache.seen.cpu().tolist() == so.tolist()
+    kg, vg = cache.k.cpu(), cache.v.cpu()
+    for b in range(cfg.B):
+        sl = torch.from_numpy(np.nonzero(live[b])[0])
+        assert torch.equal(kg[b][:, sl], I.from_np(ko[b])[:, sl])
+        assert torch.equal(vg[b][:, sl], I.from_np(vo[b])[:, sl])
 
 
 MERGE = [
@@ -300,6 +335,8 @@ MERGE = [
          n_valid=[3]),
     dict(name="decode_d256_window", dtype=I.BF16, B=1, H=8, nKV=1, D=256, C=1, cap=2048,
          window=1500, seen=[2000], n_valid=[1]),
+    dict(name="decode_d128_global_sink", dtype=I.BF16, B=1, H=8, nKV=2, D=128, C=1, cap=3000,
+         sink=4, window=1000, seen=[2900], n_valid=[1]),
 ]
 
 

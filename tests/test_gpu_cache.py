@@ -271,6 +271,7 @@ def test_global_cache_padded_append_rollback(cp):
     dict(ring=0, cap=96, seen=[40, 70], window=9),
     dict(ring=1, cap=32, seen=[7, 90], window=32),
     dict(ring=1, cap=32, sink=3, seen=[2, 90], window=20),
+    dict(ring=0, cap=96, sink=3, seen=[70, 2], window=9),
 ])
 def test_build_mask_bit_exact(cp, kw):
     cfg = I.small(dtype=I.BF16, B=2, H=3, nKV=1, D=64, C=16, n_valid=[16, 9], **kw)
@@ -284,10 +285,19 @@ def test_build_mask_bit_exact(cp, kw):
 
 
 @pytest.mark.parametrize("dtype", [I.F32, I.BF16])
-def test_select_row_bit_exact(cp, dtype):
-    x = torch.randn((3, 4, 16, 256)).to(torch.float32 if dtype == I.F32 else torch.bfloat16)
-    idx = torch.tensor([16, 1, 0], dtype=torch.int32)
-    y = cp.select_row(dev(x), dev(idx), -1)
-    assert torch.equal(y.cpu()[0], x[0, :, 15])
-    assert torch.equal(y.cpu()[1], x[1, :, 0])
-    assert (y.cpu()[2] == 0).all()  # n_valid = 0: no real row
+@pytest.mark.parametrize("off", [-1, 0, 2])
+def test_select_row_bit_exact(cp, dtype, off):
+    """cp_select_row against the oracle's orc_select_row: the selected rows are the same
+    values bit for bit (both widen exactly to fp64 for the comparison, signs of zero
+    included), rows outside [0, C) give zeros."""
+    g = torch.Generator("cpu").manual_seed(31 + off)
+    x = torch.randn((5, 4, 16, 256), generator=g).to(
+        torch.float32 if dtype == I.F32 else torch.bfloat16)
+    x[1, :, 0, :8] = -0.0
+    idx = torch.tensor([16, 1, 0, 15, 20], dtype=torch.int32)
+    y = cp.select_row(dev(x), dev(idx), off)
+    torch.cuda.synchronize()
+    got = y.cpu().double().numpy()
+    ref = O.select_row(x.double().numpy(), idx.numpy(), off)
+    np.testing.assert_array_equal(got, ref)
+    np.testing.assert_array_equal(np.signbit(got), np.signbit(ref))

@@ -91,20 +91,75 @@ def test_prefill_tail_follows_the_policy(mods, monkeypatch):
                   seen=[30], n_valid=[3])
     t = I.make_layer(cfg)
     q, k, v, cos, sin = (dev(t[n]) for n in ("q", "k", "v", "cos", "sin"))
-    c = _cache(cp, cfg, t)
-    bufs = path.make_buffers(c, q, k, v, window=cfg.window, static_append=True)
-    steps = path.token_steps(c, q, k, v, cos, sin, 3, window=cfg.window)
+    nv = dev(t["n_valid"])
     monkeypatch.delenv(path.KILL_SWITCH, raising=False)
-    mode, _, _ = path.prefill_tail(c, q, k, v, cos, sin, dev(t["n_valid"]), 3, bufs, steps,
-                                   window=cfg.window, static_append=True)
-    assert mode == "scalar"
-    c2 = _cache(cp, cfg, t)
-    mode, _, _ = path.prefill_tail(c2, q, k, v, cos, sin, dev(t["n_valid"]), 3, bufs, steps,
-                                   window=cfg.window, static_append=True, pad_from=2)
-    assert mode == "padded"
+
+    def run(n_tail, **kw):
+        c = _cache(cp, cfg, t)
+        bufs = path.make_buffers(c, q, k, v, window=cfg.window, static_append=True)
+        steps = path.token_steps(c, q, k, v, cos, sin, n_tail, window=cfg.window)
+        n = torch.full_like(nv, n_tail)
+        mode, _, _ = path.prefill_tail(c, q, k, v, cos, sin, n, n_tail, bufs, steps,
+                                       window=cfg.window, static_append=True, **kw)
+        return mode
+
+    # the default is the MI355X breakeven: one token stays a decode step, two are padded
+    assert run(1) == "scalar"
+    assert run(3) == "padded"
+    # the pages' threshold keeps tails below 9 token by token
+    assert run(3, pad_from=path.PAGES_PAD_FROM) == "scalar"
     monkeypatch.setenv(path.KILL_SWITCH, "1")
-    c3 = _cache(cp, cfg, t)
-    mode, _, _ = path.prefill_tail(c3, q, k, v, cos, sin, dev(t["n_valid"]), 3, bufs, steps,
-                                   window=cfg.window, static_append=True, pad_from=2)
-    assert mode == "scalar"
+    assert run(3) == "scalar"
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("seen", [1023, 896])
+def test_c3_tail_scalar_equals_padded(mods, seen):
+    """The sliding-window workload at its own size ([cactus] "Problem" and the review
+    hardening: the padded tail must give the scalar tail's outputs): a 512-window ring that
+    has absorbed `seen` positions (1023: the ring holds 511..1022; 896: the page's
+    1023-token prompt after its seventh full chunk), a 127-token tail run as one padded
+    128-row chunk with snapshot/rollback and as 127 one-token steps.  Real-row outputs
+    match the oracle and each other, the selections are the last real row, and both
+    caches end byte-identical to the oracle's exact append of the 127 rows."""
+    cp, path = mods
+    cfg = I.config("c3")
+    cfg.seen = [seen]
+    t = I.make_layer(cfg)
+    n_tail = cfg.n_valid[0]
+    assert (cfg.C, cfg.cap, n_tail) == (128, 512, 127)
+    q, k, v, cos, sin = (dev(t[n]) for n in ("q", "k", "v", "cos", "sin"))
+    nv = dev(t["n_valid"])
+
+    padded = _cache(cp, cfg, t)
+    bufs = path.make_buffers(padded, q, k, v, window=cfg.window, static_append=True)
+    out_p, sel_p = path.chunk_step(padded, q, k, v, cos, sin, nv, bufs, window=cfg.window,
+                                   static_append=True)
+    scalar = _cache(cp, cfg, t)
+    steps = path.token_steps(scalar, q, k, v, cos, sin, n_tail, window=cfg.window)
+    outs, sel_s = path.scalar_tail(scalar, steps, window=cfg.window)
+    torch.cuda.synchronize()
+
+    qr = O.rope(I.np_view(t["q"]), I.np_view(t["cos"]), I.np_view(t["sin"]))
+    kr = O.rope(I.np_view(t["k"]), I.np_view(t["cos"]), I.np_view(t["sin"]))
+    ref = O.attn(qr, kr, I.np_view(t["v"]), I.np_view(t["kc"]), I.np_view(t["vc"]),
+                 I.np_view(t["seen"]), I.np_view(t["n_valid"]), None, cfg.ring, cfg.sink,
+                 cfg.window, cfg.scale)[:, :, :n_tail]
+    got_p = to_f64(out_p)
+    got_s = np.concatenate([to_f64(o) for o in outs], axis=2)
+    assert rowwise_rel_err(got_p[:, :, :n_tail], ref) <= TOL[I.BF16]
+    assert rowwise_rel_err(got_s, ref) <= TOL[I.BF16]
+    assert rowwise_rel_err(got_s, got_p[:, :, :n_tail]) <= TOL[I.BF16]
+    assert (got_p[:, :, n_tail:] == 0).all()  # the pad row is written as zeros
+    np.testing.assert_array_equal(bits(sel_p), bits(out_p[:, :, n_tail - 1]))
+    np.testing.assert_array_equal(bits(sel_s), bits(outs[-1][:, :, 0]))
+
+    ko, vo, so, live = O.kv_append(I.np_view(t["kc"]), I.np_view(t["vc"]), I.np_view(t["seen"]),
+                                   kr, I.np_view(t["v"]), I.np_view(t["n_valid"]), cfg.ring,
+                                   cfg.sink)
+    assert so.tolist() == [seen + n_tail]
+    assert live.sum() == 512  # a full window: every slot is live
+    for c in (padded, scalar):
+        assert c.seen.cpu().tolist() == so.tolist()
+        np.testing.assert_array_equal(bits(c.k), ko.view(np.uint8).reshape(bits(c.k).shape))
+        np.testing.assert_array_equal(bits(c.v), vo.view(np.uint8).reshape(bits(c.v).shape))

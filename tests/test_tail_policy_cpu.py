@@ -1,5 +1,6 @@
-"""Tail policy of the prompt-tail driver ([cactus] "Fix": tails of up to 8 tokens stay
-token by token, padding from 9; a kill switch forces token by token).  Host logic only."""
+"""Tail policy of the prompt-tail driver ([cactus] "Fix": short tails stay token by token,
+longer ones run as one padded chunk, from the hardware's measured breakeven -- 9 tokens on
+the page's M4 Pro, 2 on MI355X; a kill switch forces token by token).  Host logic only."""
 import pytest
 
 
@@ -10,10 +11,17 @@ def path(monkeypatch):
     return mod
 
 
-def test_pad_from_nine(path):
-    assert path.PAD_FROM == 9
-    assert [path.pad_tail(n) for n in (1, 7, 8)] == [False, False, False]
-    assert [path.pad_tail(n) for n in (9, 10, 127)] == [True, True, True]
+def test_default_is_the_mi355x_breakeven(path):
+    assert path.PAD_FROM == 2
+    assert not path.pad_tail(1)
+    assert [path.pad_tail(n) for n in (2, 3, 8, 9, 127)] == [True] * 5
+
+
+def test_pages_threshold(path):
+    # [cactus] review: tails of up to 8 tokens stay token by token on the M4 Pro
+    assert path.PAGES_PAD_FROM == 9
+    assert [path.pad_tail(n, pad_from=path.PAGES_PAD_FROM) for n in (1, 7, 8)] == [False] * 3
+    assert [path.pad_tail(n, pad_from=path.PAGES_PAD_FROM) for n in (9, 10, 127)] == [True] * 3
 
 
 def test_threshold_is_a_parameter(path):

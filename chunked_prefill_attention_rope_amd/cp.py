@@ -17,6 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libcp.so")
 
 OK, ERR_ARG, ERR_SHAPE, ERR_DTYPE, ERR_WINDOW, ERR_STATE, ERR_WORKSPACE, ERR_HIP = (
     0, -1, -2, -3, -4, -5, -6, -7)
+ERR_SCRATCH = -8
+ATTN_SCRATCH_BYTES = 64 << 20  # CP_ATTN_SCRATCH_BYTES
 DEV_OVERFLOW, DEV_NVALID, DEV_MASK_LD, DEV_ROLLBACK, DEV_SEEN = 1, 2, 4, 8, 16
 F32, BF16 = 0, 1
 ATTN_NO_SPLIT, ATTN_FORCE_GENERIC, ATTN_FULL_TILES, ATTN_ADVANCE_SEEN = 1, 2, 4, 8
@@ -73,6 +75,7 @@ _SIGS = {
     "cp_kv_rollback_padded_append": (_i, [_P(CacheDesc), _P(SnapshotDesc), _vp]),
     "cp_attn_workspace_bytes": (ctypes.c_size_t, [_P(CacheDesc), _P(AttnArgs)]),
     "cp_attn_chunk_with_past": (_i, [_P(CacheDesc), _P(AttnArgs), _vp]),
+    "cp_attn_chunk_with_past_noalloc": (_i, [_P(CacheDesc), _P(AttnArgs), _vp]),
     "cp_build_mask": (_i, [_vp, ctypes.c_int64, _P(CacheDesc), _vp, _i, _i, _i, _vp]),
     "cp_select_row": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "cp_gdn_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i, _i]),
@@ -339,6 +342,24 @@ def attn_chunk_with_past(cache: KVCache, q: torch.Tensor, k_new: torch.Tensor,
                    select_out)
     _check(_lib.cp_attn_chunk_with_past(ctypes.byref(cache.desc), ctypes.byref(a), _stream()),
            "cp_attn_chunk_with_past")
+    return out
+
+
+def attn_chunk_with_past_noalloc(cache: KVCache, q: torch.Tensor, k_new: torch.Tensor,
+                                 v_new: torch.Tensor, out: torch.Tensor,
+                                 n_valid: Optional[torch.Tensor] = None,
+                                 mask: Optional[torch.Tensor] = None, window: int = 0,
+                                 scale: Optional[float] = None, flags: int = 0,
+                                 select_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """cp_attn_chunk_with_past_noalloc: the same attention with the key-split partials in
+    the library's own device array (no workspace; the caller passes its output)."""
+    if select_out is not None and (select_out.dtype != q.dtype or
+                                   select_out.shape != (q.shape[0], q.shape[1], q.shape[3])):
+        raise ValueError("select_out must be [B, H, D] of q's dtype")
+    a = _attn_args(cache, q, k_new, v_new, out, n_valid, mask, window, scale, None, flags,
+                   select_out)
+    _check(_lib.cp_attn_chunk_with_past_noalloc(ctypes.byref(cache.desc), ctypes.byref(a),
+                                                _stream()), "cp_attn_chunk_with_past_noalloc")
     return out
 
 

@@ -4,10 +4,17 @@
 // checked before anything is enqueued), the attention plan (kernel choice,
 // query tiling, key splits), and the launches.  No allocation, no global
 // mutable state, no stream synchronisation.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "attn_common.h"
+
+// Key-split partials of cp_attn_chunk_with_past_noalloc.  Host code never uses this
+// name as a device address (in host code it is only a stand-in for the symbol): the
+// address comes from hipGetSymbolAddress, once per device (scratch_on_current_device).
+static __device__ __align__(256) unsigned char scratch[CP_ATTN_SCRATCH_BYTES];
 
 namespace cp {
 int mfma_keys_per_tile(int D, bool explicit_tiling, int small_rows);
@@ -36,6 +43,28 @@ int check_cache(const cp_cache *c) {
 }
 
 size_t round256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Device address of `scratch` on each device, resolved on the first call that needs it
+// with that device current (each GPU holds its own copy of the array).
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_on_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CP_ERR_HIP;
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CP_ERR_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return CP_OK;
+}
 
 }  // namespace
 
@@ -207,6 +236,9 @@ const char *cp_status_str(int status) {
       return "workspace or snapshot buffer too small";
     case CP_ERR_HIP:
       return "HIP runtime error";
+    case CP_ERR_SCRATCH:
+      return "the call's key splits need more than the library's fixed scratch array "
+             "(CP_ATTN_SCRATCH_BYTES); use cp_attn_chunk_with_past with a workspace";
     default:
       return "unknown status";
   }
@@ -353,6 +385,24 @@ int cp_attn_chunk_with_past(const cp_cache *cache, const cp_attn_args *args, cp_
   const int st = check_attn(cache, args);
   if (st != CP_OK) return st;
   return to_status(launch_attention(*cache, *args, static_cast<hipStream_t>(stream)));
+}
+
+int cp_attn_chunk_with_past_noalloc(const cp_cache *cache, const cp_attn_args *args,
+                                    cp_stream_t stream) {
+  int st = check_attn(cache, args);
+  if (st != CP_OK) return st;
+  // the plan the call would take with an unlimited workspace, and what its splits need
+  const size_t need = attn_workspace_bytes(*cache, *args, plan_attention(*cache, *args, true));
+  if (need > CP_ATTN_SCRATCH_BYTES) return CP_ERR_SCRATCH;
+  cp_attn_args a = *args;
+  a.workspace = nullptr;
+  a.workspace_bytes = 0;
+  if (need > 0) {
+    st = scratch_on_current_device(&a.workspace);
+    if (st != CP_OK) return st;
+    a.workspace_bytes = CP_ATTN_SCRATCH_BYTES;
+  }
+  return to_status(launch_attention(*cache, a, static_cast<hipStream_t>(stream)));
 }
 
 int cp_build_mask(float *mask, int64_t ld, const cp_cache *cache, const int32_t *n_valid, int H,

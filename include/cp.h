@@ -79,6 +79,7 @@ typedef void *cp_stream_t; /* hipStream_t */
 #define CP_ERR_STATE (-5)     /* rollback without a matching, armed snapshot */
 #define CP_ERR_WORKSPACE (-6) /* workspace or snapshot buffer too small */
 #define CP_ERR_HIP (-7)       /* the HIP runtime refused a launch */
+#define CP_ERR_SCRATCH (-8)   /* the call needs more than the library's fixed scratch array */
 
 /* ---- bits the kernels OR into cache->status (device int32) ---- */
 #define CP_DEV_OVERFLOW 1 /* global append would pass cap: that sequence was not appended */
@@ -333,6 +334,30 @@ size_t cp_attn_workspace_bytes(const cp_cache *cache, const cp_attn_args *args);
  *         cache), CP_ERR_DTYPE, CP_ERR_HIP.
  */
 int cp_attn_chunk_with_past(const cp_cache *cache, const cp_attn_args *args, cp_stream_t stream);
+
+/*
+ * For callers that cannot allocate device memory (code being captured into a HIP
+ * graph whose owner forbids allocation, tight serving loops, harnesses that ban
+ * hipMalloc): cp_attn_chunk_with_past with the key-split partials kept in a
+ * device array that the library owns, instead of a caller workspace.  The array
+ * holds CP_ATTN_SCRATCH_BYTES on each GPU the library runs on, from the first
+ * call on that device (the current device, which must own `stream`) until the
+ * process ends.  args->workspace and args->workspace_bytes are ignored; every
+ * other argument, output and error is as for cp_attn_chunk_with_past, and the
+ * outputs are bit-identical to it.  The call allocates nothing.
+ * Every call on one GPU shares that GPU's array and leaves its partials there:
+ * calls that may overlap on one GPU (different streams, or different host
+ * threads without ordering) race and must be ordered by the caller.  Nothing in
+ * the array needs clearing between calls (each call writes every partial it
+ * reads).
+ * Errors: those of cp_attn_chunk_with_past; CP_ERR_SCRATCH (nothing enqueued)
+ *         when the call's key splits need more than CP_ATTN_SCRATCH_BYTES
+ *         (cp_attn_workspace_bytes() gives the need); CP_ERR_HIP if the
+ *         array's device address cannot be obtained.
+ */
+#define CP_ATTN_SCRATCH_BYTES (64u << 20)
+int cp_attn_chunk_with_past_noalloc(const cp_cache *cache, const cp_attn_args *args,
+                                    cp_stream_t stream);
 
 /*
  * Materialise the explicit mask from the in-kernel rule ([SKaiNET] mask

@@ -58,7 +58,7 @@ def test_binding_loads_and_struct_sizes_match(cp):
 
 
 def test_status_strings(cp):
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         assert cp.status_str(code) and cp.status_str(code) != "unknown status"
     assert cp.status_str(-99) == "unknown status"
 
@@ -160,6 +160,17 @@ def test_attention_validation(cp):
     big = _cache(cp, D=512)
     assert f(ctypes.byref(big), ctypes.byref(args()), None) == cp.ERR_SHAPE
     assert lib.cp_attn_workspace_bytes(ctypes.byref(c), ctypes.byref(args(H=7))) == 0
+    # the non-allocating form validates identically, before it looks at its scratch
+    g = lib.cp_attn_chunk_with_past_noalloc
+    assert g(ctypes.byref(c), ctypes.byref(args(q=None)), None) == cp.ERR_ARG
+    assert g(ctypes.byref(c), ctypes.byref(args(H=7)), None) == cp.ERR_SHAPE
+    assert g(ctypes.byref(big), ctypes.byref(args()), None) == cp.ERR_SHAPE
+    # splits needing more than the fixed array are refused before any device call:
+    # 64 forced splits of B=64 x 8 KV heads x 16 query tiles of 128 rows x D 256 fp32
+    huge = _cache(cp, B=64, nKV=8, cap=8192, D=256)
+    a = args(H=32, C=512, flags=cp.ATTN_SPLITS(64))
+    assert lib.cp_attn_workspace_bytes(ctypes.byref(huge), ctypes.byref(a)) > cp.ATTN_SCRATCH_BYTES
+    assert g(ctypes.byref(huge), ctypes.byref(a), None) == cp.ERR_SCRATCH
 
 
 def test_select_and_mask_validation(cp):

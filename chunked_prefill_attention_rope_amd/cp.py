@@ -70,6 +70,9 @@ _SIGS = {
     "cp_kv_advance": (_i, [_P(CacheDesc), _i, _vp, _vp]),
     "cp_rope_qk_append_chunk": (_i, [_P(CacheDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i,
                                      _i, _vp, _vp]),
+    "cp_rope_qk_snapshot_chunk": (_i, [_P(CacheDesc), _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
+                                       _vp, _P(SnapshotDesc), _vp]),
+    "cp_kv_append_rollback": (_i, [_P(CacheDesc), _vp, _vp, _i, _P(SnapshotDesc), _vp]),
     "cp_snapshot_bytes": (ctypes.c_size_t, [_P(CacheDesc), _i]),
     "cp_kv_snapshot_padded_append": (_i, [_P(CacheDesc), _i, _vp, _P(SnapshotDesc), _vp]),
     "cp_kv_rollback_padded_append": (_i, [_P(CacheDesc), _P(SnapshotDesc), _vp]),
@@ -287,6 +290,41 @@ def kv_snapshot_padded_append(cache: KVCache, C: int, n_valid: Optional[torch.Te
 def kv_rollback_padded_append(cache: KVCache, snap: Snapshot) -> None:
     _check(_lib.cp_kv_rollback_padded_append(ctypes.byref(cache.desc), ctypes.byref(snap.desc),
                                              _stream()), "cp_kv_rollback_padded_append")
+
+
+def rope_qk_snapshot_chunk(cache: KVCache, q: Optional[torch.Tensor], k: torch.Tensor,
+                           cos: torch.Tensor, sin: torch.Tensor,
+                           n_valid: Optional[torch.Tensor], snap: Snapshot,
+                           q_out: Optional[torch.Tensor] = None,
+                           k_out: Optional[torch.Tensor] = None):
+    """cp_rope_qk_snapshot_chunk: rotate q (None: keys only) and k, and take the padded-
+    append snapshot into snap, in one launch."""
+    if k.dtype != cache.k.dtype or k.shape[0] != cache.B or k.shape[1] != cache.nKV \
+            or k.shape[3] != cache.D:
+        raise ValueError("k must be [B, nKV, C, D] in the cache's dtype")
+    if q is not None and (q.dtype != k.dtype or q.shape[0] != k.shape[0] or
+                          q.shape[2:] != k.shape[2:]):
+        raise ValueError("q must be [B, H, C, D] of k's dtype")
+    if k_out is None:
+        k_out = torch.empty_like(k)
+    if q is not None and q_out is None:
+        q_out = torch.empty_like(q)
+    H = q.shape[1] if q is not None else 0
+    _check(_lib.cp_rope_qk_snapshot_chunk(
+        ctypes.byref(cache.desc), _opt(q, "q"), _opt(q_out, "q_out"), _dev(k, "k"),
+        _dev(k_out, "k_out"), _opt(cos, "cos", torch.float32), _opt(sin, "sin", torch.float32),
+        H, k.shape[2], cos.shape[0], _opt(n_valid, "n_valid", torch.int32),
+        ctypes.byref(snap.desc), _stream()), "cp_rope_qk_snapshot_chunk")
+    return q_out, k_out
+
+
+def kv_append_rollback(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor,
+                       snap: Snapshot) -> None:
+    """cp_kv_append_rollback: the padded append of all C rows and its rollback, one launch."""
+    _check(_lib.cp_kv_append_rollback(ctypes.byref(cache.desc), _dev(k_new, "k_new"),
+                                      _dev(v_new, "v_new"), k_new.shape[2],
+                                      ctypes.byref(snap.desc), _stream()),
+           "cp_kv_append_rollback")
 
 
 # ---------------------------------------------------------------- attention

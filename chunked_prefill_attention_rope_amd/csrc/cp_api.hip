@@ -304,6 +304,46 @@ int cp_rope_qk_append_chunk(const cp_cache *cache, const void *q, void *q_out, c
                                          n_valid, static_cast<hipStream_t>(stream)));
 }
 
+int cp_rope_qk_snapshot_chunk(const cp_cache *cache, const void *q, void *q_out, const void *k,
+                              void *k_out, const float *cos, const float *sin, int H, int C,
+                              int Bt, const int32_t *n_valid, cp_snapshot *snap,
+                              cp_stream_t stream) {
+  int st = check_cache(cache);
+  if (st != CP_OK) return st;
+  if (!snap || !snap->buf || H < 0 || C < 0) return CP_ERR_ARG;
+  if (cache->D % 2 != 0) return CP_ERR_SHAPE;
+  if (cache->ring && cache->cap <= C + cache->sink) return CP_ERR_WINDOW;
+  if (!cache->ring && C > cache->cap) return CP_ERR_SHAPE;
+  if (Bt != 1 && Bt != cache->B) return CP_ERR_ARG;
+  if (snap->bytes < cp_snapshot_bytes(cache, C)) return CP_ERR_WORKSPACE;
+  const bool rows = static_cast<size_t>(cache->B) * C > 0;
+  if (rows && (!k || !k_out || !cos || !sin || (H > 0 && (!q || !q_out)))) return CP_ERR_ARG;
+  if (cache->B > 0) {
+    st = to_status(launch_rope_qk_snapshot(*cache, q, q_out, H, k, k_out, cos, sin, C, Bt,
+                                           n_valid, snap->buf, static_cast<hipStream_t>(stream)));
+    if (st != CP_OK) return st;
+  }
+  snap->cache_k = cache->k;
+  snap->C = C;
+  snap->armed = 1;
+  return CP_OK;
+}
+
+int cp_kv_append_rollback(const cp_cache *cache, const void *k_new, const void *v_new, int C,
+                          cp_snapshot *snap, cp_stream_t stream) {
+  int st = check_cache(cache);
+  if (st != CP_OK) return st;
+  if (!snap || !snap->buf || C < 0) return CP_ERR_ARG;
+  if (!snap->armed || snap->cache_k != cache->k || snap->C != C) return CP_ERR_STATE;
+  if (snap->bytes < cp_snapshot_bytes(cache, C)) return CP_ERR_STATE;
+  if (static_cast<size_t>(cache->B) * C > 0 && (!k_new || !v_new)) return CP_ERR_ARG;
+  st = to_status(launch_append_rollback(*cache, k_new, v_new, C, snap->buf,
+                                        static_cast<hipStream_t>(stream)));
+  if (st != CP_OK) return st;
+  snap->armed = 0;
+  return CP_OK;
+}
+
 int cp_kv_advance(const cp_cache *cache, int C, const int32_t *n_rows, cp_stream_t stream) {
   int st = check_cache(cache);
   if (st != CP_OK) return st;

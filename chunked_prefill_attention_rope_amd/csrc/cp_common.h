@@ -132,6 +132,14 @@ hipError_t launch_rope_qk_append(const cp_cache &c, const void *q, void *q_out, 
                                  const void *k, void *k_out, const void *v, const float *cos,
                                  const float *sin, int C, int Bt, const int32_t *n_valid,
                                  hipStream_t s);
+// cp_rope_qk_chunk plus the padded-append snapshot, in one launch (H = 0: keys only).
+hipError_t launch_rope_qk_snapshot(const cp_cache &c, const void *q, void *q_out, int H,
+                                   const void *k, void *k_out, const float *cos, const float *sin,
+                                   int C, int Bt, const int32_t *n_valid, void *buf,
+                                   hipStream_t s);
+// A padded append of all C rows and its rollback, in one launch.
+hipError_t launch_append_rollback(const cp_cache &c, const void *k_new, const void *v_new, int C,
+                                  const void *buf, hipStream_t s);
 hipError_t launch_advance_seen(const cp_cache &c, int C, const int32_t *n_rows, hipStream_t s);
 hipError_t launch_kv_append(const cp_cache &c, const void *k_new, const void *v_new, int C,
                             const int32_t *n_rows, hipStream_t s);

@@ -293,6 +293,82 @@ __global__ void k_rollback_seen(cp_cache c, int C, const unsigned char *__restri
   c.seen[b] = s0 + nv;
 }
 
+// A padded append of all C rows followed by its rollback, in one launch and with the
+// same bytes in every slot (live or dead) and the same seen and status bits as the two
+// calls (cp_kv_append with n_rows NULL, then cp_kv_rollback_padded_append), on a cache
+// left unchanged since the snapshot:
+//  - row r < nv: the chunk row, at slot(s0 + r), as the append writes it;
+//  - pad row r >= nv at position p = s0 + r: in a ring with p >= cap its slot held the
+//    over-evicted position p - R, which the rollback writes back from the snapshot;
+//    otherwise (a global cache, or p < cap) it is the chunk's pad row, which the append
+//    writes and the rollback leaves in the dead region.
+// The pre-append seen comes from the snapshot header (s0), never from cache.seen, so
+// one thread per sequence can check that cache.seen still equals s0 and advance it to
+// s0 + nv in this launch without racing the copies.  A sequence the append would skip
+// (bad seen, global overflow) is skipped with the append's and the rollback's status
+// bits.  If cache.seen moved since the snapshot the rows are still written for s0, but
+// seen is left alone and CP_DEV_ROLLBACK is set (the two separate calls would append at
+// the moved seen instead: the cache state is then the caller's error either way).
+__device__ __forceinline__ bool padded_skip(const cp_cache &c, int s0, int C) {
+  return s0 < 0 || (!c.ring && (s0 > c.cap || s0 + C > c.cap));
+}
+
+template <typename W, typename I>
+__global__ void __launch_bounds__(256) k_append_rollback(cp_cache c, const void *__restrict__ kn,
+                                                         const void *__restrict__ vn, int C,
+                                                         const unsigned char *__restrict__ buf,
+                                                         size_t hdr, int cpr, size_t row_bytes) {
+  const int32_t *h = reinterpret_cast<const int32_t *>(buf);
+  const size_t half = static_cast<size_t>(c.B) * c.nKV * C * row_bytes;
+  const W *sk = reinterpret_cast<const W *>(buf + hdr);
+  const W *sv = reinterpret_cast<const W *>(buf + hdr + half);
+  const size_t w = row_bytes / sizeof(W);
+  const size_t gid = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x;
+  if (gid < static_cast<size_t>(c.B)) {  // bookkeeping of sequence gid
+    const int b = static_cast<int>(gid);
+    const int s0 = h[b], nv = h[c.B + b];
+    if (s0 < 0 || (!c.ring && s0 > c.cap)) {
+      flag(c.status, CP_DEV_SEEN | CP_DEV_ROLLBACK);
+    } else if (!c.ring && s0 + C > c.cap) {
+      flag(c.status, CP_DEV_OVERFLOW | CP_DEV_ROLLBACK);
+    } else if (c.seen[b] != s0) {
+      flag(c.status, CP_DEV_ROLLBACK);
+    } else {
+      c.seen[b] = s0 + nv;
+    }
+  }
+  const I total = static_cast<I>(c.B) * c.nKV * C * cpr;
+  for (I t = static_cast<I>(gid); t < total; t += static_cast<I>(gridDim.x) * blockDim.x) {
+    const I row = t / static_cast<I>(cpr);
+    const int ch = static_cast<int>(t - row * cpr);
+    const I bg = row / static_cast<I>(C);
+    const int r = static_cast<int>(row - bg * C);
+    const int b = static_cast<int>(bg / static_cast<I>(c.nKV));
+    const int s0 = h[b], nv = h[c.B + b];
+    if (padded_skip(c, s0, C)) continue;
+    const int p = s0 + r;
+    // an append longer than the window writes only the rows still live after it (the
+    // window guard of the snapshot makes this empty, kept for equality with the append)
+    if (c.ring && p >= c.sink && p < s0 + C - (c.cap - c.sink)) continue;
+    const int sl = slot_of(p, c.cap, c.ring, c.sink);
+    const size_t dst = (static_cast<size_t>(bg) * c.cap + sl) * w + ch;
+    if (r >= nv && c.ring && p >= c.cap) {
+      int lo, hi;
+      overevicted(c, s0, nv, C, &lo, &hi);
+      const int q = p - (c.cap - c.sink);  // the position the pad row displaced
+      if (q >= lo && q < hi) {
+        const size_t src = ((static_cast<size_t>(bg) * C) + (q - lo)) * w + ch;
+        static_cast<W *>(c.k)[dst] = sk[src];
+        static_cast<W *>(c.v)[dst] = sv[src];
+        continue;
+      }
+    }
+    const size_t src = static_cast<size_t>(row) * w + ch;
+    static_cast<W *>(c.k)[dst] = static_cast<const W *>(kn)[src];
+    static_cast<W *>(c.v)[dst] = static_cast<const W *>(vn)[src];
+  }
+}
+
 unsigned grid_for(size_t total) {
   size_t blocks = (total + 255) / 256;
   if (blocks > 8192) blocks = 8192;
@@ -396,6 +472,28 @@ hipError_t launch_rollback(const cp_cache &c, int C, const void *buf, hipStream_
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_rollback_seen, dim3((c.B + 255) / 256), dim3(256), 0, s, c, C, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_rollback(const cp_cache &c, const void *k_new, const void *v_new, int C,
+                                  const void *buf, hipStream_t s) {
+  if (c.B == 0) return hipSuccess;
+  const size_t rb = row_bytes_of(c);
+  const size_t hdr = snapshot_header_bytes(c.B);
+  const unsigned char *b = static_cast<const unsigned char *>(buf);
+  const bool c16 = rb % 16 == 0 && ((reinterpret_cast<uintptr_t>(k_new) |
+                                     reinterpret_cast<uintptr_t>(v_new) |
+                                     reinterpret_cast<uintptr_t>(c.k) |
+                                     reinterpret_cast<uintptr_t>(c.v)) & 15) == 0;
+  const int cpr = static_cast<int>(c16 ? rb / 16 : rb / 4);
+  const size_t total = static_cast<size_t>(c.B) * c.nKV * C * cpr;
+  // the grid always covers B threads: they do the bookkeeping, even for C == 0
+  const unsigned grid = grid_for(total > static_cast<size_t>(c.B) ? total : c.B);
+  const bool f32 = fits32(c, C, rb);
+  if (c16)
+    CP_LAUNCH_IDX(k_append_rollback, Chunk16, grid, c, k_new, v_new, C, b, hdr, cpr, rb);
+  else
+    CP_LAUNCH_IDX(k_append_rollback, uint32_t, grid, c, k_new, v_new, C, b, hdr, cpr, rb);
   return hipGetLastError();
 }
 

@@ -6,13 +6,17 @@ are appended, so a ring never loses keys the chunk's first rows still need):
     rope(Q, K) -> [snapshot] -> attention (+ selected row) -> append -> [rollback]
 
 Q and K are rotated by one launch, and the attention writes the last real row into
-the selection as it writes the output (a tiny append also updates seen in the
-same launch as its copy).
+the selection as it writes the output.  A global cache takes the chunk's K/V in the
+RoPE launch (slots the attention does not read) and the attention advances seen.  A
+ring cache takes the padded-append snapshot in the RoPE launch and the append with
+its rollback in one launch after the attention: RoPE+snapshot -> attention (+ split
+merge) -> append+rollback.
 
 ``static_append=True`` models a caller whose append always writes all C rows
 (a fixed-shape graph): the ring is protected by the padded-append snapshot and
-rollback ([cactus] "Fix").  Otherwise only the n_valid real rows are appended.
-Every step runs in libcp's kernels; this module only sequences the calls.
+rollback ([cactus] "Fix").  A ring takes that form in every case (with all rows real
+it saves nothing; with pad rows the live region equals the exact append of the real
+rows).  Every step runs in libcp's kernels; this module only sequences the calls.
 
 The tail of a prompt (fewer real tokens than a chunk) runs either as one padded
 chunk or token by token -- one-token steps, the decode contract of [TICO]
@@ -50,7 +54,7 @@ def make_buffers(cache: cp.KVCache, q: torch.Tensor, k: torch.Tensor, v: torch.T
                        sel=torch.empty((B, H, D), dtype=q.dtype, device=q.device))
     if ws:
         bufs.workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
-    if static_append:
+    if static_append or (cache.ring and cache.cap > C + cache.sink):
         bufs.snap = cp.Snapshot(torch.empty(max(cp.snapshot_bytes(cache, C), 1),
                                             dtype=torch.uint8, device=q.device))
     return bufs
@@ -65,7 +69,11 @@ def chunk_step(cache: cp.KVCache, q, k, v, cos, sin, n_valid, bufs: StepBuffers,
     rows past seen (slots this chunk's attention does not read), and the attention call
     advances seen afterwards -- the same cache bytes and outputs as RoPE, attention,
     append in sequence, without the append's launches.  A ring cache (whose append
-    evicts rows the attention still reads) keeps that sequence."""
+    evicts rows the attention still reads) appends after the attention: the RoPE
+    launch takes the padded-append snapshot, and one launch appends and rolls back
+    (the same bytes as the separate snapshot, append of all C rows and rollback).  A
+    padded global append takes the same form.  A ring whose window cannot take a
+    padded append (cap <= C + sink) appends its real rows with cp_kv_append."""
     if not cache.ring and not static_append:
         cp.rope_qk_append_chunk(cache, q, k, v, cos, sin, n_valid, q_out=bufs.q_rot,
                                 k_out=bufs.k_rot)
@@ -73,15 +81,20 @@ def chunk_step(cache: cp.KVCache, q, k, v, cos, sin, n_valid, bufs: StepBuffers,
                                 window=window, out=bufs.out, workspace=bufs.workspace,
                                 flags=flags | cp.ATTN_ADVANCE_SEEN, select_out=bufs.sel)
         return bufs.out, bufs.sel
+    C = q.shape[2]
+    if static_append or cache.cap > C + cache.sink:
+        cp.rope_qk_snapshot_chunk(cache, q, k, cos, sin, n_valid, bufs.snap, q_out=bufs.q_rot,
+                                  k_out=bufs.k_rot)
+        cp.attn_chunk_with_past(cache, bufs.q_rot, bufs.k_rot, v, n_valid=n_valid, mask=mask,
+                                window=window, out=bufs.out, workspace=bufs.workspace,
+                                flags=flags, select_out=bufs.sel)
+        cp.kv_append_rollback(cache, bufs.k_rot, v, bufs.snap)
+        return bufs.out, bufs.sel
     cp.rope_qk_chunk(q, k, cos, sin, q_out=bufs.q_rot, k_out=bufs.k_rot)
-    if static_append:
-        cp.kv_snapshot_padded_append(cache, q.shape[2], n_valid, bufs.snap)
     cp.attn_chunk_with_past(cache, bufs.q_rot, bufs.k_rot, v, n_valid=n_valid, mask=mask,
                             window=window, out=bufs.out, workspace=bufs.workspace, flags=flags,
                             select_out=bufs.sel)
-    cp.kv_append(cache, bufs.k_rot, v, None if static_append else n_valid)
-    if static_append:
-        cp.kv_rollback_padded_append(cache, bufs.snap)
+    cp.kv_append(cache, bufs.k_rot, v, n_valid)
     return bufs.out, bufs.sel
 
 

@@ -318,6 +318,45 @@ int cp_kv_snapshot_padded_append(const cp_cache *cache, int C, const int32_t *n_
  */
 int cp_kv_rollback_padded_append(const cp_cache *cache, cp_snapshot *snap, cp_stream_t stream);
 
+/*
+ * The padded ring append's two halves with fewer launches ([cactus] "Fix": the rows
+ * a padded append over-evicts are saved before it and written back after it, so the
+ * cache ends byte-identical to an unpadded prefill):
+ *
+ *   cp_rope_qk_snapshot_chunk -> cp_attn_chunk_with_past -> cp_kv_append_rollback
+ *
+ * does what cp_rope_qk_chunk -> cp_kv_snapshot_padded_append -> cp_attn_chunk_with_past
+ * -> cp_kv_append (all C rows) -> cp_kv_rollback_padded_append does, with the same
+ * bytes everywhere (rotated tensors, snapshot buffer, every cache slot, seen, status).
+ *
+ * cp_rope_qk_snapshot_chunk: cp_rope_qk_chunk (q, q_out [B, H, C, D]; k, k_out
+ * [B, nKV, C, D]; H = 0 rotates the keys only) and cp_kv_snapshot_padded_append (same
+ * snapshot layout and arming) in one launch.  B, nKV, D and the dtype come from the
+ * cache.  Safe because nothing writes the cache between the snapshot and the append.
+ * Errors: as the two calls (CP_ERR_WINDOW for a ring with cap <= C + sink,
+ *         CP_ERR_WORKSPACE, CP_ERR_ARG, CP_ERR_SHAPE, CP_ERR_DTYPE); nothing is
+ *         enqueued and the snapshot is not armed on error.
+ */
+int cp_rope_qk_snapshot_chunk(const cp_cache *cache, const void *q, void *q_out, const void *k,
+                              void *k_out, const float *cos, const float *sin, int H, int C,
+                              int Bt, const int32_t *n_valid, cp_snapshot *snap,
+                              cp_stream_t stream);
+
+/*
+ * cp_kv_append of all C rows of k_new, v_new [B, nKV, C, D] followed by
+ * cp_kv_rollback_padded_append, in one launch: the real rows land where the append
+ * puts them; a pad row whose slot held an over-evicted row gets that row back from the
+ * snapshot; the other pad rows land in the dead region as the append leaves them;
+ * seen = seen_before + n_valid.  The pre-append seen is the snapshot's, so this must
+ * follow the snapshot with no other change of the cache in between; if seen moved, the
+ * rows are written for seen_before, seen is left alone and CP_DEV_ROLLBACK is set.
+ * Disarms the snapshot.
+ * Errors: CP_ERR_STATE (snapshot not armed, from another cache, or for another C),
+ *         CP_ERR_ARG; nothing is enqueued on error.
+ */
+int cp_kv_append_rollback(const cp_cache *cache, const void *k_new, const void *v_new, int C,
+                          cp_snapshot *snap, cp_stream_t stream);
+
 /* ---- attention ---- */
 
 /* Workspace bytes that let cp_attn_chunk_with_past split keys (0 if never). */

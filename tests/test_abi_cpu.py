@@ -129,6 +129,32 @@ def test_snapshot_window_guard_and_sizes(cp):
     assert lib.cp_snapshot_bytes(None, 4) == 0
 
 
+def test_fused_snapshot_and_append_rollback_validation(cp):
+    lib = cp.raw()
+    f = lib.cp_rope_qk_snapshot_chunk
+    g = lib.cp_kv_append_rollback
+    c = _cache(cp, ring=1, cap=132, sink=4)
+    need = lib.cp_snapshot_bytes(ctypes.byref(c), 128)
+    snap = cp.SnapshotDesc(FAKE, need, None, 0, 0)
+    args = lambda C=128, **kw: [kw.get(n, FAKE) for n in ("q", "q_out", "k", "k_out", "cos",
+                                                           "sin")] + [8, C, 1, None]
+    # [cactus] review hardening: window <= chunk + sink is rejected, nothing armed
+    assert f(ctypes.byref(c), *args(), ctypes.byref(snap), None) == cp.ERR_WINDOW
+    assert snap.armed == 0
+    c2 = _cache(cp, ring=1, cap=512, sink=0)
+    small = cp.SnapshotDesc(FAKE, 16, None, 0, 0)
+    assert f(ctypes.byref(c2), *args(), ctypes.byref(small), None) == cp.ERR_WORKSPACE
+    assert f(ctypes.byref(c2), *args(k=None), ctypes.byref(snap), None) == cp.ERR_ARG
+    assert f(ctypes.byref(c2), *args(), None, None) == cp.ERR_ARG
+    # the fused append needs the armed snapshot of this cache for this C
+    assert g(ctypes.byref(c2), FAKE, FAKE, 128, ctypes.byref(snap), None) == cp.ERR_STATE
+    armed = cp.SnapshotDesc(FAKE, need, 0x2000, 128, 1)  # armed, for another cache
+    assert g(ctypes.byref(c2), FAKE, FAKE, 128, ctypes.byref(armed), None) == cp.ERR_STATE
+    mine = cp.SnapshotDesc(FAKE, 1 << 20, FAKE, 64, 1)  # this cache, another C
+    assert g(ctypes.byref(c2), FAKE, FAKE, 128, ctypes.byref(mine), None) == cp.ERR_STATE
+    assert mine.armed == 1
+
+
 def test_rollback_requires_armed_matching_snapshot(cp):
     lib = cp.raw()
     c = _cache(cp, ring=1, cap=512)

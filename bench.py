@@ -139,10 +139,15 @@ class Layer:
                         static_append=self.static, flags=self.flags)
 
     def attn_only(self, cp):
+        """The attention call in the step's configuration (for large chunks the kernel
+        rotates Q as it loads it, as the step does)."""
+        from chunked_prefill_attention_rope_amd import path
         d, b = self.d, self.bufs
-        cp.attn_chunk_with_past(self.caches[0], b.q_rot, b.k_rot, d["v"], n_valid=d["n_valid"],
-                                mask=self.mask, window=self.window, scale=self.cfg.scale,
-                                out=b.out, workspace=b.workspace, flags=self.flags)
+        fold = path.rope_q_in_attention(d["q"])
+        cp.attn_chunk_with_past(self.caches[0], d["q"] if fold else b.q_rot, b.k_rot, d["v"],
+                                n_valid=d["n_valid"], mask=self.mask, window=self.window,
+                                scale=self.cfg.scale, out=b.out, workspace=b.workspace,
+                                flags=self.flags, q_rope=(d["cos"], d["sin"]) if fold else None)
 
 
 def time_graph(fn, reps_inside, replays=1):

@@ -27,7 +27,7 @@ ATTN_NO_SPLIT, ATTN_FORCE_GENERIC, ATTN_FULL_TILES, ATTN_ADVANCE_SEEN = 1, 2, 4,
 def ATTN_SPLITS(n: int) -> int:
     """CP_ATTN_SPLITS(n): force n key splits (bits 8..15 of the flags)."""
     return (int(n) & 0xFF) << 8
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libcp.so is not built ({LIB_PATH}); run "
@@ -55,7 +55,9 @@ class AttnArgs(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t), ("H", ctypes.c_int32),
                 ("C", ctypes.c_int32), ("window", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("flags", ctypes.c_uint32), ("reserved", ctypes.c_int32),
-                ("select_out", ctypes.c_void_p)]
+                ("select_out", ctypes.c_void_p), ("q_cos", ctypes.c_void_p),
+                ("q_sin", ctypes.c_void_p), ("q_tables", ctypes.c_int32),
+                ("reserved2", ctypes.c_int32)]
 
 
 _vp, _i = ctypes.c_void_p, ctypes.c_int
@@ -218,27 +220,30 @@ class KVCache:
         return self.desc.D
 
 
-def rope_qk_append_chunk(cache: KVCache, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-                         cos: torch.Tensor, sin: torch.Tensor,
+def rope_qk_append_chunk(cache: KVCache, q: Optional[torch.Tensor], k: torch.Tensor,
+                         v: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor,
                          n_valid: Optional[torch.Tensor] = None,
                          q_out: Optional[torch.Tensor] = None,
                          k_out: Optional[torch.Tensor] = None):
-    """cp_rope_qk_append_chunk: rotate q and k, and write rows [0, n_valid[b]) of the
-    rotated k and of v past seen in a global cache (seen is not advanced)."""
+    """cp_rope_qk_append_chunk: rotate q (None: keys only) and k, and write rows
+    [0, n_valid[b]) of the rotated k and of v past seen in a global cache (seen is not
+    advanced)."""
     for name, t in (("q", q), ("k", k), ("v", v)):
+        if t is None:
+            continue
         if t.dtype != cache.k.dtype or t.shape[0] != cache.B or t.shape[3] != cache.k.shape[3]:
             raise ValueError(f"{name} must be [B, heads, C, D] in the cache's dtype")
     if k.shape != v.shape or k.shape[1] != cache.k.shape[1]:
         raise ValueError("k and v must be [B, nKV, C, D]")
-    if q_out is None:
+    if q is not None and q_out is None:
         q_out = torch.empty_like(q)
     if k_out is None:
         k_out = torch.empty_like(k)
     C = k.shape[2]
     _check(_lib.cp_rope_qk_append_chunk(
-        ctypes.byref(cache.desc), _dev(q, "q"), _dev(q_out, "q_out"), _dev(k, "k"),
+        ctypes.byref(cache.desc), _opt(q, "q"), _opt(q_out, "q_out"), _dev(k, "k"),
         _dev(k_out, "k_out"), _dev(v, "v"), _opt(cos, "cos", torch.float32),
-        _opt(sin, "sin", torch.float32), q.shape[1], C, cos.shape[0],
+        _opt(sin, "sin", torch.float32), q.shape[1] if q is not None else 0, C, cos.shape[0],
         _opt(n_valid, "n_valid", torch.int32), _stream()), "cp_rope_qk_append_chunk")
     return q_out, k_out
 
@@ -330,7 +335,7 @@ def kv_append_rollback(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor,
 # ---------------------------------------------------------------- attention
 
 def _attn_args(cache, q, k_new, v_new, out, n_valid, mask, window, scale, workspace, flags,
-               select_out=None):
+               select_out=None, q_rope=None):
     B, H, C, D = q.shape
     if scale is None:
         scale = float(torch.tensor(1.0 / D ** 0.5, dtype=torch.float32))
@@ -346,11 +351,18 @@ def _attn_args(cache, q, k_new, v_new, out, n_valid, mask, window, scale, worksp
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    qc = qs = None
+    qt = 0
+    if q_rope is not None:
+        cos, sin = q_rope
+        qc, qs, qt = _opt(cos, "q_cos", torch.float32), _opt(sin, "q_sin", torch.float32), \
+            cos.shape[0]
     return AttnArgs(_dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
                     _dev(out, "out") if out is not None else None,
                     _opt(n_valid, "n_valid", torch.int32), mptr, mld, mhs, mbs, ws_ptr, ws_bytes,
                     H, C, int(window), float(scale), int(flags), 0,
-                    _dev(select_out, "select_out") if select_out is not None else None)
+                    _dev(select_out, "select_out") if select_out is not None else None,
+                    qc, qs, qt, 0)
 
 
 def attn_workspace_bytes(cache: KVCache, q: torch.Tensor, k_new: torch.Tensor,
@@ -366,10 +378,12 @@ def attn_chunk_with_past(cache: KVCache, q: torch.Tensor, k_new: torch.Tensor,
                          scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                          workspace: Optional[torch.Tensor] = None,
                          flags: int = 0,
-                         select_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                         select_out: Optional[torch.Tensor] = None,
+                         q_rope=None) -> torch.Tensor:
     """cp_attn_chunk_with_past over the cache as it stands (before the append).
 
     select_out [B, H, D] (optional) also receives the last real row of each (b, h).
+    q_rope = (cos, sin): q is not rotated yet; the kernel rotates it with these tables.
     """
     if out is None:
         out = torch.empty_like(q)
@@ -377,7 +391,7 @@ def attn_chunk_with_past(cache: KVCache, q: torch.Tensor, k_new: torch.Tensor,
                                    select_out.shape != (q.shape[0], q.shape[1], q.shape[3])):
         raise ValueError("select_out must be [B, H, D] of q's dtype")
     a = _attn_args(cache, q, k_new, v_new, out, n_valid, mask, window, scale, workspace, flags,
-                   select_out)
+                   select_out, q_rope)
     _check(_lib.cp_attn_chunk_with_past(ctypes.byref(cache.desc), ctypes.byref(a), _stream()),
            "cp_attn_chunk_with_past")
     return out
@@ -388,14 +402,15 @@ def attn_chunk_with_past_noalloc(cache: KVCache, q: torch.Tensor, k_new: torch.T
                                  n_valid: Optional[torch.Tensor] = None,
                                  mask: Optional[torch.Tensor] = None, window: int = 0,
                                  scale: Optional[float] = None, flags: int = 0,
-                                 select_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                                 select_out: Optional[torch.Tensor] = None,
+                                 q_rope=None) -> torch.Tensor:
     """cp_attn_chunk_with_past_noalloc: the same attention with the key-split partials in
     the library's own device array (no workspace; the caller passes its output)."""
     if select_out is not None and (select_out.dtype != q.dtype or
                                    select_out.shape != (q.shape[0], q.shape[1], q.shape[3])):
         raise ValueError("select_out must be [B, H, D] of q's dtype")
     a = _attn_args(cache, q, k_new, v_new, out, n_valid, mask, window, scale, None, flags,
-                   select_out)
+                   select_out, q_rope)
     _check(_lib.cp_attn_chunk_with_past_noalloc(ctypes.byref(cache.desc), ctypes.byref(a),
                                                 _stream()), "cp_attn_chunk_with_past_noalloc")
     return out

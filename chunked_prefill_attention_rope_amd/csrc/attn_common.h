@@ -46,6 +46,9 @@ struct AttnParams {
   float sl2e;     // scale * log2(e)
   int advance;    // the split merge also advances cache.seen by n_valid (early append)
   cp_cache cache; // the cache the call reads (for advance)
+  // RoPE of q at load time: fp32 [q_tables][C][D] tables, or nullptr (q already rotated)
+  const float *q_cos, *q_sin;
+  int q_tables;
 };
 
 // Requests every 64-byte line of a kernel's argument block in one batch, so that the

@@ -409,6 +409,49 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
       if (row_ok) v = *reinterpret_cast<const u32x4 *>(Q + 16 * s);
       qf[s] = __builtin_bit_cast(bf16x8, v);
     }
+    // RoPE folded into the load (q given before rotation): dims 16 s + 8 hh + e of the
+    // lower half pair with the same lane's dims 16 (s + NS/2) + 8 hh + e, so the
+    // rotation is lane-local; the arithmetic and rounding are the RoPE launch's.
+    if (p.q_cos) {
+      const size_t trow = (static_cast<size_t>(p.q_tables == 1 ? 0 : b) * p.C + irow) * D + 8 * hh;
+      const float *tc = p.q_cos + trow, *ts = p.q_sin + trow;
+#pragma unroll
+      for (int s = 0; s < NS / 2; ++s) {
+        const int sh = s + NS / 2;
+        const float4 cl0 = *reinterpret_cast<const float4 *>(tc + 16 * s);
+        const float4 cl1 = *reinterpret_cast<const float4 *>(tc + 16 * s + 4);
+        const float4 sl0 = *reinterpret_cast<const float4 *>(ts + 16 * s);
+        const float4 sl1 = *reinterpret_cast<const float4 *>(ts + 16 * s + 4);
+        const float4 ch0 = *reinterpret_cast<const float4 *>(tc + 16 * sh);
+        const float4 ch1 = *reinterpret_cast<const float4 *>(tc + 16 * sh + 4);
+        const float4 sh0 = *reinterpret_cast<const float4 *>(ts + 16 * sh);
+        const float4 sh1 = *reinterpret_cast<const float4 *>(ts + 16 * sh + 4);
+        const float cl[8] = {cl0.x, cl0.y, cl0.z, cl0.w, cl1.x, cl1.y, cl1.z, cl1.w};
+        const float sl[8] = {sl0.x, sl0.y, sl0.z, sl0.w, sl1.x, sl1.y, sl1.z, sl1.w};
+        const float chv[8] = {ch0.x, ch0.y, ch0.z, ch0.w, ch1.x, ch1.y, ch1.z, ch1.w};
+        const float shv[8] = {sh0.x, sh0.y, sh0.z, sh0.w, sh1.x, sh1.y, sh1.z, sh1.w};
+        const u32x4 lo = __builtin_bit_cast(u32x4, qf[s]), hi = __builtin_bit_cast(u32x4, qf[sh]);
+        u32x4 ylo, yhi;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t rl = 0, rh = 0;
+#pragma unroll
+          for (int e2 = 0; e2 < 2; ++e2) {
+            const int e = 2 * w + e2;
+            const float xl = __uint_as_float(e2 ? lo[w] & 0xffff0000u : lo[w] << 16);
+            const float xh = __uint_as_float(e2 ? hi[w] & 0xffff0000u : hi[w] << 16);
+            const uint32_t bl = f32_to_bf16_rne(rot_lo(xl, xh, cl[e], sl[e]));
+            const uint32_t bh = f32_to_bf16_rne(rot_hi(xl, xh, chv[e], shv[e]));
+            rl |= bl << (16 * e2);
+            rh |= bh << (16 * e2);
+          }
+          ylo[w] = rl;
+          yhi[w] = rh;
+        }
+        qf[s] = __builtin_bit_cast(bf16x8, ylo);
+        qf[sh] = __builtin_bit_cast(bf16x8, yhi);
+      }
+    }
   }
 
   // seen and n_valid are both requested before either is used (scalar loads complete

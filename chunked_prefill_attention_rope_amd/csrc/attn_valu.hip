@@ -25,6 +25,17 @@ template <>
 __device__ __forceinline__ float ld<uint16_t>(const uint16_t *p, size_t i) {
   return bf16_to_f32(p[i]);
 }
+// the value an fp32 result has once stored in T (bf16: round to nearest even)
+template <typename T>
+__device__ __forceinline__ float round_to(float v);
+template <>
+__device__ __forceinline__ float round_to<float>(float v) {
+  return v;
+}
+template <>
+__device__ __forceinline__ float round_to<uint16_t>(float v) {
+  return bf16_to_f32(f32_to_bf16_rne(v));
+}
 __device__ __forceinline__ void st(float *p, size_t i, float v) { p[i] = v; }
 __device__ __forceinline__ void st(uint16_t *p, size_t i, float v) { p[i] = f32_to_bf16_rne(v); }
 
@@ -83,6 +94,25 @@ __global__ void __launch_bounds__(256) k_attn_valu(AttnParams p, int D) {
     const int d = ql + 16 * e;
     q[e] = (row_ok && d < D) ? ld<T>(Q, qoff + d) : 0.f;
     acc[e] = 0.f;
+  }
+  // RoPE folded into the load (q given before rotation): each element is rotated with
+  // its half-split partner, read again from memory, by the RoPE launch's arithmetic and
+  // rounding to the storage dtype.
+  if (p.q_cos) {
+    const int h2 = D / 2;
+    const size_t trow = (static_cast<size_t>(p.q_tables == 1 ? 0 : b) * p.C +
+                         (i < p.C ? i : 0)) * D;
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) {
+      const int d = ql + 16 * e;
+      if (row_ok && d < D) {
+        const bool low = d < h2;
+        const float other = ld<T>(Q, qoff + (low ? d + h2 : d - h2));
+        const float c = p.q_cos[trow + d], sn = p.q_sin[trow + d];
+        const float r = low ? rot_lo(q[e], other, c, sn) : rot_hi(other, q[e], c, sn);
+        q[e] = round_to<T>(r);
+      }
+    }
   }
   // seen and n_valid are both requested before either is used (scalar loads complete
   // out of order, so the first use waits for every one in flight: one round trip)

@@ -24,7 +24,7 @@ int valu_keys(int D);
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 constexpr int kNumCU = 256;
 
 int to_status(hipError_t e) { return e == hipSuccess ? CP_OK : CP_ERR_HIP; }
@@ -72,7 +72,8 @@ AttnPlan plan_attention(const cp_cache &c, const cp_attn_args &a, bool for_works
   AttnPlan pl{};
   const int G = a.H / c.nKV;
   const bool aligned = aligned16(a.q) && aligned16(a.k_new) && aligned16(a.v_new) &&
-                       aligned16(a.out) && aligned16(c.k) && aligned16(c.v);
+                       aligned16(a.out) && aligned16(c.k) && aligned16(c.v) &&
+                       (!a.q_cos || (aligned16(a.q_cos) && aligned16(a.q_sin)));
   const bool ext = a.mask != nullptr || (a.flags & CP_ATTN_FULL_TILES);
   const bool mfma_d = c.D == 64 || c.D == 128 || c.D == 256;
   // all rows of one KV head fit 64: the small-rows configuration
@@ -185,6 +186,9 @@ hipError_t launch_attention(const cp_cache &c, const cp_attn_args &a, hipStream_
   p.sl2e = a.scale * kLog2e;
   p.small_rows = pl.small_rows;
   p.cache = c;
+  p.q_cos = a.q_cos;
+  p.q_sin = a.q_sin;
+  p.q_tables = a.q_tables;
   const bool advance = (a.flags & CP_ATTN_ADVANCE_SEEN) != 0;
   p.advance = advance && pl.splits > 1 ? 1 : 0;
   p.frag_rows = pl.mfma ? pl.rows : 0;
@@ -413,6 +417,11 @@ static int check_attn(const cp_cache *cache, const cp_attn_args *a) {
   if (!cache->ring && a->C > cache->cap) return CP_ERR_SHAPE;
   if (a->mask && (a->mask_ld < a->C || a->mask_head_stride < 0 || a->mask_batch_stride < 0))
     return CP_ERR_ARG;
+  if (a->reserved2 != 0 || (!a->q_cos) != (!a->q_sin)) return CP_ERR_ARG;
+  if (a->q_cos) {
+    if (a->q_tables != 1 && a->q_tables != cache->B) return CP_ERR_ARG;
+    if (cache->D % 2 != 0) return CP_ERR_SHAPE;
+  }
   return CP_OK;
 }
 

@@ -25,6 +25,23 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// ------------------------------------------------------------------ RoPE
+
+// Half-split rotation of the pair (lo = x[j], hi = x[j + D/2]) with the position's
+// table values: each fp32 x fp32 product is exact in fp64, so the difference (or sum)
+// is rounded once, then to fp32 -- independent of FMA contraction, the same bits in
+// every kernel that rotates (RoPE launch, attention prologue).
+__device__ __forceinline__ float rot_lo(float lo, float hi, float c, float s) {
+  const double a = static_cast<double>(lo) * static_cast<double>(c);
+  const double b = static_cast<double>(hi) * static_cast<double>(s);
+  return static_cast<float>(a - b);
+}
+__device__ __forceinline__ float rot_hi(float lo, float hi, float c, float s) {
+  const double a = static_cast<double>(hi) * static_cast<double>(c);
+  const double b = static_cast<double>(lo) * static_cast<double>(s);
+  return static_cast<float>(a + b);
+}
+
 // ------------------------------------------------------------- cache layout
 
 // Geometry of one sequence's cache after `seen` positions were absorbed.

@@ -64,17 +64,6 @@ struct RawOf<2> {
   typedef unsigned short type;
 };
 
-__device__ __forceinline__ float rot_lo(float lo, float hi, float c, float s) {
-  const double a = static_cast<double>(lo) * static_cast<double>(c);
-  const double b = static_cast<double>(hi) * static_cast<double>(s);
-  return static_cast<float>(a - b);
-}
-__device__ __forceinline__ float rot_hi(float lo, float hi, float c, float s) {
-  const double a = static_cast<double>(hi) * static_cast<double>(c);
-  const double b = static_cast<double>(lo) * static_cast<double>(s);
-  return static_cast<float>(a + b);
-}
-
 // One rotated tensor of a launch: x, y [B, Hx, C, D].
 template <typename T>
 struct RopeOp {

@@ -60,6 +60,22 @@ def make_buffers(cache: cp.KVCache, q: torch.Tensor, k: torch.Tensor, v: torch.T
     return bufs
 
 
+# Queries of at least this many bytes would be rotated by the attention as it loads
+# them (cp_attn_args q_cos / q_sin: the rotated copy never goes to memory and the RoPE
+# launch rotates the keys only).  None: never.  Measured on MI355X (same box, the step
+# and the attention alone): the long-context workload's attention 1104 -> 1112 us and
+# its step 1956 -> 1967 us, the Llama-8B-like layer's attention 114 -> 123 us -- every
+# workgroup reads its rows' tables at its start (for the long-context layer about 64 MB
+# from L2 at once) and rotates in fp64 before its first tile, which costs more than the
+# RoPE launch saves.  So the RoPE launch keeps rotating Q.
+ROPE_Q_IN_ATTENTION_BYTES = None
+
+
+def rope_q_in_attention(q: torch.Tensor) -> bool:
+    return (ROPE_Q_IN_ATTENTION_BYTES is not None and
+            q.numel() * q.element_size() >= ROPE_Q_IN_ATTENTION_BYTES)
+
+
 def chunk_step(cache: cp.KVCache, q, k, v, cos, sin, n_valid, bufs: StepBuffers,
                mask: Optional[torch.Tensor] = None, window: int = 0,
                static_append: bool = False, flags: int = 0):
@@ -74,26 +90,29 @@ def chunk_step(cache: cp.KVCache, q, k, v, cos, sin, n_valid, bufs: StepBuffers,
     (the same bytes as the separate snapshot, append of all C rows and rollback).  A
     padded global append takes the same form.  A ring whose window cannot take a
     padded append (cap <= C + sink) appends its real rows with cp_kv_append."""
+    # large chunks: the attention rotates Q as it loads it
+    fold = rope_q_in_attention(q)
+    qr, q_in, q_rope = (None, q, (cos, sin)) if fold else (q, bufs.q_rot, None)
+    attn = lambda fl: cp.attn_chunk_with_past(  # noqa: E731
+        cache, q_in, bufs.k_rot, v, n_valid=n_valid, mask=mask, window=window, out=bufs.out,
+        workspace=bufs.workspace, flags=fl, select_out=bufs.sel, q_rope=q_rope)
     if not cache.ring and not static_append:
-        cp.rope_qk_append_chunk(cache, q, k, v, cos, sin, n_valid, q_out=bufs.q_rot,
+        cp.rope_qk_append_chunk(cache, qr, k, v, cos, sin, n_valid, q_out=bufs.q_rot,
                                 k_out=bufs.k_rot)
-        cp.attn_chunk_with_past(cache, bufs.q_rot, bufs.k_rot, v, n_valid=n_valid, mask=mask,
-                                window=window, out=bufs.out, workspace=bufs.workspace,
-                                flags=flags | cp.ATTN_ADVANCE_SEEN, select_out=bufs.sel)
+        attn(flags | cp.ATTN_ADVANCE_SEEN)
         return bufs.out, bufs.sel
     C = q.shape[2]
     if static_append or cache.cap > C + cache.sink:
-        cp.rope_qk_snapshot_chunk(cache, q, k, cos, sin, n_valid, bufs.snap, q_out=bufs.q_rot,
+        cp.rope_qk_snapshot_chunk(cache, qr, k, cos, sin, n_valid, bufs.snap, q_out=bufs.q_rot,
                                   k_out=bufs.k_rot)
-        cp.attn_chunk_with_past(cache, bufs.q_rot, bufs.k_rot, v, n_valid=n_valid, mask=mask,
-                                window=window, out=bufs.out, workspace=bufs.workspace,
-                                flags=flags, select_out=bufs.sel)
+        attn(flags)
         cp.kv_append_rollback(cache, bufs.k_rot, v, bufs.snap)
         return bufs.out, bufs.sel
-    cp.rope_qk_chunk(q, k, cos, sin, q_out=bufs.q_rot, k_out=bufs.k_rot)
-    cp.attn_chunk_with_past(cache, bufs.q_rot, bufs.k_rot, v, n_valid=n_valid, mask=mask,
-                            window=window, out=bufs.out, workspace=bufs.workspace, flags=flags,
-                            select_out=bufs.sel)
+    if fold:
+        cp.rope_chunk(k, cos, sin, out=bufs.k_rot)
+    else:
+        cp.rope_qk_chunk(q, k, cos, sin, q_out=bufs.q_rot, k_out=bufs.k_rot)
+    attn(flags)
     cp.kv_append(cache, bufs.k_rot, v, n_valid)
     return bufs.out, bufs.sel
 

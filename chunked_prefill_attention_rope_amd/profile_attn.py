@@ -58,9 +58,12 @@ def main():
             path.chunk_step(cache, d["q"], d["k"], d["v"], d["cos"], d["sin"], d["n_valid"],
                             bufs, mask=mask, window=window, static_append=static, flags=a.flags)
         else:
-            cp.attn_chunk_with_past(cache, bufs.q_rot, bufs.k_rot, d["v"], n_valid=d["n_valid"],
-                                    mask=mask, window=window, scale=cfg.scale, out=bufs.out,
-                                    workspace=bufs.workspace, flags=a.flags)
+            fold = path.rope_q_in_attention(d["q"])  # the step's configuration
+            cp.attn_chunk_with_past(cache, d["q"] if fold else bufs.q_rot, bufs.k_rot, d["v"],
+                                    n_valid=d["n_valid"], mask=mask, window=window,
+                                    scale=cfg.scale, out=bufs.out, workspace=bufs.workspace,
+                                    flags=a.flags,
+                                    q_rope=(d["cos"], d["sin"]) if fold else None)
     torch.cuda.synchronize()
     print(f"profile_attn: {a.workload} layer {a.layer} x{a.reps} done", flush=True)
 

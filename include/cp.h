@@ -170,6 +170,13 @@ typedef struct cp_snapshot {
  *              for a sequence without real rows -- bit-identical to
  *              cp_select_row(out, n_valid, -1) for n_valid in [0, C] (n_valid
  *              NULL selects row C - 1).  Not written when C = 0.
+ *   q_cos, q_sin  NULL: q is already rotated.  Otherwise q holds the chunk's queries
+ *              BEFORE RoPE and the kernel rotates them as it loads them, with these
+ *              fp32 [q_tables, C, D] tables (q_tables = 1 shares one table over the
+ *              batch, q_tables = B gives each sequence its own) -- bit-identical to
+ *              cp_rope_chunk(q) followed by the call with the rotated q ([SKaiNET]
+ *              "Change (additive)": RoPE from per-position tables; here folded into
+ *              the attention's load of Q, so the rotated queries never go to memory).
  *
  * The cache is read as it stands BEFORE the chunk is appended.
  */
@@ -192,6 +199,10 @@ typedef struct cp_attn_args {
   uint32_t flags;
   int32_t reserved; /* must be 0 */
   void *select_out;
+  const float *q_cos;
+  const float *q_sin;
+  int32_t q_tables;
+  int32_t reserved2; /* must be 0 */
 } cp_attn_args;
 
 #define CP_ATTN_NO_SPLIT 1u      /* one pass per query tile, no key split */
@@ -369,8 +380,9 @@ size_t cp_attn_workspace_bytes(const cp_cache *cache, const cp_attn_args *args);
  * Kernels: bf16 with D in {64, 128, 256} (and 16-byte aligned tensors) runs on
  * the matrix cores; fp32, and bf16 with any other D up to 256, on the vector-ALU
  * kernel.
- * Errors: CP_ERR_ARG, CP_ERR_SHAPE (H % nKV, D > 256, C > cap for a global
- *         cache), CP_ERR_DTYPE, CP_ERR_HIP.
+ * Errors: CP_ERR_ARG (also: only one of q_cos / q_sin, q_tables not 1 or B),
+ *         CP_ERR_SHAPE (H % nKV, D > 256, odd D with q tables, C > cap for a
+ *         global cache), CP_ERR_DTYPE, CP_ERR_HIP.
  */
 int cp_attn_chunk_with_past(const cp_cache *cache, const cp_attn_args *args, cp_stream_t stream);
 

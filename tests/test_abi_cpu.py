@@ -173,7 +173,8 @@ def test_attention_validation(cp):
     def args(**kw):
         d = dict(q=FAKE, k_new=FAKE, v_new=FAKE, out=FAKE, n_valid=None, mask=None, mask_ld=0,
                  mask_head_stride=0, mask_batch_stride=0, workspace=None, workspace_bytes=0,
-                 H=8, C=16, window=0, scale=0.1, flags=0, reserved=0)
+                 H=8, C=16, window=0, scale=0.1, flags=0, reserved=0, q_cos=None, q_sin=None,
+                 q_tables=0, reserved2=0)
         d.update(kw)
         return cp.AttnArgs(**d)
 
@@ -183,6 +184,14 @@ def test_attention_validation(cp):
     assert f(ctypes.byref(c), ctypes.byref(args(scale=float("nan"))), None) == cp.ERR_ARG
     assert f(ctypes.byref(c), ctypes.byref(args(mask=FAKE, mask_ld=8)), None) == cp.ERR_ARG
     assert f(ctypes.byref(c), ctypes.byref(args(C=65)), None) == cp.ERR_SHAPE
+    # query tables: both or neither, one per batch or per sequence, even D
+    assert f(ctypes.byref(c), ctypes.byref(args(q_cos=FAKE)), None) == cp.ERR_ARG
+    assert f(ctypes.byref(c), ctypes.byref(args(q_cos=FAKE, q_sin=FAKE, q_tables=3)),
+             None) == cp.ERR_ARG
+    assert f(ctypes.byref(c), ctypes.byref(args(reserved2=1)), None) == cp.ERR_ARG
+    odd = _cache(cp, D=63)
+    assert f(ctypes.byref(odd), ctypes.byref(args(q_cos=FAKE, q_sin=FAKE, q_tables=1)),
+             None) == cp.ERR_SHAPE
     big = _cache(cp, D=512)
     assert f(ctypes.byref(big), ctypes.byref(args()), None) == cp.ERR_SHAPE
     assert lib.cp_attn_workspace_bytes(ctypes.byref(c), ctypes.byref(args(H=7))) == 0

@@ -22,6 +22,7 @@ ATTN_SCRATCH_BYTES = 64 << 20  # CP_ATTN_SCRATCH_BYTES
 DEV_OVERFLOW, DEV_NVALID, DEV_MASK_LD, DEV_ROLLBACK, DEV_SEEN = 1, 2, 4, 8, 16
 F32, BF16 = 0, 1
 ATTN_NO_SPLIT, ATTN_FORCE_GENERIC, ATTN_FULL_TILES, ATTN_ADVANCE_SEEN = 1, 2, 4, 8
+ATTN_BALANCE = 16
 
 
 def ATTN_SPLITS(n: int) -> int:

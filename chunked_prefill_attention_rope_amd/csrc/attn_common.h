@@ -42,14 +42,31 @@ struct AttnParams {
   int qtiles;  // query tiles per (b, kv head, head group)
   int splits;
   int full_tiles;
-  int small_rows; // matrix-core kernel: 0, the 64-row configuration (1) or its deep ring (2)
+  int small_rows; // matrix-core kernel: 0, the 64-row configuration (1), its deep ring (2),
+                  // or the 128-row medium configuration (3)
   float sl2e;     // scale * log2(e)
   int advance;    // the split merge also advances cache.seen by n_valid (early append)
   cp_cache cache; // the cache the call reads (for advance)
   // RoPE of q at load time: fp32 [q_tables][C][D] tables, or nullptr (q already rotated)
   const float *q_cos, *q_sin;
   int q_tables;
+  // Balanced key splits (matrix-core kernel): the plan written by the plan kernel, or
+  // nullptr.  Block i of the attention takes item i; split items write their partials to
+  // their slot (AttnParams::wo in fragment order, slot * (frag_rows / 32) groups).
+  const int32_t *plan;
+  int plan_grid;   // blocks of the attention launch = item entries
+  int plan_slots;  // workgroups the GPU holds at once
+  int plan_kt;     // keys per tile
+  int plan_tmin;   // fewest tiles per piece
 };
+
+// Plan layout (int32): a header (split entries, piece length, total tiles, units), then
+// plan_grid items of kPlanItemInts (sequence, KV head, query tile, piece, pieces, partial
+// slot or -1, seen, n_valid; sequence -1: no work), then the split entries (sequence, KV
+// head, query tile, pieces, first partial slot, n_valid clamped).
+constexpr int kPlanHeaderInts = 64;
+constexpr int kPlanItemInts = 8;
+constexpr int kPlanMaxB = 1024;  // sequences a plan can balance
 
 // Requests every 64-byte line of a kernel's argument block in one batch, so that the
 // later reads of its fields hit the scalar cache.  Left to itself the compiler reads
@@ -159,5 +176,7 @@ __device__ __forceinline__ float inkernel_add(bool chunk, int col, const Live &g
 hipError_t launch_attn_valu(const AttnParams &p, int D, int dtype, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnParams &p, int D, hipStream_t s);
 hipError_t launch_attn_combine(const AttnParams &p, int D, int dtype, hipStream_t s);
+hipError_t launch_attn_plan(const AttnParams &p, hipStream_t s);
+hipError_t launch_attn_merge_plan(const AttnParams &p, int D, hipStream_t s);
 
 }  // namespace cp

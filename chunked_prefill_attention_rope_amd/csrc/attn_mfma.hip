@@ -285,6 +285,16 @@ struct Sel<D, EX, 2> : Sel<D, EX, 1> {
   static constexpr int STAGES = EX ? 2 : 3;
   static constexpr int WAVES = D == 256 ? 1 : 2;
 };
+//  SM = 3 (D = 128, in-kernel rule, 64 < C * G <= 128 rows per KV head): 128-row
+//  workgroups of 4 waves with 32-key tiles in a 4-stage ring (64 KB), two per CU.  The
+//  standard 256-row workgroup would leave half its rows empty and stream one tile at a
+//  time per CU in a regime (C = 32, G = 4) where the keys' bytes, not the products, set
+//  the time.
+template <int D, bool EX>
+struct Sel<D, EX, 3> {
+  static constexpr int KT = 32, STAGES = 4, WAVES = 2, DSPLIT = 1;
+  static constexpr int ROWW = 4;
+};
 
 // One wave-wide 4-byte direct-to-LDS load (mask blocks: no alignment beyond 4 bytes).
 __device__ __forceinline__ void dma4(const float *src, float *lds_base) {
@@ -371,22 +381,41 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
   // only its own blocks); and the split index varies slowest, so that the first part
   // of every sequence starts at once and the later parts of long sequences fill the
   // CUs that short sequences free.
-  const unsigned nbg = static_cast<unsigned>(p.B) * p.nKV;
-  const unsigned groups = static_cast<unsigned>(p.splits) * nbg;
-  unsigned gi, qt;
-  if (groups % 8 == 0) {
-    const unsigned rest = blockIdx.x / 8;
-    qt = rest % p.qtiles;
-    gi = (rest / p.qtiles) * 8 + blockIdx.x % 8;
+  // With a balancing plan, block i takes item i of the plan: its sequence, KV head,
+  // query tile, key piece and partial slot, and the sequence's seen and n_valid (one
+  // scalar load; the plan kernel read them).
+  int qtile, split, nsplit, b, g, slot = -1, seen_in = 0, nv_in = 0;
+  if (p.plan) {
+    const int32_t *it = p.plan + kPlanHeaderInts + static_cast<size_t>(blockIdx.x) * kPlanItemInts;
+    b = it[0];
+    g = it[1];
+    qtile = it[2];
+    split = it[3];
+    nsplit = it[4];
+    slot = it[5];
+    seen_in = it[6];
+    nv_in = it[7];
+    if (b < 0) return;  // no work in this entry (uniform over the workgroup)
   } else {
-    qt = blockIdx.x % p.qtiles;
-    gi = blockIdx.x / p.qtiles;
+    const unsigned nbg = static_cast<unsigned>(p.B) * p.nKV;
+    const unsigned groups = static_cast<unsigned>(p.splits) * nbg;
+    unsigned gi, qt;
+    if (groups % 8 == 0) {
+      const unsigned rest = blockIdx.x / 8;
+      qt = rest % p.qtiles;
+      gi = (rest / p.qtiles) * 8 + blockIdx.x % 8;
+    } else {
+      qt = blockIdx.x % p.qtiles;
+      gi = blockIdx.x / p.qtiles;
+    }
+    qtile = static_cast<int>(qt);
+    split = static_cast<int>(gi / nbg);
+    nsplit = p.splits;
+    const int bg0 = static_cast<int>(gi % nbg);
+    b = bg0 / p.nKV;
+    g = bg0 % p.nKV;
   }
-  const int qtile = static_cast<int>(qt);
-  const int split = static_cast<int>(gi / nbg);
-  const int bg = static_cast<int>(gi % nbg);
-  const int b = bg / p.nKV;
-  const int g = bg % p.nKV;
+  const int bg = b * p.nKV + g;
 
   const int r = (wave % ROWW) * 32 + n;
   const int hl = r / p.qpos;
@@ -456,8 +485,8 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
 
   // seen and n_valid are both requested before either is used (scalar loads complete
   // out of order, so the first use waits for every one in flight: one round trip)
-  const int seen = p.seen[b];
-  int nv = p.n_valid ? p.n_valid[b] : p.C;
+  const int seen = p.plan ? seen_in : p.seen[b];
+  int nv = p.plan ? nv_in : (p.n_valid ? p.n_valid[b] : p.C);
   const bool lead = tid == 0 && qtile == 0 && split == 0 && g == 0;
   if (nv < 0 || nv > p.C) {
     if (lead) flag(p.status, CP_DEV_NVALID);
@@ -520,7 +549,7 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
                     EXPLICIT || p.full_tiles);
     // near-equal split ranges, the first cnt % splits one tile longer (one 32-bit
     // division: a 64-bit one is a long software sequence ahead of the first load)
-    const unsigned cnt = static_cast<unsigned>(ts.count()), ns = static_cast<unsigned>(p.splits);
+    const unsigned cnt = static_cast<unsigned>(ts.count()), ns = static_cast<unsigned>(nsplit);
     const unsigned q = cnt / ns, rm = cnt - q * ns, us = static_cast<unsigned>(split);
     u0 = static_cast<int>(us * q + (us < rm ? us : rm));
     u1 = u0 + static_cast<int>(q + (us < rm ? 1u : 0u));
@@ -888,7 +917,7 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
   if (!row_ok) return;
   const bool real = any_real && i < nv;
   const size_t orow = (static_cast<size_t>(b) * p.H + head) * p.C + i;
-  if (p.splits == 1) {
+  if (nsplit == 1) {
     uint16_t *O = static_cast<uint16_t *>(p.out) + orow * D;
     uint16_t *S = p.sel && i == selected_row(nv)
                       ? static_cast<uint16_t *>(p.sel) + (static_cast<size_t>(b) * p.H + head) * D
@@ -913,7 +942,8 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
     // would touch 32 rows)
     const size_t nu = static_cast<size_t>(p.B) * p.nKV * p.qtiles * ROWW;
     const size_t u = (static_cast<size_t>(bg) * p.qtiles + qtile) * ROWW + wave % ROWW;
-    const size_t grp = static_cast<size_t>(split) * nu + u;
+    const size_t grp = slot >= 0 ? static_cast<size_t>(slot) * ROWW + wave % ROWW
+                                 : static_cast<size_t>(split) * nu + u;
     float *WO = p.wo + grp * (D / 32) * 1024 + 4 * lane;
 #pragma unroll
     for (int db = 0; db < NDW; ++db) {
@@ -939,7 +969,7 @@ template <int D, bool EXPLICIT, bool EXT, int SM>
 hipError_t launch_one(const AttnParams &p, unsigned blocks, hipStream_t s) {
   using CF = Sel<D, EXT, SM>;
   // split partials go out in the fragment order of this configuration's query tile
-  if (p.splits > 1 && p.frag_rows != 32 * CF::ROWW) return hipErrorInvalidValue;
+  if ((p.splits > 1 || p.plan) && p.frag_rows != 32 * CF::ROWW) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_attn_mfma<D, EXPLICIT, EXT, SM>), dim3(blocks),
                      dim3(64 * CF::ROWW * CF::DSPLIT), 0, s, p);
   return hipSuccess;
@@ -954,10 +984,20 @@ hipError_t launch_mode(const AttnParams &p, unsigned blocks, hipStream_t s) {
 
 template <int D>
 hipError_t launch_d(const AttnParams &p, hipStream_t s) {
-  const unsigned blocks = static_cast<unsigned>(p.qtiles) * p.splits * p.B * p.nKV;
+  const unsigned blocks =
+      p.plan ? static_cast<unsigned>(p.plan_grid)
+             : static_cast<unsigned>(p.qtiles) * p.splits * p.B * p.nKV;
   if (blocks == 0) return hipSuccess;
   hipError_t e;
-  if (p.small_rows == 2) {
+  if (p.small_rows == 3) {
+    // medium rows: D = 128 and the in-kernel rule only
+    if constexpr (D == 128) {
+      if (p.mask || p.full_tiles) return hipErrorInvalidValue;
+      e = launch_one<D, false, false, 3>(p, blocks, s);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else if (p.small_rows == 2) {
     if (p.mask || p.full_tiles) return hipErrorInvalidValue;  // deep ring: in-kernel rule only
     e = launch_one<D, false, false, 2>(p, blocks, s);
   } else if (p.small_rows == 1) {
@@ -996,6 +1036,7 @@ int keys_of(int D) {
 
 // small_rows: 0 standard, 1 small rows, 2 small rows with the deep ring (same tiling)
 int mfma_rows_per_tile(int D, bool explicit_tiling, int small_rows) {
+  if (small_rows == 3) return 32 * Sel<128, false, 3>::ROWW;
   if (small_rows) return explicit_tiling ? rows_of<true, 1>(D) : rows_of<false, 1>(D);
   return explicit_tiling ? rows_of<true, 0>(D) : rows_of<false, 0>(D);
 }
@@ -1017,12 +1058,14 @@ int wgs_d(int D) {
 }
 
 int mfma_wgs_per_cu(int D, bool explicit_tiling, int small_rows) {
+  if (small_rows == 3) return wgs_of<128, false, 3>();
   if (small_rows == 2) return wgs_d<false, 2>(D);
   if (small_rows == 1) return explicit_tiling ? wgs_d<true, 1>(D) : wgs_d<false, 1>(D);
   return explicit_tiling ? wgs_d<true, 0>(D) : wgs_d<false, 0>(D);
 }
 
 int mfma_keys_per_tile(int D, bool explicit_tiling, int small_rows) {
+  if (small_rows == 3) return Sel<128, false, 3>::KT;
   if (small_rows) return explicit_tiling ? keys_of<true, 1>(D) : keys_of<false, 1>(D);
   return explicit_tiling ? keys_of<true, 0>(D) : keys_of<false, 0>(D);
 }

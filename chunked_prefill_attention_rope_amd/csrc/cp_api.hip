@@ -26,6 +26,9 @@ namespace {
 
 constexpr int kAbiVersion = 3;
 constexpr int kNumCU = 256;
+// Fewest key tiles per piece of a balanced split (each workgroup pays a prologue and the
+// first tile's latency, about two tiles' time).
+constexpr int kPlanMinTiles = 4;
 
 int to_status(hipError_t e) { return e == hipSuccess ? CP_OK : CP_ERR_HIP; }
 
@@ -78,6 +81,9 @@ AttnPlan plan_attention(const cp_cache &c, const cp_attn_args &a, bool for_works
   const bool mfma_d = c.D == 64 || c.D == 128 || c.D == 256;
   // all rows of one KV head fit 64: the small-rows configuration
   pl.small_rows = static_cast<long>(a.C) * G <= 64 ? 1 : 0;
+  // medium rows (D = 128, in-kernel rule): the rows of one KV head fit 128
+  if (!pl.small_rows && c.D == 128 && !ext && static_cast<long>(a.C) * G <= 128)
+    pl.small_rows = 3;
   const int rows = mfma_d ? mfma_rows_per_tile(c.D, ext, pl.small_rows) : 0;
   pl.mfma = c.dtype == CP_BF16 && mfma_d && G <= rows && !(a.flags & CP_ATTN_FORCE_GENERIC) &&
             aligned;
@@ -128,13 +134,30 @@ AttnPlan plan_attention(const cp_cache &c, const cp_attn_args &a, bool for_works
   }
   // Small rows whose splits each stream many tiles (long decode contexts): the deep-ring
   // configuration, three workgroups per CU (in-kernel rule only).
-  if (pl.mfma && pl.small_rows && !ext && tiles / pl.splits >= 24) {
+  if (pl.mfma && pl.small_rows == 1 && !ext && tiles / pl.splits >= 24) {
     pl.small_rows = 2;
     if (forced == 0 && split_ok) pl.splits = split_for(mfma_wgs_per_cu(c.D, ext, 2));
   }
-  if (pl.splits > 1 && !for_workspace &&
-      (!a.workspace || a.workspace_bytes < attn_workspace_bytes(c, a, pl)))
+  // Balanced splits (standard matrix-core configuration): a device-side plan cuts each
+  // sequence's keys by its own length.  The launch holds every item the plan can make:
+  // with pieces of at least total / slots tiles there are at most slots + base of them
+  // (plus the padding of the last group of 8 units).
+  if ((a.flags & CP_ATTN_BALANCE) && pl.mfma && pl.small_rows == 0 && forced == 0 &&
+      c.B <= kPlanMaxB && base > 0) {
+    pl.planned = true;
     pl.splits = 1;
+    pl.plan_slots = mfma_wgs_per_cu(c.D, ext, 0) * kNumCU;
+    const long per = 8L * pl.qtiles;
+    long grid = pl.plan_slots + base + per;
+    grid = (grid + per - 1) / per * per;
+    pl.plan_grid = static_cast<int>(grid);
+  }
+  const bool needs_ws = pl.splits > 1 || pl.planned;
+  if (needs_ws && !for_workspace &&
+      (!a.workspace || a.workspace_bytes < attn_workspace_bytes(c, a, pl))) {
+    pl.splits = 1;
+    pl.planned = false;
+  }
   return pl;
 }
 
@@ -146,7 +169,19 @@ static size_t partial_rows(const cp_cache &c, const cp_attn_args &a, const AttnP
   return static_cast<size_t>(c.B) * a.H * a.C;
 }
 
+// Planned mode: the plan (header, items, split entries), then the partials of at most
+// plan_grid slots in fragment order, then their (m, l).
+static size_t plan_bytes(const AttnPlan &p) {
+  return round256(sizeof(int32_t) *
+                  (kPlanHeaderInts + 2 * static_cast<size_t>(p.plan_grid) * kPlanItemInts));
+}
+
 size_t attn_workspace_bytes(const cp_cache &c, const cp_attn_args &a, const AttnPlan &p) {
+  if (p.planned) {
+    const size_t rows = static_cast<size_t>(p.plan_grid) * p.rows;
+    return plan_bytes(p) + round256(rows * c.D * sizeof(float)) +
+           round256(rows * 2 * sizeof(float));
+  }
   if (p.splits <= 1) return 0;
   const size_t rows = partial_rows(c, a, p);
   return round256(static_cast<size_t>(p.splits) * rows * c.D * sizeof(float)) +
@@ -192,7 +227,18 @@ hipError_t launch_attention(const cp_cache &c, const cp_attn_args &a, hipStream_
   const bool advance = (a.flags & CP_ATTN_ADVANCE_SEEN) != 0;
   p.advance = advance && pl.splits > 1 ? 1 : 0;
   p.frag_rows = pl.mfma ? pl.rows : 0;
-  if (pl.splits > 1) {
+  if (pl.planned) {
+    unsigned char *w = static_cast<unsigned char *>(a.workspace);
+    const size_t rows = static_cast<size_t>(pl.plan_grid) * pl.rows;
+    p.plan = reinterpret_cast<const int32_t *>(w);
+    p.plan_grid = pl.plan_grid;
+    p.plan_slots = pl.plan_slots;
+    p.plan_kt = pl.kt;
+    p.plan_tmin = kPlanMinTiles;
+    p.wo = reinterpret_cast<float *>(w + plan_bytes(pl));
+    p.wml = reinterpret_cast<float *>(w + plan_bytes(pl) + round256(rows * c.D * sizeof(float)));
+    p.advance = advance ? 1 : 0;
+  } else if (pl.splits > 1) {
     const size_t rows = partial_rows(c, a, pl);
     unsigned char *w = static_cast<unsigned char *>(a.workspace);
     p.wo = reinterpret_cast<float *>(w);
@@ -202,6 +248,14 @@ hipError_t launch_attention(const cp_cache &c, const cp_attn_args &a, hipStream_
   if (static_cast<size_t>(c.B) * a.H * a.C == 0)
     return advance ? launch_advance_seen(c, a.C, a.n_valid, s) : hipSuccess;
   hipError_t e;
+  if (pl.planned) {
+    p.hb = p.G;
+    p.hgroups = 1;
+    e = launch_attn_plan(p, s);
+    if (e == hipSuccess) e = launch_attn_mfma(p, c.D, s);
+    if (e == hipSuccess) e = launch_attn_merge_plan(p, c.D, s);  // also advances seen
+    return e;
+  }
   if (pl.mfma) {
     p.hb = p.G;
     p.hgroups = 1;

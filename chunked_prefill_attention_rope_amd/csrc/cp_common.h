@@ -182,9 +182,13 @@ struct AttnPlan {
   int qtiles;     // query tiles per (b, kv head)
   int qpos;       // chunk rows per query tile
   int kt;         // keys per tile
-  int small_rows;   // matrix-core kernel: 0, or its 64-row configuration (1; 2 = deep ring)
+  int small_rows;   // matrix-core kernel: 0, or its 64-row configuration (1; 2 = deep ring),
+                    // or the 128-row medium configuration (3)
   int rows;         // matrix-core kernel: query rows per query tile (its split partials
                     // are stored in that tile's fragment order)
+  bool planned;     // balanced key splits from a device-side plan (CP_ATTN_BALANCE)
+  int plan_grid;    // ... its attention blocks (item entries)
+  int plan_slots;   // ... workgroups the GPU holds at once
 };
 
 AttnPlan plan_attention(const cp_cache &c, const cp_attn_args &a, bool for_workspace);

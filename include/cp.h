@@ -216,6 +216,14 @@ typedef struct cp_attn_args {
    chunk whose rows cp_rope_qk_append_chunk already wrote): inside the split merge when
    the keys are split, else by one small launch after the attention. */
 #define CP_ATTN_ADVANCE_SEEN 8u
+/* Balance the work of a batch whose past lengths differ: a one-workgroup kernel reads the
+   lengths on the device, cuts each sequence's keys into pieces by its own length (no
+   piece shorter than the total over the workgroups the GPU holds at once), orders them
+   longest first, and a merge combines the cut rows; the other rows are written directly
+   (the bf16 matrix-core kernel's standard configuration, up to 1024 sequences; otherwise
+   the flag is ignored).  Needs the workspace cp_attn_workspace_bytes() returns with it;
+   with less the call runs unbalanced.  Three launches (plan, attention, merge). */
+#define CP_ATTN_BALANCE 16u
 
 /* ---- introspection ---- */
 

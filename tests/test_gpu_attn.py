@@ -100,6 +100,11 @@ SMALL = [
          sink=4, window=64, seen=[500, 2], n_valid=[32, 20]),
     dict(name="global_sink_window_d256", dtype=I.BF16, B=1, H=8, nKV=1, D=256, C=24, cap=400,
          sink=2, window=40, seen=[300], n_valid=[21]),
+    # 64 < C * G <= 128 at D = 128: the 128-row medium configuration (in-kernel rule)
+    dict(name="medium_c32_d128", dtype=I.BF16, B=2, H=8, nKV=2, D=128, C=32, cap=2000,
+         seen=[1900, 37], n_valid=[32, 20]),
+    dict(name="medium_g3_window", dtype=I.BF16, B=2, H=6, nKV=2, D=128, C=40, cap=600,
+         window=300, seen=[550, 100], n_valid=[40, 39]),
     # C * G <= 64: the matrix-core kernel's small-rows configuration
     dict(name="small_c16_d128", dtype=I.BF16, B=2, H=8, nKV=2, D=128, C=16, cap=300,
          seen=[100, 250], n_valid=[16, 9]),

@@ -15,8 +15,9 @@
 //  - writes one 8-int item per block (sequence, KV head, query tile, piece, pieces,
 //    partial slot, seen, n_valid), so the attention reads its work and the lengths in one
 //    scalar load, and one 8-int entry per split (sequence, KV head, query tile).
-// Unsplit items write their output directly; the split ones write fp32 partials in the
-// matrix-core fragment order to their slots, and k_attn_merge_plan combines them.
+// Unsplit items write their output directly; the split ones write normalized bf16
+// partials (and fp32 m, l) in the matrix-core fragment order to their slots, and
+// k_attn_merge_plan combines them.
 #include "attn_common.h"
 
 namespace cp {
@@ -221,14 +222,16 @@ __global__ void __launch_bounds__(256) k_attn_merge_plan(AttnParams p, int D) {
         for (int s = 0; s < P; ++s) {
           const size_t grp = static_cast<size_t>(base + s) * rw + rg;
           const float2 ml = *reinterpret_cast<const float2 *>(p.wml + (grp * 32 + n) * 2);
-          const float4 v = *reinterpret_cast<const float4 *>(
-              p.wo + (grp << lgb) * 1024 + static_cast<size_t>(k) * 1024 + (e & 255) * 4);
+          const uint2 v = *reinterpret_cast<const uint2 *>(
+              reinterpret_cast<const uint16_t *>(p.wo) + (grp << lgb) * 1024 +
+              static_cast<size_t>(k) * 1024 + (e & 255) * 4);  // normalized, bf16
           const float w = __builtin_amdgcn_exp2f(ml.x - M);  // 0 for an empty piece
+          const float wl = w * ml.y;
           l = fmaf(w, ml.y, l);
-          o[0] = fmaf(w, v.x, o[0]);
-          o[1] = fmaf(w, v.y, o[1]);
-          o[2] = fmaf(w, v.z, o[2]);
-          o[3] = fmaf(w, v.w, o[3]);
+          o[0] = fmaf(wl, __uint_as_float(v.x << 16), o[0]);
+          o[1] = fmaf(wl, __uint_as_float(v.x & 0xffff0000u), o[1]);
+          o[2] = fmaf(wl, __uint_as_float(v.y << 16), o[2]);
+          o[3] = fmaf(wl, __uint_as_float(v.y & 0xffff0000u), o[3]);
         }
         const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll

@@ -20,15 +20,16 @@ struct AttnParams {
   int32_t *status;
   const float *mask;
   int64_t mld, mhs, mbs;
-  // Split partials.  Row-major (frag_rows == 0): O [S][B][H][C][D], m and l
-  // [S][B][H][C][2].  Fragment order (frag_rows = R, the rows of one query tile, a
-  // multiple of 32): a query tile's rows form R / 32 groups of 32, numbered
+  // Split partials.  Row-major (frag_rows == 0, vector-ALU kernel): fp32 sums O
+  // [S][B][H][C][D], m and l [S][B][H][C][2].  Fragment order (frag_rows = R, the rows
+  // of one query tile, a multiple of 32; matrix-core kernel): bf16 normalized O / l; a
+  // query tile's rows form R / 32 groups of 32, numbered
   // u = ((b * nKV + g) * qtiles + qtile) * (R / 32) + group, NU groups in all; O of
-  // split s, group u, dims 32 k .. 32 k + 31 is a block of 1024 floats at
+  // split s, group u, dims 32 k .. 32 k + 31 is a block of 1024 elements at
   // ((s * NU + u) * (D / 32) + k) * 1024, holding row n of the group, dims
   // 32 k + 8 j + 4 h + e (n, j, e < 4, h < 2) at (j * 64 + 32 h + n) * 4 + e -- the
   // order in which a 32 x 32 matrix-core accumulator sits in a wave's lanes, so that
-  // each store instruction writes 1 KB of consecutive bytes; m and l of the row at
+  // each store instruction writes 512 consecutive bytes; fp32 m and l of the row at
   // ((s * NU + u) * 32 + n) * 2.  Row r of a query tile is head g * G + r / qpos,
   // chunk row qtile * qpos + r % qpos.
   float *wo;

@@ -938,23 +938,23 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
     }
   } else if (i < nv) {  // partials of real rows only: the merge writes pad rows as zeros
     // fragment order (p.frag_rows == ROWS): the accumulators leave as they sit in the
-    // lanes, each store instruction 1 KB of consecutive bytes (in row order every one
-    // would touch 32 rows)
+    // lanes, each store instruction 512 bytes of consecutive bytes (in row order every
+    // one would touch 32 rows)
     const size_t nu = static_cast<size_t>(p.B) * p.nKV * p.qtiles * ROWW;
     const size_t u = (static_cast<size_t>(bg) * p.qtiles + qtile) * ROWW + wave % ROWW;
     const size_t grp = slot >= 0 ? static_cast<size_t>(slot) * ROWW + wave % ROWW
                                  : static_cast<size_t>(split) * nu + u;
-    float *WO = p.wo + grp * (D / 32) * 1024 + 4 * lane;
+    // normalized (O / l) in bf16, half the bytes of fp32 sums; the merge weighs each
+    // split by 2^(m - M) l (an empty split: l = 0, zeros here)
+    uint16_t *WO = reinterpret_cast<uint16_t *>(p.wo) + grp * (D / 32) * 1024 + 4 * lane;
+    const float inv = real && l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
     for (int db = 0; db < NDW; ++db) {
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        float4 w;
-        w.x = real ? oacc[db][4 * rq + 0] : 0.f;
-        w.y = real ? oacc[db][4 * rq + 1] : 0.f;
-        w.z = real ? oacc[db][4 * rq + 2] : 0.f;
-        w.w = real ? oacc[db][4 * rq + 3] : 0.f;
-        *reinterpret_cast<float4 *>(WO + (dgrp * NDW + db) * 1024 + rq * 256) = w;
+        const u32x2 w = {pack_bf16x2(oacc[db][4 * rq + 0] * inv, oacc[db][4 * rq + 1] * inv),
+                         pack_bf16x2(oacc[db][4 * rq + 2] * inv, oacc[db][4 * rq + 3] * inv)};
+        *reinterpret_cast<u32x2 *>(WO + (dgrp * NDW + db) * 1024 + rq * 256) = w;
       }
     }
     if (hh == 0 && dgrp == 0) {

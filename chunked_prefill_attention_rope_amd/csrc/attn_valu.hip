@@ -303,9 +303,10 @@ __global__ void __launch_bounds__(256) k_attn_valu(AttnParams p, int D) {
 // for up to 32), else 16 (the narrower kernel keeps more waves resident for merges of
 // many rows).
 // FRAG: the partials are in the matrix-core kernel's fragment order (AttnParams::wo),
-// D a power of two.  Thread t takes the 4 floats at 4 t of each split, so that a
-// wave's partial reads are 1 KB of consecutive bytes (the reads are SB times the
-// writes; the bf16 output rows are written 16 bytes per row and instruction).
+// D a power of two, normalized (O / l) in bf16: out = sum_s 2^(m_s - M) l_s O_s /
+// sum_s 2^(m_s - M) l_s.  Thread t takes the 4 values at 4 t of each split, so that a
+// wave's partial reads are 512 bytes of consecutive bytes (the reads are SB times the
+// writes; the bf16 output rows are written 8 bytes per row and instruction).
 template <typename T, int VEC, typename I, int SB, bool FRAG>
 __global__ void __launch_bounds__(256) k_attn_combine(AttnParams p, int D) {
   static_assert(!FRAG || VEC == 4, "fragment order: 4 floats per thread");
@@ -349,21 +350,34 @@ __global__ void __launch_bounds__(256) k_attn_combine(AttnParams p, int D) {
     }
     // partials of splits s0 .. s0 + SB - 1 (pad rows, and the spare rows of a query
     // tile, have none written: their values are read but not used)
-    float mv[SB], lv[SB], ov[SB][VEC];
+    // (fragment order: the packed bf16 pairs as loaded, widened only where they are
+    // used -- widening them here would make each split's load wait before the next
+    // split's goes out)
+    float mv[SB], lv[SB], ov[SB][FRAG ? 1 : VEC];
+    uint32_t pk[SB][2];
     auto fetch = [&](int s0) __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < SB; ++j) {
         mv[j] = -INFINITY;
         lv[j] = 0.f;
+        if constexpr (FRAG) {
+          pk[j][0] = pk[j][1] = 0u;
+        } else {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) ov[j][e] = 0.f;
+          for (int e = 0; e < VEC; ++e) ov[j][e] = 0.f;
+        }
         if (s0 + j < nsp) {
           const I sj = static_cast<I>(s0 + j);
           const float2 ml = *reinterpret_cast<const float2 *>(p.wml + (sj * ms + ml_at));
           mv[j] = ml.x;
           lv[j] = ml.y;
           const float *src = p.wo + (sj * os + o_at);
-          if constexpr (VEC == 4) {
+          if constexpr (FRAG) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(
+                reinterpret_cast<const uint16_t *>(p.wo) + (sj * os + o_at));
+            pk[j][0] = v.x;
+            pk[j][1] = v.y;
+          } else if constexpr (VEC == 4) {
             const float4 v = *reinterpret_cast<const float4 *>(src);
             ov[j][0] = v.x;
             ov[j][1] = v.y;
@@ -425,8 +439,16 @@ __global__ void __launch_bounds__(256) k_attn_combine(AttnParams p, int D) {
         for (int j = 0; j < SB; ++j) {
           const float wgt = __builtin_amdgcn_exp2f(mv[j] - Mn);
           l = fmaf(wgt, lv[j], l);
+          if constexpr (FRAG) {
+            const float wo = wgt * lv[j];  // normalized partials carry l apart
+            o[0] = fmaf(wo, __uint_as_float(pk[j][0] << 16), o[0]);
+            o[1] = fmaf(wo, __uint_as_float(pk[j][0] & 0xffff0000u), o[1]);
+            o[2] = fmaf(wo, __uint_as_float(pk[j][1] << 16), o[2]);
+            o[3] = fmaf(wo, __uint_as_float(pk[j][1] & 0xffff0000u), o[3]);
+          } else {
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) o[e] = fmaf(wgt, ov[j][e], o[e]);
+            for (int e = 0; e < VEC; ++e) o[e] = fmaf(wgt, ov[j][e], o[e]);
+          }
         }
         M = Mn;
       }

@@ -169,6 +169,10 @@ static size_t partial_rows(const cp_cache &c, const cp_attn_args &a, const AttnP
   return static_cast<size_t>(c.B) * a.H * a.C;
 }
 
+// Bytes per partial O element: the matrix-core kernel stores normalized bf16, the
+// vector-ALU kernel fp32 sums.
+static size_t partial_esize(const AttnPlan &p) { return p.mfma ? 2 : 4; }
+
 // Planned mode: the plan (header, items, split entries), then the partials of at most
 // plan_grid slots in fragment order, then their (m, l).
 static size_t plan_bytes(const AttnPlan &p) {
@@ -179,12 +183,12 @@ static size_t plan_bytes(const AttnPlan &p) {
 size_t attn_workspace_bytes(const cp_cache &c, const cp_attn_args &a, const AttnPlan &p) {
   if (p.planned) {
     const size_t rows = static_cast<size_t>(p.plan_grid) * p.rows;
-    return plan_bytes(p) + round256(rows * c.D * sizeof(float)) +
+    return plan_bytes(p) + round256(rows * c.D * partial_esize(p)) +
            round256(rows * 2 * sizeof(float));
   }
   if (p.splits <= 1) return 0;
   const size_t rows = partial_rows(c, a, p);
-  return round256(static_cast<size_t>(p.splits) * rows * c.D * sizeof(float)) +
+  return round256(static_cast<size_t>(p.splits) * rows * c.D * partial_esize(p)) +
          round256(static_cast<size_t>(p.splits) * rows * 2 * sizeof(float));
 }
 
@@ -236,14 +240,15 @@ hipError_t launch_attention(const cp_cache &c, const cp_attn_args &a, hipStream_
     p.plan_kt = pl.kt;
     p.plan_tmin = kPlanMinTiles;
     p.wo = reinterpret_cast<float *>(w + plan_bytes(pl));
-    p.wml = reinterpret_cast<float *>(w + plan_bytes(pl) + round256(rows * c.D * sizeof(float)));
+    p.wml = reinterpret_cast<float *>(w + plan_bytes(pl) +
+                                      round256(rows * c.D * partial_esize(pl)));
     p.advance = advance ? 1 : 0;
   } else if (pl.splits > 1) {
     const size_t rows = partial_rows(c, a, pl);
     unsigned char *w = static_cast<unsigned char *>(a.workspace);
     p.wo = reinterpret_cast<float *>(w);
     p.wml = reinterpret_cast<float *>(
-        w + round256(static_cast<size_t>(pl.splits) * rows * c.D * sizeof(float)));
+        w + round256(static_cast<size_t>(pl.splits) * rows * c.D * partial_esize(pl)));
   }
   if (static_cast<size_t>(c.B) * a.H * a.C == 0)
     return advance ? launch_advance_seen(c, a.C, a.n_valid, s) : hipSuccess;

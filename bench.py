@@ -126,6 +126,9 @@ class Layer:
             self.mask = cp.build_mask(self.caches[0], d["n_valid"], cfg.H, cfg.C, cfg.mask_ld())
         self.static = bool(cfg.ring) and any(n < cfg.C for n in cfg.n_valid)
         self.window = 0 if cfg.explicit_mask else cfg.window
+        # the host knows the past lengths it generated: the attention sizes its key
+        # splits from the longest (a serving scheduler holds them the same way)
+        self.max_seen = max(1, max(cfg.seen))
         self.bufs = path.make_buffers(self.caches[0], d["q"], d["k"], d["v"], mask=self.mask,
                                       window=self.window, static_append=self.static, flags=flags)
 
@@ -136,7 +139,7 @@ class Layer:
         d = self.d
         path.chunk_step(self.caches[s], d["q"], d["k"], d["v"], d["cos"], d["sin"],
                         d["n_valid"], self.bufs, mask=self.mask, window=self.window,
-                        static_append=self.static, flags=self.flags)
+                        static_append=self.static, flags=self.flags, max_seen=self.max_seen)
 
     def attn_only(self, cp):
         """The attention call in the step's configuration (for large chunks the kernel
@@ -147,7 +150,8 @@ class Layer:
         cp.attn_chunk_with_past(self.caches[0], d["q"] if fold else b.q_rot, b.k_rot, d["v"],
                                 n_valid=d["n_valid"], mask=self.mask, window=self.window,
                                 scale=self.cfg.scale, out=b.out, workspace=b.workspace,
-                                flags=self.flags, q_rope=(d["cos"], d["sin"]) if fold else None)
+                                flags=self.flags, q_rope=(d["cos"], d["sin"]) if fold else None,
+                                max_seen=self.max_seen)
 
 
 def time_graph(fn, reps_inside, replays=1):

@@ -28,7 +28,7 @@ ATTN_BALANCE = 16
 def ATTN_SPLITS(n: int) -> int:
     """CP_ATTN_SPLITS(n): force n key splits (bits 8..15 of the flags)."""
     return (int(n) & 0xFF) << 8
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libcp.so is not built ({LIB_PATH}); run "
@@ -58,7 +58,7 @@ class AttnArgs(ctypes.Structure):
                 ("flags", ctypes.c_uint32), ("reserved", ctypes.c_int32),
                 ("select_out", ctypes.c_void_p), ("q_cos", ctypes.c_void_p),
                 ("q_sin", ctypes.c_void_p), ("q_tables", ctypes.c_int32),
-                ("reserved2", ctypes.c_int32)]
+                ("max_seen", ctypes.c_int32)]
 
 
 _vp, _i = ctypes.c_void_p, ctypes.c_int
@@ -336,7 +336,7 @@ def kv_append_rollback(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor,
 # ---------------------------------------------------------------- attention
 
 def _attn_args(cache, q, k_new, v_new, out, n_valid, mask, window, scale, workspace, flags,
-               select_out=None, q_rope=None):
+               select_out=None, q_rope=None, max_seen=0):
     B, H, C, D = q.shape
     if scale is None:
         scale = float(torch.tensor(1.0 / D ** 0.5, dtype=torch.float32))
@@ -363,13 +363,14 @@ def _attn_args(cache, q, k_new, v_new, out, n_valid, mask, window, scale, worksp
                     _opt(n_valid, "n_valid", torch.int32), mptr, mld, mhs, mbs, ws_ptr, ws_bytes,
                     H, C, int(window), float(scale), int(flags), 0,
                     _dev(select_out, "select_out") if select_out is not None else None,
-                    qc, qs, qt, 0)
+                    qc, qs, qt, int(max_seen))
 
 
 def attn_workspace_bytes(cache: KVCache, q: torch.Tensor, k_new: torch.Tensor,
                          v_new: torch.Tensor, mask: Optional[torch.Tensor] = None,
-                         window: int = 0, flags: int = 0) -> int:
-    a = _attn_args(cache, q, k_new, v_new, q, None, mask, window, None, None, flags)
+                         window: int = 0, flags: int = 0, max_seen: int = 0) -> int:
+    a = _attn_args(cache, q, k_new, v_new, q, None, mask, window, None, None, flags,
+                   max_seen=max_seen)
     return int(_lib.cp_attn_workspace_bytes(ctypes.byref(cache.desc), ctypes.byref(a)))
 
 
@@ -380,11 +381,12 @@ def attn_chunk_with_past(cache: KVCache, q: torch.Tensor, k_new: torch.Tensor,
                          workspace: Optional[torch.Tensor] = None,
                          flags: int = 0,
                          select_out: Optional[torch.Tensor] = None,
-                         q_rope=None) -> torch.Tensor:
+                         q_rope=None, max_seen: int = 0) -> torch.Tensor:
     """cp_attn_chunk_with_past over the cache as it stands (before the append).
 
     select_out [B, H, D] (optional) also receives the last real row of each (b, h).
     q_rope = (cos, sin): q is not rotated yet; the kernel rotates it with these tables.
+    max_seen: 0, or the host's upper bound on every seen (sizes the key splits).
     """
     if out is None:
         out = torch.empty_like(q)
@@ -392,7 +394,7 @@ def attn_chunk_with_past(cache: KVCache, q: torch.Tensor, k_new: torch.Tensor,
                                    select_out.shape != (q.shape[0], q.shape[1], q.shape[3])):
         raise ValueError("select_out must be [B, H, D] of q's dtype")
     a = _attn_args(cache, q, k_new, v_new, out, n_valid, mask, window, scale, workspace, flags,
-                   select_out, q_rope)
+                   select_out, q_rope, max_seen)
     _check(_lib.cp_attn_chunk_with_past(ctypes.byref(cache.desc), ctypes.byref(a), _stream()),
            "cp_attn_chunk_with_past")
     return out
@@ -404,14 +406,14 @@ def attn_chunk_with_past_noalloc(cache: KVCache, q: torch.Tensor, k_new: torch.T
                                  mask: Optional[torch.Tensor] = None, window: int = 0,
                                  scale: Optional[float] = None, flags: int = 0,
                                  select_out: Optional[torch.Tensor] = None,
-                                 q_rope=None) -> torch.Tensor:
+                                 q_rope=None, max_seen: int = 0) -> torch.Tensor:
     """cp_attn_chunk_with_past_noalloc: the same attention with the key-split partials in
     the library's own device array (no workspace; the caller passes its output)."""
     if select_out is not None and (select_out.dtype != q.dtype or
                                    select_out.shape != (q.shape[0], q.shape[1], q.shape[3])):
         raise ValueError("select_out must be [B, H, D] of q's dtype")
     a = _attn_args(cache, q, k_new, v_new, out, n_valid, mask, window, scale, None, flags,
-                   select_out, q_rope)
+                   select_out, q_rope, max_seen)
     _check(_lib.cp_attn_chunk_with_past_noalloc(ctypes.byref(cache.desc), ctypes.byref(a),
                                                 _stream()), "cp_attn_chunk_with_past_noalloc")
     return out

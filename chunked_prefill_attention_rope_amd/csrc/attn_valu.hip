@@ -305,11 +305,11 @@ __global__ void __launch_bounds__(256) k_attn_valu(AttnParams p, int D) {
 // FRAG: the partials are in the matrix-core kernel's fragment order (AttnParams::wo),
 // D a power of two, normalized (O / l) in bf16: out = sum_s 2^(m_s - M) l_s O_s /
 // sum_s 2^(m_s - M) l_s.  Thread t takes the 4 values at 4 t of each split, so that a
-// wave's partial reads are 512 bytes of consecutive bytes (the reads are SB times the
-// writes; the bf16 output rows are written 8 bytes per row and instruction).
+// wave's partial reads are 512 consecutive bytes (the reads are SB times the writes;
+// the bf16 output rows are written 8 bytes per row and instruction).
 template <typename T, int VEC, typename I, int SB, bool FRAG>
 __global__ void __launch_bounds__(256) k_attn_combine(AttnParams p, int D) {
-  static_assert(!FRAG || VEC == 4, "fragment order: 4 floats per thread");
+  static_assert(!FRAG || (VEC == 4 && sizeof(T) == 2), "fragment order: 4 bf16 per thread");
   const size_t rows = static_cast<size_t>(p.B) * p.H * p.C;
   // rows of one split's partials (fragment order: every row of every query tile)
   const size_t prow = FRAG ? static_cast<size_t>(p.B) * p.nKV * p.qtiles * p.frag_rows : rows;
@@ -456,8 +456,17 @@ __global__ void __launch_bounds__(256) k_attn_combine(AttnParams p, int D) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) res[e] = o[e] * inv;
     }
+    if constexpr (FRAG) {
+      // one 8-byte store per lane (the matrix-core path's out is 16-byte aligned and
+      // d0 a multiple of 4); four 2-byte stores made partial-line writes
+      const uint2 w = make_uint2(
+          f32_to_bf16_rne(res[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(res[1])) << 16),
+          f32_to_bf16_rne(res[2]) | (static_cast<uint32_t>(f32_to_bf16_rne(res[3])) << 16));
+      *reinterpret_cast<uint2 *>(O + (row * D + d0)) = w;
+    } else {
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) st(O, row * D + d0 + e, res[e]);
+      for (int e = 0; e < VEC; ++e) st(O, row * D + d0 + e, res[e]);
+    }
     if (p.sel && i == selected_row(nv)) {
       T *S = static_cast<T *>(p.sel) + static_cast<size_t>(bh) * D + d0;  // bh = b * H + h
 #pragma unroll

@@ -24,7 +24,7 @@ int valu_keys(int D);
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 constexpr int kNumCU = 256;
 // Fewest key tiles per piece of a balanced split (each workgroup pays a prologue and the
 // first tile's latency, about two tiles' time).
@@ -101,28 +101,32 @@ AttnPlan plan_attention(const cp_cache &c, const cp_attn_args &a, bool for_works
   pl.qtiles = (a.C + pl.qpos - 1) / pl.qpos;
   pl.splits = 1;
   const long base = static_cast<long>(pl.qtiles) * hgroups * c.B * c.nKV;
-  long keys = static_cast<long>(c.cap) + a.C;
+  // keys one query tile can see: the live past (at most the capacity, or the caller's
+  // bound on seen) and the chunk, or the window's reach
+  long keys = static_cast<long>(a.max_seen > 0 && a.max_seen < c.cap ? a.max_seen : c.cap) + a.C;
   if (a.window > 0 && !a.mask) {
     const long wk = static_cast<long>(a.window) + pl.qpos + c.sink;
     if (wk < keys) keys = wk;
   }
   const long tiles = (keys + pl.kt - 1) / pl.kt;
   const int forced = static_cast<int>((a.flags >> 8) & 0xffu);
-  // Few query tiles: split the keys so that more CUs work -- each split writes fp32
+  // Few query tiles: split the keys so that more CUs work -- each split writes
   // partials that a second kernel merges.  The matrix-core kernel keeps >= 2 key tiles
   // per split (its prologue and first-tile latency is paid per workgroup; with the
   // merge reading all splits in one round, 2 measured best: the 864-key D = 256 chunk
   // step 18.75 -> 18.50 us, the 640-key ring step 22.05 -> 20.59 us against 3); the
   // vector-ALU kernel's 16-key tiles each cost a memory round trip that their
   // arithmetic does not hide, so it goes down to one tile per split.  The tile count is
-  // a bound from the capacity (the live length is on the device), so a split can get
-  // one tile less than this.
+  // a bound (from the capacity or max_seen; the live length is on the device), so a
+  // split can get one tile less than this.  Rounded up: an odd count leaves one split a
+  // single tile rather than one split three (the 864-key chunk: 14 splits 13.96 us per
+  // call, 13 or 12 splits 15.4).
   const long per = pl.mfma ? 2 : 1;
   // as many splits as fill the CUs once (rounded down: a partial second round of
   // workgroups would double the time of the last ones)
   auto split_for = [&](long wg_per_cu) {
     long s = wg_per_cu * kNumCU / base;
-    if (s > tiles / per) s = tiles / per;
+    if (s > (tiles + per - 1) / per) s = (tiles + per - 1) / per;
     if (s > 64) s = 64;
     return s > 1 ? static_cast<int>(s) : 1;
   };
@@ -476,7 +480,7 @@ static int check_attn(const cp_cache *cache, const cp_attn_args *a) {
   if (!cache->ring && a->C > cache->cap) return CP_ERR_SHAPE;
   if (a->mask && (a->mask_ld < a->C || a->mask_head_stride < 0 || a->mask_batch_stride < 0))
     return CP_ERR_ARG;
-  if (a->reserved2 != 0 || (!a->q_cos) != (!a->q_sin)) return CP_ERR_ARG;
+  if (a->max_seen < 0 || (!a->q_cos) != (!a->q_sin)) return CP_ERR_ARG;
   if (a->q_cos) {
     if (a->q_tables != 1 && a->q_tables != cache->B) return CP_ERR_ARG;
     if (cache->D % 2 != 0) return CP_ERR_SHAPE;

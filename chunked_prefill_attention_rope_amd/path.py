@@ -78,8 +78,11 @@ def rope_q_in_attention(q: torch.Tensor) -> bool:
 
 def chunk_step(cache: cp.KVCache, q, k, v, cos, sin, n_valid, bufs: StepBuffers,
                mask: Optional[torch.Tensor] = None, window: int = 0,
-               static_append: bool = False, flags: int = 0):
+               static_append: bool = False, flags: int = 0, max_seen: int = 0):
     """Run the whole hot path of one layer for one chunk; returns (out, selected row).
+
+    max_seen: 0, or an upper bound on every sequence's seen known on the host (the
+    attention sizes its key splits from it instead of from the cache capacity).
 
     A global cache takes the fused form: the RoPE launch also writes the chunk's K/V
     rows past seen (slots this chunk's attention does not read), and the attention call
@@ -95,7 +98,8 @@ def chunk_step(cache: cp.KVCache, q, k, v, cos, sin, n_valid, bufs: StepBuffers,
     qr, q_in, q_rope = (None, q, (cos, sin)) if fold else (q, bufs.q_rot, None)
     attn = lambda fl: cp.attn_chunk_with_past(  # noqa: E731
         cache, q_in, bufs.k_rot, v, n_valid=n_valid, mask=mask, window=window, out=bufs.out,
-        workspace=bufs.workspace, flags=fl, select_out=bufs.sel, q_rope=q_rope)
+        workspace=bufs.workspace, flags=fl, select_out=bufs.sel, q_rope=q_rope,
+        max_seen=max_seen)
     if not cache.ring and not static_append:
         cp.rope_qk_append_chunk(cache, qr, k, v, cos, sin, n_valid, q_out=bufs.q_rot,
                                 k_out=bufs.k_rot)
@@ -244,12 +248,15 @@ def prompt_chunks(cache: cp.KVCache, q, k, v, cos, sin, C: int, window: int = 0,
 
 
 def prefill(cache: cp.KVCache, pc: PromptChunks, window: int = 0,
-            static_append: bool = False):
+            static_append: bool = False, seen_start: Optional[int] = None):
     """Run a whole prompt chunk after chunk (the cache grows as it goes); returns the last
-    chunk's selection (the prompt's last real row)."""
+    chunk's selection (the prompt's last real row).  seen_start: the largest seen before
+    the prompt, when the host knows it -- chunk c then passes seen_start + c * C as the
+    attention's bound on seen (at least 1: 0 means no bound)."""
     for c in range(len(pc.q)):
+        ms = 0 if seen_start is None else max(1, seen_start + c * pc.C)
         chunk_step(cache, pc.q[c], pc.k[c], pc.v[c], pc.cos[c], pc.sin[c], pc.n_valid[c],
-                   pc.bufs[c], window=window, static_append=static_append)
+                   pc.bufs[c], window=window, static_append=static_append, max_seen=ms)
     return pc.bufs[-1].sel
 
 

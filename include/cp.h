@@ -177,6 +177,15 @@ typedef struct cp_snapshot {
  *              cp_rope_chunk(q) followed by the call with the rotated q ([SKaiNET]
  *              "Change (additive)": RoPE from per-position tables; here folded into
  *              the attention's load of Q, so the rotated queries never go to memory).
+ *   max_seen   0, or an upper bound on every sequence's seen that the caller knows on
+ *              the host (a serving scheduler holds the lengths; the device counters
+ *              are not read back).  The host planner sizes the key splits from it
+ *              instead of from the capacity, so that a past much shorter than the
+ *              cache does not get more splits than it has key tiles.  It chooses the
+ *              split count only: every sequence's keys are still divided on the device
+ *              by its own live length, so a bound below some seen is not an error
+ *              (the results are those of a call with that split count).  Negative:
+ *              CP_ERR_ARG.
  *
  * The cache is read as it stands BEFORE the chunk is appended.
  */
@@ -202,7 +211,7 @@ typedef struct cp_attn_args {
   const float *q_cos;
   const float *q_sin;
   int32_t q_tables;
-  int32_t reserved2; /* must be 0 */
+  int32_t max_seen;
 } cp_attn_args;
 
 #define CP_ATTN_NO_SPLIT 1u      /* one pass per query tile, no key split */

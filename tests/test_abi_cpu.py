@@ -166,6 +166,27 @@ def test_rollback_requires_armed_matching_snapshot(cp):
                                             None) == cp.ERR_STATE
 
 
+def test_split_count_from_max_seen(cp):
+    """Host planner: the key splits of a one-sequence chunk are counted from max_seen
+    when the caller gives it (else from the capacity), two 32-key tiles per split, the
+    count rounded up.  Read off the workspace size, which is splits x partial rows x
+    (D bf16 + fp32 m and l)."""
+    lib = cp.raw()
+    c = _cache(cp, B=1, nKV=1, cap=1024, D=256)
+
+    def ws(max_seen):
+        a = cp.AttnArgs(q=FAKE, k_new=FAKE, v_new=FAKE, out=FAKE, mask=FAKE, mask_ld=1088,
+                        mask_head_stride=64 * 1088, H=4, C=64, scale=0.0625, max_seen=max_seen)
+        return lib.cp_attn_workspace_bytes(ctypes.byref(c), ctypes.byref(a))
+
+    rows = 256  # two 128-row query tiles (4 heads x 32 chunk rows)
+    per_split = rows * 256 * 2 + rows * 2 * 4
+    assert ws(0) == 17 * per_split      # 1024 + 64 keys: 34 tiles
+    assert ws(5000) == ws(0)            # a bound above the capacity changes nothing
+    assert ws(800) == 14 * per_split    # 800 + 64 keys: 27 tiles, rounded up
+    assert ws(1) == 2 * per_split       # 1 + 64 keys: 3 tiles
+
+
 def test_attention_validation(cp):
     lib = cp.raw()
     c = _cache(cp)
@@ -174,7 +195,7 @@ def test_attention_validation(cp):
         d = dict(q=FAKE, k_new=FAKE, v_new=FAKE, out=FAKE, n_valid=None, mask=None, mask_ld=0,
                  mask_head_stride=0, mask_batch_stride=0, workspace=None, workspace_bytes=0,
                  H=8, C=16, window=0, scale=0.1, flags=0, reserved=0, q_cos=None, q_sin=None,
-                 q_tables=0, reserved2=0)
+                 q_tables=0, max_seen=0)
         d.update(kw)
         return cp.AttnArgs(**d)
 
@@ -188,7 +209,7 @@ def test_attention_validation(cp):
     assert f(ctypes.byref(c), ctypes.byref(args(q_cos=FAKE)), None) == cp.ERR_ARG
     assert f(ctypes.byref(c), ctypes.byref(args(q_cos=FAKE, q_sin=FAKE, q_tables=3)),
              None) == cp.ERR_ARG
-    assert f(ctypes.byref(c), ctypes.byref(args(reserved2=1)), None) == cp.ERR_ARG
+    assert f(ctypes.byref(c), ctypes.byref(args(max_seen=-1)), None) == cp.ERR_ARG
     odd = _cache(cp, D=63)
     assert f(ctypes.byref(odd), ctypes.byref(args(q_cos=FAKE, q_sin=FAKE, q_tables=1)),
              None) == cp.ERR_SHAPE

@@ -448,3 +448,34 @@ def test_merge_rounds(cp, splits, mode):
     assert np.array_equal(bits(outs[1]), bits(outs[0]))
     assert np.array_equal(bits(sel), bits(cp.select_row(outs[0], nv, -1)))
     assert int(status.item()) == 0
+
+
+@pytest.mark.parametrize("max_seen", [1, 400, 800, 5000])
+@pytest.mark.parametrize("mode", ["inkernel", "explicit"])
+def test_max_seen_bound(cp, max_seen, mode):
+    """The Gemma-270M-like chunk (seen 800, capacity 1024, 32-key tiles) with a host bound
+    on seen: exact (800), loose (5000: the capacity rules), or below the real seen (1,
+    400 -- it only sizes the splits, the device still divides each sequence's own live
+    tiles).  Within tolerance of the oracle in every case, and bit for bit the call that
+    forces the split count the bound implies: ceil(tiles / 2) for
+    tiles = ceil((min(max_seen, 1024) + 64) / 32)."""
+    cfg = I.config("c2")
+    t, cache, status = _setup(cp, cfg)
+    q, k, v = dev(t["q"]), dev(t["k"]), dev(t["v"])
+    nv = dev(t["n_valid"])
+    mask = None
+    if mode == "explicit":
+        mask = cp.build_mask(cache, nv, cfg.H, cfg.C, cfg.mask_ld())
+    tiles = (min(max_seen, cfg.cap) + cfg.C + 31) // 32
+    splits = (tiles + 1) // 2
+    outs = []
+    for flags, ms in ((0, max_seen), (cp.ATTN_SPLITS(splits), 0)):
+        nb = cp.attn_workspace_bytes(cache, q, k, v, mask=mask, flags=flags, max_seen=ms)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        outs.append(cp.attn_chunk_with_past(cache, q, k, v, n_valid=nv, mask=mask,
+                                            scale=cfg.scale, workspace=ws, flags=flags,
+                                            max_seen=ms))
+    torch.cuda.synchronize()
+    _check(cfg, outs[0], _oracle(cfg, t))
+    assert np.array_equal(bits(outs[0]), bits(outs[1]))
+    assert int(status.item()) == 0

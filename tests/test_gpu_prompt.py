@@ -34,11 +34,13 @@ def test_prompt_in_chunks_of_any_size(case):
                                    kr, I.np_view(t["v"]), I.np_view(t["n_valid"]), cfg.ring,
                                    cfg.sink)
     q, k, v, cos, sin = (dev(t[n]) for n in ("q", "k", "v", "cos", "sin"))
-    for C in (8, 16, 33, 64):
+    # seen_start: the host's bound on seen before the prompt (sizes the key splits only)
+    ms = max(cfg.seen)
+    for C, ss in ((8, None), (16, None), (33, None), (64, None), (16, ms), (33, ms)):
         cache = cp.KVCache(dev(t["kc"]), dev(t["vc"]), dev(t["seen"]), ring=cfg.ring,
                            sink=cfg.sink)
         pc = path.prompt_chunks(cache, q, k, v, cos, sin, C, window=cfg.window)
-        sel = path.prefill(cache, pc, window=cfg.window)
+        sel = path.prefill(cache, pc, window=cfg.window, seen_start=ss)
         torch.cuda.synchronize()
         got = np.concatenate([to_f64(b.out) for b in pc.bufs], axis=2)[:, :, :P]
         assert rowwise_rel_err(got, ref) <= TOL[I.BF16], C

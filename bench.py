@@ -112,7 +112,8 @@ class Layer:
 
     def __init__(self, cp, path, cfg, nsteps, flags=0):
         self.cfg = cfg
-        self.flags = flags
+        # no flags given: the ones a caller that knows its past lengths would pass
+        self.flags = flags if flags else path.attn_flags_for(cfg.seen)
         t = I.make_layer(cfg, nan_dead=False)
         self.host = t
         d = {k: v.to("cuda") for k, v in t.items()}
@@ -130,7 +131,8 @@ class Layer:
         # splits from the longest (a serving scheduler holds them the same way)
         self.max_seen = max(1, max(cfg.seen))
         self.bufs = path.make_buffers(self.caches[0], d["q"], d["k"], d["v"], mask=self.mask,
-                                      window=self.window, static_append=self.static, flags=flags)
+                                      window=self.window, static_append=self.static,
+                                      flags=self.flags)
 
     def reset(self):
         self.seen_all.copy_(self.seen0.expand_as(self.seen_all))
@@ -578,7 +580,7 @@ def main():
         roof = {"bound": "mfma" if lay_dom.cfg.dtype == I.BF16 else "alu",
                 "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 5)}
-    roof["traffic"] = measured_traffic(args.workload, args.attn_flags)
+    roof["traffic"] = measured_traffic(args.workload, lay_dom.flags)
     roof["kernel"] = "cp_attn_chunk_with_past"
     roof["avg_launch_us"] = round(attn_ms * 1e3, 3)
     roof["algorithmic_bytes"] = nbytes
@@ -594,7 +596,8 @@ def main():
                    "value_is": "real tokens per layer x layers per step / step time",
                    "stack_tok_per_s": round(stack_tok_s, 1),
                    "launch": mode, "eager_ms_per_step": round(eager_ms, 6),
-                   "attn_flags": args.attn_flags},
+                   "attn_flags": lay_dom.flags,
+                   "max_seen": lay_dom.max_seen},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -23,23 +23,43 @@
 namespace cp {
 namespace {
 
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 256;
+constexpr int kMergeRound = 4;  // pieces the plan merge fetches per memory round trip
 
-// exclusive prefix sums of in[0..n) into out[0..n] (out[n] = total); n <= blockDim.x;
-// every thread of the block calls it
-__device__ void block_scan(const int *in, int *out, int n, int *buf) {
-  const int t = threadIdx.x;
-  buf[t] = t < n ? in[t] : 0;
-  __syncthreads();
-  for (int off = 1; off < static_cast<int>(blockDim.x); off <<= 1) {
-    const int add = t >= off ? buf[t - off] : 0;
-    __syncthreads();
-    buf[t] += add;
-    __syncthreads();
+// Exclusive prefix sums of in[0, n) into out[0, n], out[n] = the total; every thread of
+// the block calls it (in and out distinct).  Each thread sums a run of consecutive
+// elements, the runs' sums are scanned within each wave by lane shuffles, and the waves'
+// totals are added through LDS: two barriers (a log-step scan through LDS costs two per
+// step, each behind an LDS round trip).
+__device__ void block_scan(const int *in, int *out, int n, int *wsum) {
+  const int t = threadIdx.x, nt = blockDim.x;
+  const int per = (n + nt - 1) / nt;
+  const int lo = imin(n, t * per), hi = imin(n, lo + per);
+  int sum = 0;
+  for (int k = lo; k < hi; ++k) sum += in[k];
+  const int lane = t & 63, w = t >> 6;
+  int x = sum;  // inclusive scan over the wave
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
   }
-  if (t < n) out[t + 1] = buf[t];
-  if (t == 0) out[0] = 0;
+  if (lane == 63) wsum[w] = x;
   __syncthreads();
+  int run = x - sum;
+  for (int v = 0; v < w; ++v) run += wsum[v];
+  for (int k = lo; k < hi; ++k) {
+    out[k] = run;
+    run += in[k];
+  }
+  if (t == nt - 1) out[n] = run;  // the last thread's run ends at the total
+  __syncthreads();
+}
+
+// Sum of v over the block, added into *acc (which the caller zeroed and publishes with a
+// barrier): a shuffle reduction per wave, one LDS atomic per wave.
+__device__ void block_add(int v, int *acc) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) atomicAdd(acc, v);
 }
 
 __global__ void __launch_bounds__(kPlanThreads) k_attn_plan(AttnParams p, int32_t *plan) {
@@ -49,17 +69,21 @@ __global__ void __launch_bounds__(kPlanThreads) k_attn_plan(AttnParams p, int32_
   __shared__ int order_s[kPlanMaxB];  // sequences by rank
   __shared__ int tmp_s[kPlanMaxB];
   __shared__ int upre_s[kPlanMaxB + 1], gpre_s[kPlanMaxB + 1], spre_s[kPlanMaxB + 1];
-  __shared__ int buf_s[kPlanThreads];
+  __shared__ int seen_s[kPlanMaxB], nvr_s[kPlanMaxB];  // seen and raw n_valid, read once
+  __shared__ int wsum_s[kPlanThreads / 64];
   __shared__ int tot_s, sum_s, T_s;
-  const int t = threadIdx.x, nt = static_cast<int>(blockDim.x);  // nt >= B (one per sequence)
+  const int t = threadIdx.x, nt = static_cast<int>(blockDim.x);
   const int B = p.B;
   const bool explicit_mask = p.mask != nullptr;
   if (t == 0) tot_s = 0;
   __syncthreads();
   // 1. tile counts per sequence (bad sequences count nothing; the attention flags them)
+  int tot = 0;
   for (int b = t; b < B; b += nt) {
     const int seen = p.seen[b];
     int nv = p.n_valid ? p.n_valid[b] : p.C;
+    seen_s[b] = seen;
+    nvr_s[b] = nv;
     nv = nv < 0 ? 0 : (nv > p.C ? p.C : nv);
     bool bad = seen < 0 || (!p.ring && seen > p.cap);
     const Live gl = live_geometry(bad ? 0 : seen, p.cap, p.ring, p.sink);
@@ -76,8 +100,9 @@ __global__ void __launch_bounds__(kPlanThreads) k_attn_plan(AttnParams p, int32_
       sum += ts.count();
     }
     nb_s[b] = nmax;
-    atomicAdd(&tot_s, sum);
+    tot += sum;
   }
+  block_add(tot, &tot_s);
   __syncthreads();
   // 2. piece length: at least plan_tmin tiles and the total over the resident slots;
   // longer while the items would not fit the launch's grid (its last group of 8 padded)
@@ -93,7 +118,7 @@ __global__ void __launch_bounds__(kPlanThreads) k_attn_plan(AttnParams p, int32_
     __syncthreads();
     int part = 0;
     for (int b = t; b < B; b += nt) part += imax(1, (nb_s[b] + T - 1) / T);
-    atomicAdd(&sum_s, part);
+    block_add(part, &sum_s);
     __syncthreads();
     const int units = sum_s * p.nKV;
     const bool fits = ((units + 7) / 8) * 8 * p.qtiles <= p.plan_grid;
@@ -121,13 +146,13 @@ __global__ void __launch_bounds__(kPlanThreads) k_attn_plan(AttnParams p, int32_
   // sequence order
   for (int k = t; k < B; k += nt) tmp_s[k] = pc_s[order_s[k]] * p.nKV;
   __syncthreads();
-  block_scan(tmp_s, upre_s, B, buf_s);
+  block_scan(tmp_s, upre_s, B, wsum_s);
   for (int b = t; b < B; b += nt) tmp_s[b] = pc_s[b] > 1 ? p.nKV * p.qtiles : 0;
   __syncthreads();
-  block_scan(tmp_s, gpre_s, B, buf_s);
+  block_scan(tmp_s, gpre_s, B, wsum_s);
   for (int b = t; b < B; b += nt) tmp_s[b] = pc_s[b] > 1 ? p.nKV * p.qtiles * pc_s[b] : 0;
   __syncthreads();
-  block_scan(tmp_s, spre_s, B, buf_s);
+  block_scan(tmp_s, spre_s, B, wsum_s);
   const int U = upre_s[B];
   // 5. one item per block: unit r's query tile q at block (r / 8) * 8 * qtiles + 8 q + r % 8
   int32_t *items = plan + kPlanHeaderInts;
@@ -155,27 +180,23 @@ __global__ void __launch_bounds__(kPlanThreads) k_attn_plan(AttnParams p, int32_
     it[3] = piece;
     it[4] = P;
     it[5] = P > 1 ? spre_s[b] + (g * p.qtiles + q) * P + piece : -1;
-    it[6] = p.seen[b];
-    it[7] = p.n_valid ? p.n_valid[b] : p.C;
+    it[6] = seen_s[b];  // (from LDS: a global read here would cost every item a round trip)
+    it[7] = nvr_s[b];
   }
-  // 6. the split entries, for the merge
+  // 6. the split entries, for the merge: one thread per (sequence, KV head, query tile)
   int32_t *groups = items + static_cast<size_t>(p.plan_grid) * kPlanItemInts;
-  for (int b = t; b < B; b += nt) {
+  const int per_b = p.nKV * p.qtiles;
+  for (int x = t; x < B * per_b; x += nt) {
+    const int b = x / per_b, j = x - b * per_b;
     const int P = pc_s[b];
     if (P <= 1) continue;
-    int nv = p.n_valid ? p.n_valid[b] : p.C;
-    nv = nv < 0 ? 0 : (nv > p.C ? p.C : nv);
-    for (int g = 0; g < p.nKV; ++g)
-      for (int q = 0; q < p.qtiles; ++q) {
-        const int j = g * p.qtiles + q;
-        int32_t *e = groups + static_cast<size_t>(gpre_s[b] + j) * kPlanItemInts;
-        e[0] = b;
-        e[1] = g;
-        e[2] = q;
-        e[3] = P;
-        e[4] = spre_s[b] + j * P;
-        e[5] = nv;
-      }
+    int32_t *e = groups + static_cast<size_t>(gpre_s[b] + j) * kPlanItemInts;
+    e[0] = b;
+    e[1] = j / p.qtiles;
+    e[2] = j % p.qtiles;
+    e[3] = P;
+    e[4] = spre_s[b] + j * P;
+    e[5] = imin(imax(nvr_s[b], 0), p.C);
   }
   if (t == 0) {
     plan[0] = gpre_s[B];  // split entries
@@ -212,31 +233,54 @@ __global__ void __launch_bounds__(256) k_attn_merge_plan(AttnParams p, int D) {
     const int d0 = 32 * k + 8 * static_cast<int>((e >> 6) & 3) + 4 * static_cast<int>((e >> 5) & 1);
     float res[4] = {0.f, 0.f, 0.f, 0.f};
     if (i < nv) {
-      float M = -INFINITY;
-      for (int s = 0; s < P; ++s) {
-        const size_t grp = static_cast<size_t>(base + s) * rw + rg;
-        M = fmaxf(M, p.wml[(grp * 32 + n) * 2]);
-      }
-      if (M != -INFINITY) {
-        float l = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < P; ++s) {
-          const size_t grp = static_cast<size_t>(base + s) * rw + rg;
-          const float2 ml = *reinterpret_cast<const float2 *>(p.wml + (grp * 32 + n) * 2);
-          const uint2 v = *reinterpret_cast<const uint2 *>(
-              reinterpret_cast<const uint16_t *>(p.wo) + (grp << lgb) * 1024 +
-              static_cast<size_t>(k) * 1024 + (e & 255) * 4);  // normalized, bf16
-          const float w = __builtin_amdgcn_exp2f(ml.x - M);  // 0 for an empty piece
-          const float wl = w * ml.y;
-          l = fmaf(w, ml.y, l);
-          o[0] = fmaf(wl, __uint_as_float(v.x << 16), o[0]);
-          o[1] = fmaf(wl, __uint_as_float(v.x & 0xffff0000u), o[1]);
-          o[2] = fmaf(wl, __uint_as_float(v.y << 16), o[2]);
-          o[3] = fmaf(wl, __uint_as_float(v.y & 0xffff0000u), o[3]);
-        }
-        const float inv = l > 0.f ? 1.f / l : 0.f;
+      // the pieces' (m, l) and O in rounds of kMergeRound, every load of a round issued
+      // before any is used (one memory round trip per round), with a running maximum;
+      // the bf16 pairs stay packed until they are used
+      const uint16_t *WO = reinterpret_cast<const uint16_t *>(p.wo) +
+                           static_cast<size_t>(k) * 1024 + (e & 255) * 4;
+      float M = -INFINITY, l = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int s0 = 0; s0 < P; s0 += kMergeRound) {
+        // (unconditional loads: the pieces past P read piece P - 1 again and are masked
+        // afterwards; loads under a per-piece branch waited one by one)
+        float2 mlv[kMergeRound];
+        uint2 pk[kMergeRound];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) res[x] = o[x] * inv;
+        for (int j = 0; j < kMergeRound; ++j) {
+          const size_t grp = static_cast<size_t>(base + imin(s0 + j, P - 1)) * rw + rg;
+          mlv[j] = *reinterpret_cast<const float2 *>(p.wml + (grp * 32 + n) * 2);
+          pk[j] = *reinterpret_cast<const uint2 *>(WO + (grp << lgb) * 1024);  // O / l, bf16
+        }
+        float mv[kMergeRound], lv[kMergeRound];
+#pragma unroll
+        for (int j = 0; j < kMergeRound; ++j) {
+          mv[j] = s0 + j < P ? mlv[j].x : -INFINITY;
+          lv[j] = s0 + j < P ? mlv[j].y : 0.f;
+        }
+        float Mn = M;
+#pragma unroll
+        for (int j = 0; j < kMergeRound; ++j) Mn = fmaxf(Mn, mv[j]);
+        // no branch on an empty maximum (the compiler would sink the l and O loads below
+        // it, a second round trip): with nothing attended so far every weight is 0
+        const float Ms = Mn == -INFINITY ? 0.f : Mn;
+        const float a = __builtin_amdgcn_exp2f(M - Ms);  // 0 while M = -inf
+        l *= a;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) o[x] *= a;
+#pragma unroll
+        for (int j = 0; j < kMergeRound; ++j) {
+          const float w = __builtin_amdgcn_exp2f(mv[j] - Ms);  // 0 for an empty piece
+          const float wl = w * lv[j];
+          l += wl;
+          o[0] = fmaf(wl, __uint_as_float(pk[j].x << 16), o[0]);
+          o[1] = fmaf(wl, __uint_as_float(pk[j].x & 0xffff0000u), o[1]);
+          o[2] = fmaf(wl, __uint_as_float(pk[j].y << 16), o[2]);
+          o[3] = fmaf(wl, __uint_as_float(pk[j].y & 0xffff0000u), o[3]);
+        }
+        M = Mn;
       }
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) res[x] = o[x] * inv;
     }
     uint32_t w0 = f32_to_bf16_rne(res[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(res[1])) << 16);
     uint32_t w1 = f32_to_bf16_rne(res[2]) | (static_cast<uint32_t>(f32_to_bf16_rne(res[3])) << 16);
@@ -256,10 +300,8 @@ __global__ void __launch_bounds__(256) k_attn_merge_plan(AttnParams p, int D) {
 }  // namespace
 
 hipError_t launch_attn_plan(const AttnParams &p, hipStream_t s) {
-  // one wave for up to 64 sequences (its barriers cost next to nothing), else as many
-  // threads as sequences, rounded up to whole waves
-  const unsigned nt = p.B <= 64 ? 64u : static_cast<unsigned>((p.B + 63) / 64 * 64);
-  hipLaunchKernelGGL(k_attn_plan, dim3(1), dim3(nt), 0, s, p, const_cast<int32_t *>(p.plan));
+  hipLaunchKernelGGL(k_attn_plan, dim3(1), dim3(kPlanThreads), 0, s, p,
+                     const_cast<int32_t *>(p.plan));
   return hipGetLastError();
 }
 
@@ -267,7 +309,7 @@ hipError_t launch_attn_merge_plan(const AttnParams &p, int D, hipStream_t s) {
   // at most plan_grid split entries; a grid-stride loop over the ones the plan made
   const size_t most = static_cast<size_t>(p.plan_grid) * p.frag_rows * D / 4;
   size_t blocks = (most + 255) / 256;
-  if (blocks > 512) blocks = 512;
+  if (blocks > 2048) blocks = 2048;
   if (blocks == 0) blocks = 1;
   hipLaunchKernelGGL(k_attn_merge_plan, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p,
                      D);

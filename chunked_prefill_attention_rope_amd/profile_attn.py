@@ -49,22 +49,24 @@ def main():
     window = 0 if mask is not None else cfg.window
     static = bool(cfg.ring) and any(n < cfg.C for n in cfg.n_valid)
     max_seen = max(1, max(cfg.seen))  # the host's bound on seen, as the bench passes it
+    # no flags given: the ones the bench passes (balanced splits for a skewed batch)
+    flags = a.flags if a.flags else path.attn_flags_for(cfg.seen)
     bufs = path.make_buffers(cache, d["q"], d["k"], d["v"], mask=mask, window=window,
-                             static_append=static, flags=a.flags)
+                             static_append=static, flags=flags)
     cp.rope_chunk(d["q"], d["cos"], d["sin"], out=bufs.q_rot)
     cp.rope_chunk(d["k"], d["cos"], d["sin"], out=bufs.k_rot)
     for _ in range(a.reps):
         if a.step:
             d["seen"].copy_(seen0)
             path.chunk_step(cache, d["q"], d["k"], d["v"], d["cos"], d["sin"], d["n_valid"],
-                            bufs, mask=mask, window=window, static_append=static, flags=a.flags,
+                            bufs, mask=mask, window=window, static_append=static, flags=flags,
                             max_seen=max_seen)
         else:
             fold = path.rope_q_in_attention(d["q"])  # the step's configuration
             cp.attn_chunk_with_past(cache, d["q"] if fold else bufs.q_rot, bufs.k_rot, d["v"],
                                     n_valid=d["n_valid"], mask=mask, window=window,
                                     scale=cfg.scale, out=bufs.out, workspace=bufs.workspace,
-                                    flags=a.flags, max_seen=max_seen,
+                                    flags=flags, max_seen=max_seen,
                                     q_rope=(d["cos"], d["sin"]) if fold else None)
     torch.cuda.synchronize()
     print(f"profile_attn: {a.workload} layer {a.layer} x{a.reps} done", flush=True)

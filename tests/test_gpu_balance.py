@@ -139,3 +139,40 @@ def test_balance_flag_ignored_where_it_does_not_apply(cp):
         got = to_f64(out)
         assert rowwise_rel_err(got, _oracle(cfg, t), real_rows_mask(cfg, got.shape)) <= \
             TOL[cfg.dtype]
+
+
+def test_balanced_path_step_c4():
+    """The Llama-8B-like layer's whole step as the benchmark runs it: the layer driver's
+    flags for its skewed batch (balanced splits), RoPE with the early append, the
+    balanced attention, and the merge advancing seen.  Every output row against the
+    oracle, the selection is the last row, the cache ends byte-identical to the oracle's
+    append on its live slots."""
+    from chunked_prefill_attention_rope_amd import cp, path
+    cfg = I.config("c4")
+    flags = path.attn_flags_for(cfg.seen)
+    assert flags == cp.ATTN_BALANCE
+    t = I.make_layer(cfg)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cache = cp.KVCache(dev(t["kc"]), dev(t["vc"]), dev(t["seen"]), status=status)
+    d = {n: dev(t[n]) for n in ("q", "k", "v", "cos", "sin", "n_valid")}
+    bufs = path.make_buffers(cache, d["q"], d["k"], d["v"], flags=flags)
+    out, sel = path.chunk_step(cache, d["q"], d["k"], d["v"], d["cos"], d["sin"], d["n_valid"],
+                               bufs, flags=flags, max_seen=max(cfg.seen))
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    v = I.np_view
+    qr = O.rope(v(t["q"]), v(t["cos"]), v(t["sin"]))
+    kr = O.rope(v(t["k"]), v(t["cos"]), v(t["sin"]))
+    ref = O.attn(qr, kr, v(t["v"]), v(t["kc"]), v(t["vc"]), v(t["seen"]), v(t["n_valid"]), None,
+                 cfg.ring, cfg.sink, cfg.window, cfg.scale)
+    got = to_f64(out)
+    assert rowwise_rel_err(got, ref, real_rows_mask(cfg, got.shape)) <= TOL[I.BF16]
+    np.testing.assert_array_equal(bits(sel), bits(out[:, :, cfg.C - 1]))
+    ko, vo, so, live = O.kv_append(v(t["kc"]), v(t["vc"]), v(t["seen"]), kr, v(t["v"]),
+                                   v(t["n_valid"]), cfg.ring, cfg.sink)
+    assert cache.seen.cpu().tolist() == so.tolist()
+    kg, vg = bits(cache.k), bits(cache.v)
+    for b in range(cfg.B):
+        sl = np.nonzero(live[b])[0]
+        np.testing.assert_array_equal(kg[b][:, sl], ko.view(np.uint8).reshape(kg.shape)[b][:, sl])
+        np.testing.assert_array_equal(vg[b][:, sl], vo.view(np.uint8).reshape(vg.shape)[b][:, sl])

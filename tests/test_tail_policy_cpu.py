@@ -44,3 +44,17 @@ def test_choose_chunk_minimises_total_time(path):
     assert path.choose_chunk(64, {32: 10.0, 64: 20.0}) == 32
     with pytest.raises(ValueError):
         path.choose_chunk(0, table)
+
+
+def test_balance_policy():
+    """Balanced key splits for a batch whose longest past exceeds 1.5x the mean (the
+    Llama-8B-like batch), not for equal pasts, one sequence or an empty batch."""
+    from chunked_prefill_attention_rope_amd import cp, inputs as I, path
+    assert path.attn_flags_for(I.config("c4").seen) == cp.ATTN_BALANCE
+    assert path.attn_flags_for(I.config("c5", 5).seen) == 0
+    assert path.attn_flags_for([800]) == 0
+    assert path.attn_flags_for([]) == 0
+    assert path.attn_flags_for([0, 0, 0]) == 0
+    assert path.attn_flags_for([100, 100, 100, 140]) == 0     # longest 1.27x the mean
+    assert path.attn_flags_for([100, 100, 100, 400]) == cp.ATTN_BALANCE  # 2.29x
+    assert path.attn_flags_for([10, 10, 10, 1000]) == cp.ATTN_BALANCE

@@ -1,6 +1,10 @@
 """Run one workload's attention call (or whole layer step) N times, for profilers.
 
     python -m chunked_prefill_attention_rope_amd.profile_attn --workload c5 --layer 5 --reps 5
+    python -m chunked_prefill_attention_rope_amd.profile_attn --workload c5g --C 16 --reps 5
+
+A workload of the bandwidth sweep (c2 at batch --B, c4 or c5g at chunk --C, --explicit
+for c2's mask) is built as the sweep builds it.
 
 Eager launches on torch's current stream, inputs resident in HBM, nothing
 else timed or checked: meant to sit under `rocprofv3 --kernel-trace` or
@@ -26,6 +30,9 @@ def main():
     ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--step", action="store_true", help="whole layer step, not attention only")
     ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--B", type=int, default=None, help="sweep shape: batch (c2)")
+    ap.add_argument("--C", type=int, default=None, help="sweep shape: chunk rows (c4, c5g)")
+    ap.add_argument("--explicit", type=int, default=None, help="sweep shape: c2's mask (1/0)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead: copy a buffer of this many bytes (counter calibration)")
     a = ap.parse_args()
@@ -38,7 +45,11 @@ def main():
         torch.cuda.synchronize()
         print(f"profile_attn: copy of {a.copy_bytes} bytes x{a.reps} done", flush=True)
         return
-    cfg = I.config(a.workload, a.layer)
+    if a.B is not None or a.C is not None or a.explicit is not None or a.workload == "c5g":
+        cfg = I.derived(a.workload, B=a.B, C=a.C,
+                        explicit_mask=None if a.explicit is None else bool(a.explicit))
+    else:
+        cfg = I.config(a.workload, a.layer)
     t = I.make_layer(cfg, nan_dead=False)
     d = {k: v.to("cuda") for k, v in t.items()}
     seen0 = d["seen"].clone()

@@ -176,3 +176,32 @@ def test_balanced_path_step_c4():
         sl = np.nonzero(live[b])[0]
         np.testing.assert_array_equal(kg[b][:, sl], ko.view(np.uint8).reshape(kg.shape)[b][:, sl])
         np.testing.assert_array_equal(vg[b][:, sl], vo.view(np.uint8).reshape(vg.shape)[b][:, sl])
+
+
+def test_balanced_many_sequences(cp):
+    """More sequences than the plan kernel has threads (300 over 256): its per-sequence
+    loops and prefix sums take several elements per thread.  Pasts from 0 to 2990, every
+    output row against the oracle; then at the plan's limit (1024 sequences) the call is
+    still balanced, and above it (1025) the flag is ignored."""
+    seen = [(i * 37) % 2991 for i in range(300)]
+    nvs = [64 if i % 7 else 9 for i in range(300)]
+    cfg = I.small(dtype=I.BF16, B=300, H=4, nKV=1, D=128, C=64, cap=3000, seen=seen,
+                  n_valid=nvs, seed=21)
+    t = I.make_layer(cfg)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cache = cp.KVCache(dev(t["kc"]), dev(t["vc"]), dev(t["seen"]), status=status)
+    out, nb = _call(cp, cfg, t, cache, cp.ATTN_BALANCE)
+    torch.cuda.synchronize()
+    assert nb > 0
+    got = to_f64(out)
+    m = real_rows_mask(cfg, got.shape)
+    assert rowwise_rel_err(got, _oracle(cfg, t), m) <= TOL[I.BF16]
+    assert (got[~m] == 0).all()
+    assert int(status.item()) == 0
+    for B, planned in ((1024, True), (1025, False)):
+        big = I.small(dtype=I.BF16, B=B, H=4, nKV=1, D=128, C=64, cap=64, seen=[0] * B,
+                      n_valid=[64] * B, seed=22)
+        tb = I.make_layer(big, nan_dead=False)
+        cb = cp.KVCache(dev(tb["kc"]), dev(tb["vc"]), dev(tb["seen"]))
+        q, k, v = dev(tb["q"]), dev(tb["k"]), dev(tb["v"])
+        assert (cp.attn_workspace_bytes(cb, q, k, v, flags=cp.ATTN_BALANCE) > 0) == planned

@@ -109,3 +109,29 @@ def test_noalloc_unsplit_and_refusal(cp):
     assert e.value.code == cp.ERR_SCRATCH
     torch.cuda.synchronize()
     assert (ob.float() == 7.0).all()
+
+
+def test_noalloc_balanced(cp):
+    """Balanced key splits (CP_ATTN_BALANCE) through the array: the plan and the pieces'
+    partials of the Llama-8B-like batch, then of a smaller skewed batch (the array keeps
+    the first plan), each bit-identical to the workspace call and within tolerance of
+    the oracle."""
+    small = I.small(dtype=I.BF16, B=5, H=8, nKV=2, D=128, C=96, cap=3200,
+                    seen=[3000, 5, 700, 2500, 64], n_valid=[96, 96, 40, 77, 1], seed=14)
+    for cfg in (I.config("c4"), small):
+        t, cache, status, q, k, v, nv, mask, window = _case(cp, cfg, False)
+        flags = cp.ATTN_BALANCE
+        need = cp.attn_workspace_bytes(cache, q, k, v, flags=flags)
+        assert 0 < need <= cp.ATTN_SCRATCH_BYTES
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        ref = cp.attn_chunk_with_past(cache, q, k, v, n_valid=nv, scale=cfg.scale, workspace=ws,
+                                      flags=flags)
+        out = torch.full_like(q, 3.0)
+        cp.attn_chunk_with_past_noalloc(cache, q, k, v, out, n_valid=nv, scale=cfg.scale,
+                                        flags=flags)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(out), bits(ref))
+        got = to_f64(out)
+        err = rowwise_rel_err(got, _oracle(cfg, t), real_rows_mask(cfg, got.shape))
+        assert err <= TOL[cfg.dtype], (cfg.name, err)
+        assert int(status.item()) == 0

@@ -36,6 +36,7 @@
 // product's register r is therefore a valid B operand for the k-step whose four
 // contraction indices are {4g + r}, which chains products without a trip through LDS.
 #include <algorithm>
+#include <type_traits>
 
 #include "cp_common.h"
 
@@ -67,16 +68,30 @@ __device__ __forceinline__ bool head_slot(int per, int BH, int &G, int &k) {
 __device__ __forceinline__ f4 ld4(const float *p) { return *reinterpret_cast<const f4 *>(p); }
 __device__ __forceinline__ void st4(float *p, f4 v) { *reinterpret_cast<f4 *>(p) = v; }
 
+// Block orders of the chunk products.  A matrix with ncb column blocks of 16 is stored
+// as 16 x 16 blocks, block (rb, cb) the 256 consecutive floats at (rb * ncb + cb) * 256,
+// in which lane l = 16 g + m of a wave owns the four floats at 4 l:
+//  - operand order: row m, columns 4 g .. 4 g + 3 of the block (an A operand's four
+//    k-steps);
+//  - accumulator order: rows 4 g .. 4 g + 3, column m (a 16x16x4 product's registers).
+// A wave moves a block with one 16-byte access per lane, 1 KB of consecutive memory.
+// Row-major, a wave's 16 lanes of one column group would touch 16 different rows, and
+// an accumulator would leave in four 4-byte stores.  A product computed transposed
+// (operands swapped) leaves its accumulator in operand order.
+__device__ __forceinline__ size_t blk(int rb, int cb, int ncb, int lane) {
+  return ((static_cast<size_t>(rb) * ncb + cb) * 64 + lane) * 4;
+}
+
 // Workspace of one (sequence, head, chunk), in floats.
 template <int DK, int DV>
 struct Chunk {
-  static constexpr size_t W = 0;               // [CH][DK]  T diag(beta e^lg) K
-  static constexpr size_t U = W + CH * DK;     // [CH][DV]  T diag(beta) V
-  static constexpr size_t P = U + CH * DV;     // [CH][CH]  tril(R) * Q K^T (lower blocks)
+  static constexpr size_t W = 0;               // [CH][DK]  T diag(beta e^lg) K, operand order
+  static constexpr size_t U = W + CH * DK;     // [CH][DV]  T diag(beta) V, accumulator order
+  static constexpr size_t P = U + CH * DV;     // [CH][CH]  tril(R) * Q K^T (lower blocks), operand order
   static constexpr size_t LG = P + CH * CH;    // [CH]      cumulated log-gates
-  static constexpr size_t KT = LG + CH;        // [DK][CH]  K^T
-  static constexpr size_t SC = KT + DK * CH;   // [DK][DV]  entry state
-  static constexpr size_t DC = SC + DK * DV;   // [CH][DV]  D
+  static constexpr size_t KT = LG + CH;        // [DK][CH]  K^T, operand order
+  static constexpr size_t SC = KT + DK * CH;   // [DK][DV]  entry state, accumulator order
+  static constexpr size_t DC = SC + DK * DV;   // [CH][DV]  D, accumulator order
   static constexpr size_t SIZE = DC + CH * DV;
 };
 
@@ -162,7 +177,8 @@ __global__ void __launch_bounds__(PREP_THREADS) k_gdn_prep(const float *__restri
   __syncthreads();
 
   // Gram tiles on and below the diagonal: the 10 tiles of K K^T (-> A, role 0) or of
-  // Q K^T (-> P, role 1), dealt over the waves.  Contraction index of k-step (kk, j):
+  // Q K^T (-> P, role 1), dealt over the waves, computed transposed so that lane (m, g)
+  // holds row tt 16 + m, columns st 16 + 4 g .. + 3.  Contraction index of k-step (kk, j):
   // g * DK/4 + 4 kk + j.
   for (int p = w + 10 * role; p < 10 + 10 * role; p += PREP_THREADS / 64) {
     const int tl = p % 10;
@@ -179,26 +195,33 @@ __global__ void __launch_bounds__(PREP_THREADS) k_gdn_prep(const float *__restri
       const f4 b1 = ld4(&Ks[(st * 16 + m) * KP + i0 + 4]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        acc0 = mma(a0[j], b0[j], acc0);
-        acc1 = mma(a1[j], b1[j], acc1);
+        acc0 = mma(b0[j], a0[j], acc0);
+        acc1 = mma(b1[j], a1[j], acc1);
       }
     }
-    const int s = st * 16 + m;
+    const int t = tt * 16 + m;
+    const float lgt = lg[t], bq = bt[t];
+    f4 o;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = tt * 16 + 4 * g + r;
+      const int s = st * 16 + 4 * g + r;
       const float gram = acc0[r] + acc1[r];
-      const float rr = s <= t ? __expf(lg[t] - lg[s]) : 0.f;
-      if (p < 10)
-        As[t * AP + s] = s < t ? bt[t] * rr * gram : 0.f;
-      else
-        ck[L::P + t * CH + s] = rr * gram;
+      const float rr = s <= t ? __expf(lgt - lg[s]) : 0.f;
+      o[r] = p < 10 ? (s < t ? bq * rr * gram : 0.f) : rr * gram;
     }
+    if (p < 10)
+      st4(&As[t * AP + st * 16 + 4 * g], o);
+    else
+      st4(&ck[L::P + blk(tt, st, CH / 16, lane)], o);
   }
   if (role == 1) {
-    for (int e = tid; e < DK * CH; e += PREP_THREADS) {  // K^T for the scan's state update
-      const int i = e / CH, t = e % CH;
-      ck[L::KT + e] = Ks[t * KP + i];
+    // K^T for the scan's state update, one lane's four operand floats per thread
+    for (int e = tid; e < DK * CH / 4; e += PREP_THREADS) {
+      const int b = e / 64, l = e % 64;
+      const int i = (b / (CH / 16)) * 16 + l % 16, t = (b % (CH / 16)) * 16 + 4 * (l / 16);
+      const f4 x = {Ks[t * KP + i], Ks[(t + 1) * KP + i], Ks[(t + 2) * KP + i],
+                    Ks[(t + 3) * KP + i]};
+      st4(&ck[L::KT + 4 * static_cast<size_t>(e)], x);
     }
     return;  // (the whole workgroup: role 1 passes no further barrier)
   }
@@ -244,12 +267,13 @@ __global__ void __launch_bounds__(PREP_THREADS) k_gdn_prep(const float *__restri
   __syncthreads();
 
   // [U | W] = T [diag(beta) V | diag(beta e^lg) K]: column tiles dealt over the waves.
-  constexpr int NCT = (DV + DK) / 16;
-  for (int ct = w; ct < NCT; ct += PREP_THREADS / 64) {
-    const bool isv = ct < DV / 16;
-    const float *Y = isv ? Vs + ct * 16 : Ks + (ct - DV / 16) * 16;
-    const int yp = isv ? VP : KP;
-    const float *f = isv ? bt : fk;
+  // U leaves in accumulator order (the scan's D rows take it so); W is computed
+  // transposed and leaves in operand order (the scan's A operand).
+  auto tile = [&](auto transposed, int ct) {
+    constexpr bool TR = decltype(transposed)::value;
+    const float *Y = TR ? Ks + ct * 16 : Vs + ct * 16;
+    const int yp = TR ? KP : VP;
+    const float *f = TR ? fk : bt;
     f4 acc[4] = {zero, zero, zero, zero};
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
@@ -263,16 +287,16 @@ __global__ void __launch_bounds__(PREP_THREADS) k_gdn_prep(const float *__restri
       for (int tt = sb; tt < 4; ++tt) {
         const f4 a = ld4(&Ts[(tt * 16 + m) * AP + sb * 16 + 4 * g]);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc[tt] = mma(a[kk], bv[kk], acc[tt]);
+        for (int kk = 0; kk < 4; ++kk)
+          acc[tt] = TR ? mma(bv[kk], a[kk], acc[tt]) : mma(a[kk], bv[kk], acc[tt]);
       }
     }
-    float *dst = isv ? ck + L::U + ct * 16 : ck + L::W + (ct - DV / 16) * 16;
-    const int ld = isv ? DV : DK;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dst[(tt * 16 + 4 * g + r) * ld + m] = acc[tt][r];
-  }
+      st4(&ck[TR ? L::W + blk(tt, ct, DK / 16, lane) : L::U + blk(tt, ct, DV / 16, lane)], acc[tt]);
+  };
+  for (int ct = w; ct < DV / 16; ct += PREP_THREADS / 64) tile(std::false_type{}, ct);
+  for (int ct = w; ct < DK / 16; ct += PREP_THREADS / 64) tile(std::true_type{}, ct);
 }
 
 template <int DK, int DV>
@@ -307,19 +331,18 @@ __global__ void __launch_bounds__(256) k_gdn_scan(float *__restrict__ ws,
   // burst those loads fill the vector-memory queue and stall the wave's MFMAs behind
   // them, so they are spread over the D products below (four loads per eight MFMAs).
   struct Ops {
-    f4 w[NIB], kt[OWN * 4], lg;
-    float u[4], lglast;
+    f4 w[NIB], kt[OWN * 4], lg, u;
+    float lglast;
   };
   auto fetch_pair = [&](const float *ck, int ib, Ops &x) {  // four of the 2 NIB large loads
-    x.w[ib] = ld4(&ck[L::W + (w * 16 + m) * DK + ib * 16 + 4 * g]);
-    x.w[ib + 1] = ld4(&ck[L::W + (w * 16 + m) * DK + ib * 16 + 16 + 4 * g]);
+    x.w[ib] = ld4(&ck[L::W + blk(w, ib, NIB, lane)]);
+    x.w[ib + 1] = ld4(&ck[L::W + blk(w, ib + 1, NIB, lane)]);
 #pragma unroll
     for (int u = ib; u < ib + 2; ++u)
-      x.kt[u] = ld4(&ck[L::KT + ((w * OWN + u / 4) * 16 + m) * CH + (u % 4) * 16 + 4 * g]);
+      x.kt[u] = ld4(&ck[L::KT + blk(w * OWN + u / 4, u % 4, CH / 16, lane)]);
   };
   auto fetch_small = [&](const float *ck, Ops &x) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) x.u[r] = ck[L::U + (w * 16 + 4 * g + r) * DV + j0 + m];
+    x.u = ld4(&ck[L::U + blk(w, jb, DV / 16, lane)]);
     x.lg = ld4(&ck[L::LG + w * 16 + 4 * g]);
     x.lglast = ck[L::LG + CH - 1];
   };
@@ -337,11 +360,7 @@ __global__ void __launch_bounds__(256) k_gdn_scan(float *__restrict__ ws,
     const float *cn = ws + (bh * nch + min(c + 1, nch - 1)) * L::SIZE;
     // entry state of the chunk, for the output kernel
 #pragma unroll
-    for (int o = 0; o < OWN; ++o) {
-      const int ib = w * OWN + o;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ck[L::SC + (ib * 16 + 4 * g + r) * DV + j0 + m] = sacc[o][r];
-    }
+    for (int o = 0; o < OWN; ++o) st4(&ck[L::SC + blk(w * OWN + o, jb, DV / 16, lane)], sacc[o]);
     // rows 16w..16w+15 of D = U - W S (contraction over the state's rows)
     f4 d0 = zero, d1 = zero;
 #pragma unroll
@@ -357,14 +376,11 @@ __global__ void __launch_bounds__(256) k_gdn_scan(float *__restrict__ ws,
       __builtin_amdgcn_sched_barrier(0);  // keep the next loads behind these MFMAs
     }
     fetch_small(cn, nx);
+    const f4 dd = cu.u - (d0 + d1);
+    st4(&ck[L::DC + blk(w, jb, DV / 16, lane)], dd);
     f4 dw;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = w * 16 + 4 * g + r;
-      const float dd = cu.u[r] - (d0[r] + d1[r]);
-      ck[L::DC + t * DV + j0 + m] = dd;
-      dw[r] = __expf(cu.lglast - cu.lg[r]) * dd;
-    }
+    for (int r = 0; r < 4; ++r) dw[r] = __expf(cu.lglast - cu.lg[r]) * dd[r];
     st4(&Dt[m * AP + w * 16 + 4 * g], dw);
     __syncthreads();  // Dt complete; every wave is done reading St
     // S = e^{lg_last} S + K^T diag(R[last, :]) D for this wave's row blocks
@@ -426,31 +442,33 @@ __global__ void __launch_bounds__(256) k_gdn_out(const float *__restrict__ q,
   for (int ib = 0; ib < DK / 16; ++ib) qa[ib] = qin ? ld4(qr + ib * 16 + 4 * g) : zero;
 #pragma unroll
   for (int sb = 0; sb < 4; ++sb)
-    pa[sb] = sb <= w ? ld4(&ck[L::P + (w * 16 + m) * CH + sb * 16 + 4 * g]) : zero;
+    pa[sb] = sb <= w ? ld4(&ck[L::P + blk(w, sb, CH / 16, lane)]) : zero;
   const f4 lgr = ld4(&ck[L::LG + w * 16 + 4 * g]);
-  {  // the shared B operands
-    constexpr int Q4 = OC / 4;  // float4s per staged row
-    constexpr int NS = DK * Q4 / 256, ND = CH * Q4 / 256;
+  {  // the shared B operands, stored in accumulator order: wave w moves blocks w, w + 4, ...
+    constexpr int NB = OC / 16;  // column blocks of the staged columns
+    constexpr int NS = DK / 16 * NB / 4, ND = CH / 16 * NB / 4;
     f4 sr[NS], dr[ND];
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
-      const int e = tid + 256 * u;
-      sr[u] = ld4(&ck[L::SC + (e / Q4) * DV + j0 + (e % Q4) * 4]);
+      const int b = w + 4 * u;
+      sr[u] = ld4(&ck[L::SC + blk(b / NB, j0 / 16 + b % NB, DV / 16, lane)]);
     }
 #pragma unroll
     for (int u = 0; u < ND; ++u) {
-      const int e = tid + 256 * u;
-      dr[u] = ld4(&ck[L::DC + (e / Q4) * DV + j0 + (e % Q4) * 4]);
+      const int b = w + 4 * u;
+      dr[u] = ld4(&ck[L::DC + blk(b / NB, j0 / 16 + b % NB, DV / 16, lane)]);
     }
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
-      const int e = tid + 256 * u;
-      st4(&Ss[(e / Q4) * OP + (e % Q4) * 4], sr[u]);
+      const int b = w + 4 * u;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Ss[((b / NB) * 16 + 4 * g + r) * OP + (b % NB) * 16 + m] = sr[u][r];
     }
 #pragma unroll
     for (int u = 0; u < ND; ++u) {
-      const int e = tid + 256 * u;
-      st4(&Ds[(e / Q4) * OP + (e % Q4) * 4], dr[u]);
+      const int b = w + 4 * u;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Ds[((b / NB) * 16 + 4 * g + r) * OP + (b % NB) * 16 + m] = dr[u][r];
     }
   }
   __syncthreads();

@@ -15,19 +15,18 @@
 // A, T, U and W never see the state, and O of a chunk needs only the chunk's entry
 // state and D: only D and the state update form the serial chain across chunks.
 //
-// Three kernels, all on v_mfma_f32_16x16x4f32 (fp32 products, fp32 sums):
+// Two kernels, both on v_mfma_f32_16x16x4f32 (fp32 products, fp32 sums):
 //  - k_gdn_prep, two workgroups per (chunk, head, sequence): one forms the Gram
 //    product K K^T, T by inverting the four 16x16 diagonal blocks of I + A
 //    (one lane per column) and filling the blocks below them in three rounds
 //    (T_ij = -T_ii sum_k A_ik T_kj); then [U | W] = T [diag(beta) V | diag(beta e^lg) K],
 //    and writes W, U and lg; the other forms P = tril(R) * Q K^T and writes it with K^T.
 //  - k_gdn_scan, one workgroup per (16 state columns, head, sequence): the state's
-//    columns evolve independently.  Walks the chunks: each wave computes 16 rows of
-//    D = U - W S, then updates its own row blocks of S (kept in MFMA accumulators,
-//    mirrored to LDS transposed for the next chunk's D).  Stores each chunk's entry
-//    state and D for the output kernel.
-//  - k_gdn_out, one workgroup per (32 output columns of a chunk, head, sequence):
-//    O = diag(e^lg) Q S_c + P D_c.
+//    columns evolve independently.  Four waves walk the chunks: each computes 16 rows
+//    of D = U - W S, then updates its own row blocks of S (kept in MFMA accumulators,
+//    mirrored to LDS transposed for the next chunk's D).  Four more waves form the
+//    chunk's output O = diag(e^lg) Q S_c + P D_c for the same 16 columns from the entry
+//    state and D in LDS, so neither goes back to memory.
 // Pad rows of a last partial chunk are zero with beta = 0 and a zero log-gate: their
 // rows of A, U, W and D are zero, they leave the state untouched and are not stored.
 //
@@ -46,7 +45,6 @@ namespace {
 constexpr int CH = 64;      // tokens per chunk
 constexpr int VB = 16;      // state columns per scan workgroup
 constexpr int AP = CH + 4;  // LDS row stride of the 64 x 64 tiles
-constexpr int OC = 32;      // output columns per output workgroup
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
@@ -90,14 +88,11 @@ struct Chunk {
   static constexpr size_t P = U + CH * DV;     // [CH][CH]  tril(R) * Q K^T (lower blocks), operand order
   static constexpr size_t LG = P + CH * CH;    // [CH]      cumulated log-gates
   static constexpr size_t KT = LG + CH;        // [DK][CH]  K^T, operand order
-  static constexpr size_t SC = KT + DK * CH;   // [DK][DV]  entry state, accumulator order
-  static constexpr size_t DC = SC + DK * DV;   // [CH][DV]  D, accumulator order
-  static constexpr size_t SIZE = DC + CH * DV;
+  static constexpr size_t SIZE = KT + DK * CH;
 };
 
 __host__ __device__ constexpr size_t gdn_chunk_floats(int dk, int dv) {
-  return 2 * static_cast<size_t>(CH) * dk + 2 * static_cast<size_t>(CH) * dv + CH * CH + CH +
-         static_cast<size_t>(dk) * dv;
+  return 2 * static_cast<size_t>(CH) * dk + static_cast<size_t>(CH) * dv + CH * CH + CH;
 }
 static_assert(Chunk<128, 64>::SIZE == gdn_chunk_floats(128, 64), "workspace layout");
 
@@ -299,47 +294,55 @@ __global__ void __launch_bounds__(PREP_THREADS) k_gdn_prep(const float *__restri
   for (int ct = w; ct < DK / 16; ct += PREP_THREADS / 64) tile(std::true_type{}, ct);
 }
 
+constexpr int SCAN_THREADS = 512;  // four waves walk the state, four form the output
+
 template <int DK, int DV>
-__global__ void __launch_bounds__(256) k_gdn_scan(float *__restrict__ ws,
-                                                  float *__restrict__ state, int BH, int nch) {
+__global__ void __launch_bounds__(SCAN_THREADS) k_gdn_scan(const float *__restrict__ q,
+                                                           float *__restrict__ ws,
+                                                           float *__restrict__ state,
+                                                           float *__restrict__ out, int BH, int P,
+                                                           int nch) {
   using L = Chunk<DK, DV>;
   constexpr int NIB = DK / 16;  // row blocks of the state
-  constexpr int OWN = NIB / 4;  // row blocks each wave updates
+  constexpr int OWN = NIB / 4;  // row blocks each state wave updates
   constexpr int SP = DK + 4;
-  __shared__ __align__(16) float St[VB * SP];  // S^T of this column block: St[j][i]
-  __shared__ __align__(16) float Dt[VB * AP];  // (diag(R[last, :]) D)^T: Dt[j][t]
+  constexpr int QP = DK + 4;    // LDS row stride of an output wave's staged rows of Q
+  __shared__ __align__(16) float St[VB * SP];     // S^T of this column block: St[j][i]
+  __shared__ __align__(16) float Dt[VB * AP];     // (diag(R[last, :]) D)^T: Dt[j][t]
+  __shared__ __align__(16) float Dc[CH * VB];     // D, row blocks in accumulator order
+  __shared__ __align__(16) float Qs[4 * 16 * QP];  // output wave ow's 16 rows of Q
   int G, jb;
   if (!head_slot(DV / VB, BH, G, jb)) return;  // whole workgroup, before any barrier
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, m = lane & 15, g = lane >> 4;
+  const bool walker = w < 4;  // waves 0..3 walk the state, 4..7 form the output
   const size_t bh = G;
   const int j0 = jb * VB;
   float *S = state + bh * DK * DV;
   const f4 zero = {0.f, 0.f, 0.f, 0.f};
 
-  f4 sacc[OWN];
-#pragma unroll
-  for (int o = 0; o < OWN; ++o) {
-    const int ib = w * OWN + o;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sacc[o][r] = S[(ib * 16 + 4 * g + r) * DV + j0 + m];
-    st4(&St[m * SP + ib * 16 + 4 * g], sacc[o]);
-  }
-  __syncthreads();
+  // The state walk (waves 0..3) is the serial chain; the output waves fill the matrix
+  // cores' idle cycles, so the walkers take issue priority on their SIMDs.
+  if (walker) __builtin_amdgcn_s_setprio(1);
 
-  // A operands of a chunk (rows of W, K^T), U and the log-gates, loaded one chunk ahead.
-  // Each workgroup pulls 64 KB of W and K^T per chunk through its CU: issued in one
-  // burst those loads fill the vector-memory queue and stall the wave's MFMAs behind
-  // them, so they are spread over the D products below (four loads per eight MFMAs).
-  struct Ops {
-    f4 w[NIB], kt[OWN * 4], lg, u;
-    float lglast;
-  };
-  auto fetch_pair = [&](const float *ck, int ib, Ops &x) {  // four of the 2 NIB large loads
-    x.w[ib] = ld4(&ck[L::W + blk(w, ib, NIB, lane)]);
-    x.w[ib + 1] = ld4(&ck[L::W + blk(w, ib + 1, NIB, lane)]);
+  f4 sacc[OWN];
+  if (walker) {
 #pragma unroll
-    for (int u = ib; u < ib + 2; ++u)
-      x.kt[u] = ld4(&ck[L::KT + blk(w * OWN + u / 4, u % 4, CH / 16, lane)]);
+    for (int o = 0; o < OWN; ++o) {
+      const int ib = w * OWN + o;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sacc[o][r] = S[(ib * 16 + 4 * g + r) * DV + j0 + m];
+      st4(&St[m * SP + ib * 16 + 4 * g], sacc[o]);
+    }
+  }
+
+  // Walker operands: rows of W, U and the log-gates of a chunk, loaded one chunk ahead;
+  // the K^T rows of the state update during the same chunk's D products.  Each
+  // workgroup pulls 64 KB of W and K^T per chunk through its CU: issued in one burst
+  // those loads fill the vector-memory queue and stall the wave's MFMAs behind them,
+  // so they are spread over the D products below (four loads per eight MFMAs).
+  struct Ops {
+    f4 w[NIB], lg, u;
+    float lglast;
   };
   auto fetch_small = [&](const float *ck, Ops &x) {
     x.u = ld4(&ck[L::U + blk(w, jb, DV / 16, lane)]);
@@ -349,168 +352,151 @@ __global__ void __launch_bounds__(256) k_gdn_scan(float *__restrict__ ws,
   auto fetch = [&](int c, Ops &x) {
     const float *ck = ws + (bh * nch + c) * L::SIZE;
 #pragma unroll
-    for (int ib = 0; ib < NIB; ib += 2) fetch_pair(ck, ib, x);
+    for (int ib = 0; ib < NIB; ++ib) x.w[ib] = ld4(&ck[L::W + blk(w, ib, NIB, lane)]);
     fetch_small(ck, x);
   };
-  // One chunk: consumes the operands in cu, loads chunk c + 1's into nx.  Two operand
-  // sets alternate roles (the loop below is unrolled by two), so the prefetched
-  // registers are never copied -- a copy would wait for the loads it is meant to hide.
-  auto step = [&](int c, const Ops &cu, Ops &nx) {
-    float *ck = ws + (bh * nch + c) * L::SIZE;
-    const float *cn = ws + (bh * nch + min(c + 1, nch - 1)) * L::SIZE;
-    // entry state of the chunk, for the output kernel
+
+  // Output waves: O = diag(e^lg) Q S_c + P D_c for rows 16 ow .. 16 ow + 15 of chunk c and
+  // this workgroup's 16 columns.  Q S_c runs while the walkers form D_c (S_c is in St
+  // until the state update); P D_c while they update the state (D_c in Dc).  Chunk
+  // c + 1's rows of Q (loaded row-major into registers, then through the wave's LDS
+  // stage into operand order), its P blocks and log-gates are loaded one chunk ahead.
+  const int ow = w - 4;
+  constexpr int NQ = 16 * DK / 4 / 64;  // float4s per lane of 16 rows of Q
+  f4 qreg[NQ], pa[4], lgo = zero, oacc = zero;
+  auto out_fetch = [&](int c) {
+    const int t0 = c * CH;
+    const float *ck = ws + (bh * nch + c) * L::SIZE;
 #pragma unroll
-    for (int o = 0; o < OWN; ++o) st4(&ck[L::SC + blk(w * OWN + o, jb, DV / 16, lane)], sacc[o]);
-    // rows 16w..16w+15 of D = U - W S (contraction over the state's rows)
-    f4 d0 = zero, d1 = zero;
+    for (int u = 0; u < NQ; ++u) {
+      const int e = lane + 64 * u, row = e / (DK / 4), t = t0 + 16 * ow + row;
+      qreg[u] = t < P ? ld4(q + (bh * P + t) * DK + (e % (DK / 4)) * 4) : zero;
+    }
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) pa[sb] = sb <= ow ? ld4(&ck[L::P + blk(ow, sb, CH / 16, lane)]) : zero;
+    lgo = ld4(&ck[L::LG + 16 * ow + 4 * g]);
+  };
+  float *qs = Qs + ow * 16 * QP;
+  auto out_qs = [&](int c) {  // Q S_c, scaled by e^lg
+    (void)c;
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int e = lane + 64 * u;
+      st4(&qs[(e / (DK / 4)) * QP + (e % (DK / 4)) * 4], qreg[u]);
+    }
+    f4 qa[NIB], sv[NIB];
+#pragma unroll
+    for (int ib = 0; ib < NIB; ++ib) {
+      qa[ib] = ld4(&qs[m * QP + ib * 16 + 4 * g]);
+      sv[ib] = ld4(&St[m * SP + ib * 16 + 4 * g]);
+    }
+    f4 o0 = zero, o1 = zero;
 #pragma unroll
     for (int ib = 0; ib < NIB; ib += 2) {
-      const f4 b0 = ld4(&St[m * SP + ib * 16 + 4 * g]);
-      const f4 b1 = ld4(&St[m * SP + ib * 16 + 16 + 4 * g]);
-      fetch_pair(cn, ib, nx);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        d0 = mma(cu.w[ib][kk], b0[kk], d0);
-        d1 = mma(cu.w[ib + 1][kk], b1[kk], d1);
+        o0 = mma(qa[ib][kk], sv[ib][kk], o0);
+        o1 = mma(qa[ib + 1][kk], sv[ib + 1][kk], o1);
       }
-      __builtin_amdgcn_sched_barrier(0);  // keep the next loads behind these MFMAs
     }
-    fetch_small(cn, nx);
-    const f4 dd = cu.u - (d0 + d1);
-    st4(&ck[L::DC + blk(w, jb, DV / 16, lane)], dd);
-    f4 dw;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dw[r] = __expf(cu.lglast - cu.lg[r]) * dd[r];
-    st4(&Dt[m * AP + w * 16 + 4 * g], dw);
-    __syncthreads();  // Dt complete; every wave is done reading St
-    // S = e^{lg_last} S + K^T diag(R[last, :]) D for this wave's row blocks
-    const float glast = __expf(cu.lglast);
+    for (int r = 0; r < 4; ++r) oacc[r] = (o0[r] + o1[r]) * __expf(lgo[r]);
+  };
+  auto out_pd = [&](int c) {  // + P D_c over the chunk's rows up to the wave's, then store
+    const int t0 = c * CH;
 #pragma unroll
-    for (int o = 0; o < OWN; ++o) {
-      const int ib = w * OWN + o;
-      f4 acc = sacc[o] * glast;
+    for (int sb = 0; sb < 4; ++sb) {
+      if (sb > ow) break;
+      const f4 db = ld4(&Dc[sb * 256 + 4 * lane]);
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const f4 a = cu.kt[o * 4 + tb];
-        const f4 bb = ld4(&Dt[m * AP + tb * 16 + 4 * g]);
+      for (int kk = 0; kk < 4; ++kk) oacc = mma(pa[sb][kk], db[kk], oacc);
+    }
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc = mma(a[kk], bb[kk], acc);
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + 16 * ow + 4 * g + r;
+      if (t < P) out[(bh * P + t) * DV + j0 + m] = oacc[r];
+    }
+  };
+
+  // One chunk: the walkers consume the operands in cu and load chunk c + 1's into nx.
+  // Two operand sets alternate roles (the loop below is unrolled by two), so the
+  // prefetched registers are never copied -- a copy would wait for the loads it is
+  // meant to hide.
+  auto step = [&](int c, const Ops &cu, Ops &nx) {
+    const float *ck = ws + (bh * nch + c) * L::SIZE;
+    const float *cn = ws + (bh * nch + min(c + 1, nch - 1)) * L::SIZE;
+    float glast = 0.f;
+    f4 kt[OWN * 4];  // this chunk's K^T operands, for the state update
+    if (walker) {
+      // rows 16w..16w+15 of D = U - W S (contraction over the state's rows)
+      f4 d0 = zero, d1 = zero;
+#pragma unroll
+      for (int ib = 0; ib < NIB; ib += 2) {
+        const f4 b0 = ld4(&St[m * SP + ib * 16 + 4 * g]);
+        const f4 b1 = ld4(&St[m * SP + ib * 16 + 16 + 4 * g]);
+        nx.w[ib] = ld4(&cn[L::W + blk(w, ib, NIB, lane)]);
+        nx.w[ib + 1] = ld4(&cn[L::W + blk(w, ib + 1, NIB, lane)]);
+#pragma unroll
+        for (int u = ib; u < ib + 2; ++u)
+          kt[u] = ld4(&ck[L::KT + blk(w * OWN + u / 4, u % 4, CH / 16, lane)]);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          d0 = mma(cu.w[ib][kk], b0[kk], d0);
+          d1 = mma(cu.w[ib + 1][kk], b1[kk], d1);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the next loads behind these MFMAs
       }
-      sacc[o] = acc;
-      st4(&St[m * SP + ib * 16 + 4 * g], acc);
+      fetch_small(cn, nx);
+      const f4 dd = cu.u - (d0 + d1);
+      st4(&Dc[w * 256 + 4 * lane], dd);
+      f4 dw;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dw[r] = __expf(cu.lglast - cu.lg[r]) * dd[r];
+      st4(&Dt[m * AP + w * 16 + 4 * g], dw);
+      glast = __expf(cu.lglast);
+    } else {
+      out_qs(c);
     }
-    __syncthreads();  // St holds the next entry state; Dt is free
+    __syncthreads();  // Dt and Dc complete; every wave is done reading St
+    if (walker) {
+      // S = e^{lg_last} S + K^T diag(R[last, :]) D for this wave's row blocks
+#pragma unroll
+      for (int o = 0; o < OWN; ++o) {
+        const int ib = w * OWN + o;
+        f4 acc = sacc[o] * glast;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          const f4 a = kt[o * 4 + tb];
+          const f4 bb = ld4(&Dt[m * AP + tb * 16 + 4 * g]);
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) acc = mma(a[kk], bb[kk], acc);
+        }
+        sacc[o] = acc;
+        st4(&St[m * SP + ib * 16 + 4 * g], acc);
+      }
+    } else {
+      out_pd(c);
+      if (c + 1 < nch) out_fetch(c + 1);
+    }
+    __syncthreads();  // St holds the next entry state; Dt and Dc are free
   };
   Ops xa, xb;
-  fetch(0, xa);
+  if (walker)
+    fetch(0, xa);
+  else
+    out_fetch(0);
+  __syncthreads();  // St holds the entry state
   for (int c = 0; c < nch; c += 2) {
     step(c, xa, xb);
     if (c + 1 < nch) step(c + 1, xb, xa);
   }
+  if (walker) {
 #pragma unroll
-  for (int o = 0; o < OWN; ++o) {
-    const int ib = w * OWN + o;
+    for (int o = 0; o < OWN; ++o) {
+      const int ib = w * OWN + o;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) S[(ib * 16 + 4 * g + r) * DV + j0 + m] = sacc[o][r];
-  }
-}
-
-template <int DK, int DV>
-__global__ void __launch_bounds__(256) k_gdn_out(const float *__restrict__ q,
-                                                 const float *__restrict__ ws,
-                                                 float *__restrict__ out, int BH, int P, int nch) {
-  using L = Chunk<DK, DV>;
-  constexpr int NJ = DV / OC;  // column blocks of the output
-  constexpr int OP = OC + 4;
-  __shared__ __align__(16) float Ss[DK * OP];  // S_c[:, j0:j0+OC]
-  __shared__ __align__(16) float Ds[CH * OP];  // D_c[:, j0:j0+OC]
-  int G, k;
-  if (!head_slot(nch * NJ, BH, G, k)) return;  // whole workgroup, before any barrier
-  const int c = k / NJ, jh = k % NJ;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, m = lane & 15, g = lane >> 4;
-  const size_t bh = G;
-  const int t0 = c * CH;
-  const int n = min(CH, P - t0);
-  const float *ck = ws + (bh * nch + c) * L::SIZE;
-  const int j0 = jh * OC;
-  const f4 zero = {0.f, 0.f, 0.f, 0.f};
-  // this wave's A operands: rows 16w.. of Q and of P
-  const bool qin = w * 16 + m < n;
-  const float *qr = q + (bh * P + t0 + w * 16 + m) * DK;
-  f4 qa[DK / 16], pa[4];
-#pragma unroll
-  for (int ib = 0; ib < DK / 16; ++ib) qa[ib] = qin ? ld4(qr + ib * 16 + 4 * g) : zero;
-#pragma unroll
-  for (int sb = 0; sb < 4; ++sb)
-    pa[sb] = sb <= w ? ld4(&ck[L::P + blk(w, sb, CH / 16, lane)]) : zero;
-  const f4 lgr = ld4(&ck[L::LG + w * 16 + 4 * g]);
-  {  // the shared B operands, stored in accumulator order: wave w moves blocks w, w + 4, ...
-    constexpr int NB = OC / 16;  // column blocks of the staged columns
-    constexpr int NS = DK / 16 * NB / 4, ND = CH / 16 * NB / 4;
-    f4 sr[NS], dr[ND];
-#pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      const int b = w + 4 * u;
-      sr[u] = ld4(&ck[L::SC + blk(b / NB, j0 / 16 + b % NB, DV / 16, lane)]);
+      for (int r = 0; r < 4; ++r) S[(ib * 16 + 4 * g + r) * DV + j0 + m] = sacc[o][r];
     }
-#pragma unroll
-    for (int u = 0; u < ND; ++u) {
-      const int b = w + 4 * u;
-      dr[u] = ld4(&ck[L::DC + blk(b / NB, j0 / 16 + b % NB, DV / 16, lane)]);
-    }
-#pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      const int b = w + 4 * u;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Ss[((b / NB) * 16 + 4 * g + r) * OP + (b % NB) * 16 + m] = sr[u][r];
-    }
-#pragma unroll
-    for (int u = 0; u < ND; ++u) {
-      const int b = w + 4 * u;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Ds[((b / NB) * 16 + 4 * g + r) * OP + (b % NB) * 16 + m] = dr[u][r];
-    }
-  }
-  __syncthreads();
-  if (w * 16 >= n) return;  // a wave of pad rows only
-  constexpr int NC = OC / 16;  // column tiles per wave
-  f4 acc[NC];
-#pragma unroll
-  for (int ct = 0; ct < NC; ++ct) acc[ct] = zero;
-  // Q S_c for rows 16w.. of the chunk, contraction over the state's rows
-#pragma unroll
-  for (int ib = 0; ib < DK / 16; ++ib) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const float *srow = Ss + (ib * 16 + 4 * g + kk) * OP + m;
-#pragma unroll
-      for (int ct = 0; ct < NC; ++ct) acc[ct] = mma(qa[ib][kk], srow[ct * 16], acc[ct]);
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float e = __expf(lgr[r]);
-#pragma unroll
-    for (int ct = 0; ct < NC; ++ct) acc[ct][r] *= e;
-  }
-  // + P D_c over the chunk's rows up to this wave's (P is zero above the diagonal)
-#pragma unroll
-  for (int sb = 0; sb < 4; ++sb) {
-    if (sb > w) break;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const float *drow = Ds + (sb * 16 + 4 * g + kk) * OP + m;
-#pragma unroll
-      for (int ct = 0; ct < NC; ++ct) acc[ct] = mma(pa[sb][kk], drow[ct * 16], acc[ct]);
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int t = w * 16 + 4 * g + r;
-    if (t >= n) continue;
-    float *orow = out + (bh * P + t0 + t) * DV + j0 + m;
-#pragma unroll
-    for (int ct = 0; ct < NC; ++ct) orow[ct * 16] = acc[ct][r];
   }
 }
 
@@ -524,12 +510,8 @@ hipError_t launch_dims(const float *q, const float *k, const float *v, const flo
                      k, v, beta, alpha, ws, BH, P, nch);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_gdn_scan<DK, DV>), dim3(slots * (DV / VB)), dim3(256), 0, s, ws, state,
-                     BH, nch);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_gdn_out<DK, DV>), dim3(slots * nch * (DV / OC)), dim3(256), 0, s, q, ws,
-                     out, BH, P, nch);
+  hipLaunchKernelGGL((k_gdn_scan<DK, DV>), dim3(slots * (DV / VB)), dim3(SCAN_THREADS), 0, s, q,
+                     ws, state, out, BH, P, nch);
   return hipGetLastError();
 }
 
@@ -543,7 +525,7 @@ size_t gdn_workspace_bytes(int B, int H, int P, int dk, int dv) {
 bool gdn_grid_fits(int B, int H, int P) {
   const size_t slots = 8 * ((static_cast<size_t>(B) * H + 7) / 8);
   const size_t nch = (static_cast<size_t>(P) + CH - 1) / CH;
-  const size_t per = std::max<size_t>(nch * (128 / OC), 128 / VB);  // the largest of the three grids
+  const size_t per = std::max<size_t>(2 * nch, 128 / VB);  // the larger of the two grids
   return slots * per <= 0x7fffffff;
 }
 

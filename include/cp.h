@@ -466,9 +466,9 @@ int cp_select_row(const void *x, void *y, const int32_t *idx, int offset, int B,
  *              after the last token (the layer's "cache")
  *   out        fp32 [B, H, P, dv]
  *   workspace  device scratch of at least cp_gdn_workspace_bytes(); it holds the
- *              per-chunk products and every chunk's entry state and is overwritten
+ *              per-chunk products and is overwritten
  * dk and dv each 64 or 128; q, k, v and workspace 16-byte aligned.
- * All three launches go to `stream` in order; the call returns once they are queued.
+ * Both launches go to `stream` in order; the call returns once they are queued.
  * Errors: CP_ERR_ARG (null, misaligned, negative sizes), CP_ERR_SHAPE (dk, dv; B * H * P beyond one launch grid),
  *         CP_ERR_WORKSPACE, CP_ERR_HIP.  P = 0 is a no-op (state untouched).
  */

@@ -242,8 +242,8 @@ def test_gdn_validation(cp):
     lib = cp.raw()
     f = lib.cp_gdn_chunk_prefill
     ws = cp.gdn_workspace_bytes(1, 2, 100, 64, 64)
-    # per (sequence, head, chunk of 64): W, U, P, lg, K^T, entry state, D (fp32)
-    assert ws == 1 * 2 * 2 * (2 * 64 * 64 + 2 * 64 * 64 + 64 * 64 + 64 + 64 * 64) * 4
+    # per (sequence, head, chunk of 64): W, U, P, lg, K^T (fp32)
+    assert ws == 1 * 2 * 2 * (64 * 64 + 64 * 64 + 64 * 64 + 64 + 64 * 64) * 4
     assert cp.gdn_workspace_bytes(1, 2, 100, 96, 64) == 0
     call = lambda **kw: f(*[kw.get(n, FAKE) for n in ("q", "k", "v", "beta", "alpha", "state", "out")],
                           kw.get("B", 1), kw.get("H", 2), kw.get("P", 100), kw.get("dk", 64),

@@ -377,33 +377,54 @@ __global__ void __launch_bounds__(SCAN_THREADS) k_gdn_scan(const float *__restri
     lgo = ld4(&ck[L::LG + 16 * ow + 4 * g]);
   };
   float *qs = Qs + ow * 16 * QP;
-  auto out_qs = [&](int c) {  // Q S_c, scaled by e^lg
-    (void)c;
+  // Q S_c is split over both intervals, so that the output waves' share of the matrix
+  // cores in each is about half the walkers' and the barriers do not wait for them: the
+  // first half of the contraction while the walkers form D_c, the second half (its S_c
+  // operands kept in registers, since the state update overwrites St) with P D_c.
+  constexpr int NH = NIB / 2;
+  f4 svh[NH];  // S_c operands of the second half
+  auto out_qs = [&]() {  // first half of Q S_c
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
       const int e = lane + 64 * u;
       st4(&qs[(e / (DK / 4)) * QP + (e % (DK / 4)) * 4], qreg[u]);
     }
-    f4 qa[NIB], sv[NIB];
+    f4 qa[NH], sv[NH];
 #pragma unroll
-    for (int ib = 0; ib < NIB; ++ib) {
+    for (int ib = 0; ib < NH; ++ib) {
       qa[ib] = ld4(&qs[m * QP + ib * 16 + 4 * g]);
       sv[ib] = ld4(&St[m * SP + ib * 16 + 4 * g]);
+      svh[ib] = ld4(&St[m * SP + (NH + ib) * 16 + 4 * g]);
     }
     f4 o0 = zero, o1 = zero;
 #pragma unroll
-    for (int ib = 0; ib < NIB; ib += 2) {
+    for (int ib = 0; ib < NH; ib += 2) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         o0 = mma(qa[ib][kk], sv[ib][kk], o0);
         o1 = mma(qa[ib + 1][kk], sv[ib + 1][kk], o1);
       }
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) oacc[r] = (o0[r] + o1[r]) * __expf(lgo[r]);
+    oacc = o0 + o1;
   };
-  auto out_pd = [&](int c) {  // + P D_c over the chunk's rows up to the wave's, then store
+  auto out_pd = [&](int c) {  // second half of Q S_c, e^lg, + P D_c, then store
     const int t0 = c * CH;
+    {
+      f4 qa[NH];
+#pragma unroll
+      for (int ib = 0; ib < NH; ++ib) qa[ib] = ld4(&qs[m * QP + (NH + ib) * 16 + 4 * g]);
+      f4 o1 = zero;
+#pragma unroll
+      for (int ib = 0; ib < NH; ib += 2) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          oacc = mma(qa[ib][kk], svh[ib][kk], oacc);
+          o1 = mma(qa[ib + 1][kk], svh[ib + 1][kk], o1);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) oacc[r] = (oacc[r] + o1[r]) * __expf(lgo[r]);
+    }
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
       if (sb > ow) break;
@@ -455,7 +476,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) k_gdn_scan(const float *__restri
       st4(&Dt[m * AP + w * 16 + 4 * g], dw);
       glast = __expf(cu.lglast);
     } else {
-      out_qs(c);
+      out_qs();
     }
     __syncthreads();  // Dt and Dc complete; every wave is done reading St
     if (walker) {

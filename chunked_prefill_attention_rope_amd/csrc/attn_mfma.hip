@@ -70,18 +70,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// acc + lo + hi of a packed bf16 pair, in one instruction (a dot product with (1, 1)).
-// The builtin only exists for the gfx950 device pass; the host pass never runs it.
-__device__ __forceinline__ float add_bf16x2(uint32_t pair, float acc) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
-                                         __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
-#else
-  return acc + static_cast<float>(__builtin_bit_cast(bf16x2, pair)[0]) +
-         static_cast<float>(__builtin_bit_cast(bf16x2, pair)[1]);
-#endif
-}
-
 // One wave-wide direct-to-LDS load: each lane's 16 bytes at src land at
 // lds_base + 16 * lane.  The builtin only exists for the gfx950 device pass; the
 // host pass of a HIP kernel never runs device code, and would otherwise drop the
@@ -812,9 +800,8 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
           const float x0 = sacc[kb][8 * half + 2 * e], x1 = sacc[kb][8 * half + 2 * e + 1];
           const float p0 = __builtin_amdgcn_exp2f(fmaf(x0, kx, neg_m));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(x1, kx, neg_m));
+          l_run += p0 + p1;
           w[e] = pack_bf16x2(p0, p1);
-          // the row sum takes the rounded probabilities that P V multiplies
-          l_run = add_bf16x2(w[e], l_run);
         }
         pb[2 * kb + half] = __builtin_bit_cast(bf16x8, w);
       }

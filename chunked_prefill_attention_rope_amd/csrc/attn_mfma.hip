@@ -667,6 +667,7 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
     const uint32_t kbase = lds_addr(Ks) + 2 * (n * D);
     const int kx = hh ^ k_sw;
     u32x4 kf[KP][NKB];
+    __builtin_amdgcn_s_setprio(1);  // the products go first when both waves of a SIMD are ready
 #pragma unroll
     for (int s = 0; s + 1 < KP; ++s) k_read_blocks<D, 0, NKB>(kbase + 16 * ((2 * s) ^ kx), kf[s]);
 #pragma unroll
@@ -687,6 +688,7 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
         sacc[kb] = mfma(__builtin_bit_cast(bf16x8, cur[kb]), qf[s], sacc[kb]);
       hook(s);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Masking and online softmax of tile u: turns the scores in sacc into the bf16
@@ -812,6 +814,7 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
   // are already in wv[0], those of block db + 1 are in flight while block db multiplies
   auto pv_tile = [&](uint32_t vbase, const bf16x8 *pb, u32x2 (*wv)[2 * NPT])
                      __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int db = 0; db < NDW; ++db) {
       u32x2 *cur = wv[db & 1];
@@ -827,6 +830,7 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
         oacc[db] = mfma(__builtin_bit_cast(bf16x8, a), pb[t], oacc[db]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Staggered stages (in-kernel rule, 8 waves as two per SIMD): waves 4..7 run a tile's

@@ -26,32 +26,69 @@ namespace {
 constexpr int kPlanThreads = 256;
 constexpr int kMergeRound = 4;  // pieces the plan merge fetches per memory round trip
 
-// Exclusive prefix sums of in[0, n) into out[0, n], out[n] = the total; every thread of
-// the block calls it (in and out distinct).  Each thread sums a run of consecutive
-// elements, the runs' sums are scanned within each wave by lane shuffles, and the waves'
-// totals are added through LDS: two barriers (a log-step scan through LDS costs two per
-// step, each behind an LDS round trip).
-__device__ void block_scan(const int *in, int *out, int n, int *wsum) {
-  const int t = threadIdx.x, nt = blockDim.x;
+// The plan's three exclusive prefix sums in one pass (out[n] = the total; every thread
+// of the block calls it): units per rank k (pieces of the k-th longest sequence times
+// the KV heads), split entries per sequence and partial slots per sequence, formed from
+// pc (pieces per sequence) and order (sequences by rank) as they are summed.  Each
+// thread sums a run of consecutive elements, the runs' sums are scanned within each wave
+// by lane shuffles, and the waves' totals are added through LDS: two barriers for all
+// three (a log-step scan through LDS costs two per step).  wsum: 3 x (threads / 64).
+__device__ void plan_scans(const int *pc, const int *order, int n, int nKV, int qtiles,
+                           int *upre, int *gpre, int *spre, int *wsum) {
+  const int t = threadIdx.x, nt = blockDim.x, nw = nt / 64;
   const int per = (n + nt - 1) / nt;
   const int lo = imin(n, t * per), hi = imin(n, lo + per);
-  int sum = 0;
-  for (int k = lo; k < hi; ++k) sum += in[k];
-  const int lane = t & 63, w = t >> 6;
-  int x = sum;  // inclusive scan over the wave
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) wsum[w] = x;
-  __syncthreads();
-  int run = x - sum;
-  for (int v = 0; v < w; ++v) run += wsum[v];
+  auto vals = [&](int k, int &u, int &gq, int &sq) {
+    const int P = pc[k];
+    u = pc[order[k]] * nKV;
+    gq = P > 1 ? nKV * qtiles : 0;
+    sq = P > 1 ? nKV * qtiles * P : 0;
+  };
+  int s0 = 0, s1 = 0, s2 = 0;
   for (int k = lo; k < hi; ++k) {
-    out[k] = run;
-    run += in[k];
+    int u, gq, sq;
+    vals(k, u, gq, sq);
+    s0 += u;
+    s1 += gq;
+    s2 += sq;
   }
-  if (t == nt - 1) out[n] = run;  // the last thread's run ends at the total
+  const int lane = t & 63, w = t >> 6;
+  int x0 = s0, x1 = s1, x2 = s2;  // inclusive scans over the wave
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y0 = __shfl_up(x0, o, 64), y1 = __shfl_up(x1, o, 64), y2 = __shfl_up(x2, o, 64);
+    if (lane >= o) {
+      x0 += y0;
+      x1 += y1;
+      x2 += y2;
+    }
+  }
+  if (lane == 63) {
+    wsum[w] = x0;
+    wsum[nw + w] = x1;
+    wsum[2 * nw + w] = x2;
+  }
+  __syncthreads();
+  int r0 = x0 - s0, r1 = x1 - s1, r2 = x2 - s2;
+  for (int v = 0; v < w; ++v) {
+    r0 += wsum[v];
+    r1 += wsum[nw + v];
+    r2 += wsum[2 * nw + v];
+  }
+  for (int k = lo; k < hi; ++k) {
+    int u, gq, sq;
+    vals(k, u, gq, sq);
+    upre[k] = r0;
+    gpre[k] = r1;
+    spre[k] = r2;
+    r0 += u;
+    r1 += gq;
+    r2 += sq;
+  }
+  if (t == nt - 1) {  // the last thread's runs end at the totals
+    upre[n] = r0;
+    gpre[n] = r1;
+    spre[n] = r2;
+  }
   __syncthreads();
 }
 
@@ -67,10 +104,9 @@ __global__ void __launch_bounds__(kPlanThreads) k_attn_plan(AttnParams p, int32_
   __shared__ int pc_s[kPlanMaxB];     // pieces of b
   __shared__ int len_s[kPlanMaxB];    // tiles per piece of b (ranking key)
   __shared__ int order_s[kPlanMaxB];  // sequences by rank
-  __shared__ int tmp_s[kPlanMaxB];
   __shared__ int upre_s[kPlanMaxB + 1], gpre_s[kPlanMaxB + 1], spre_s[kPlanMaxB + 1];
   __shared__ int seen_s[kPlanMaxB], nvr_s[kPlanMaxB];  // seen and raw n_valid, read once
-  __shared__ int wsum_s[kPlanThreads / 64];
+  __shared__ int wsum_s[3 * (kPlanThreads / 64)];
   __shared__ int tot_s, sum_s, T_s;
   const int t = threadIdx.x, nt = static_cast<int>(blockDim.x);
   const int B = p.B;
@@ -136,23 +172,19 @@ __global__ void __launch_bounds__(kPlanThreads) k_attn_plan(AttnParams p, int32_
   __syncthreads();
   // 3. rank: longest piece first, ties by sequence
   for (int b = t; b < B; b += nt) {
+    const int lb = len_s[b];
     int r = 0;
-    for (int o = 0; o < B; ++o)
-      r += (len_s[o] > len_s[b]) || (len_s[o] == len_s[b] && o < b);
+#pragma unroll 8
+    for (int o = 0; o < B; ++o) {  // (unrolled: eight LDS reads in flight, not one)
+      const int lo_ = len_s[o];
+      r += (lo_ > lb) || (lo_ == lb && o < b);
+    }
     order_s[r] = b;
   }
   __syncthreads();
   // 4. units (sequence, piece, KV head) in rank order; split entries and partial slots in
   // sequence order
-  for (int k = t; k < B; k += nt) tmp_s[k] = pc_s[order_s[k]] * p.nKV;
-  __syncthreads();
-  block_scan(tmp_s, upre_s, B, wsum_s);
-  for (int b = t; b < B; b += nt) tmp_s[b] = pc_s[b] > 1 ? p.nKV * p.qtiles : 0;
-  __syncthreads();
-  block_scan(tmp_s, gpre_s, B, wsum_s);
-  for (int b = t; b < B; b += nt) tmp_s[b] = pc_s[b] > 1 ? p.nKV * p.qtiles * pc_s[b] : 0;
-  __syncthreads();
-  block_scan(tmp_s, spre_s, B, wsum_s);
+  plan_scans(pc_s, order_s, B, p.nKV, p.qtiles, upre_s, gpre_s, spre_s, wsum_s);
   const int U = upre_s[B];
   // 5. one item per block: unit r's query tile q at block (r / 8) * 8 * qtiles + 8 q + r % 8
   int32_t *items = plan + kPlanHeaderInts;

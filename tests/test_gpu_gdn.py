@@ -42,6 +42,14 @@ def test_gdn_matches_token_recurrence(cp, dk, dv, P):
     _check(cp, I.make_gdn(cfg))
 
 
+def test_gdn_many_heads(cp):
+    """33 (sequence, head) pairs over five chunks, the last one ragged: the scan
+    workgroups of several heads share each XCD's slots (surplus workgroups of the last
+    group exit at once), and the output waves run over an odd number of chunks."""
+    cfg = I.GdnCfg("t", 3, 11, 300, 128, 128, 91)
+    _check(cp, I.make_gdn(cfg))
+
+
 @pytest.mark.parametrize("name", ["g0", "g1"])
 def test_gdn_workloads(cp, name):
     _check(cp, I.make_gdn(I.gdn_config(name)))

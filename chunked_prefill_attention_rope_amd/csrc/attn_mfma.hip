@@ -153,6 +153,7 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
   constexpr int NL = NK / (64 * NW); // direct-to-LDS loads per wave per tile per tensor
   constexpr int RPI = 64 / CPR;      // rows covered by one wave-wide 1 KB load
   constexpr int NS = D / 16;         // k-steps of QK^T
+  constexpr bool PRESCALE = D == 128;  // Q scaled by scale * log2 e, products from C = -m
   constexpr int NKB = KT / 32;       // 32-key blocks per tile
   constexpr int NDB = D / 32;        // 32-dim blocks of the output
   constexpr int NDW = NDB / DSPLIT;  // ... accumulated by one wave
@@ -285,6 +286,20 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
         qf[sh] = __builtin_bit_cast(bf16x8, yhi);
       }
     }
+    // D = 128 (the long tile loops): scaled by scale * log2 e and rounded to bf16 (RNE),
+    // so that the products give the scores in the base-2 units of the softmax with no
+    // multiply per score.  (At D = 256 the scaling costs a latency-bound call more
+    // than it saves: its scores are scaled in the softmax.)
+#pragma unroll
+    for (int s = 0; s < (PRESCALE ? NS : 0); ++s) {
+      const u32x4 v = __builtin_bit_cast(u32x4, qf[s]);
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = pack_bf16x2(__uint_as_float(v[e] << 16) * p.sl2e,
+                           __uint_as_float(v[e] & 0xffff0000u) * p.sl2e);
+      qf[s] = __builtin_bit_cast(bf16x8, w);
+    }
   }
 
   // seen and n_valid are both requested before either is used (scalar loads complete
@@ -345,6 +360,15 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  // With the scaled Q the score products start from C = -msub (nmb), so that they give
+  // s' = s * scale * log2 e - msub, the exponent of the probability: msub is the
+  // running maximum once a row has seen an attended key (0 before).  Otherwise the
+  // products give the raw scores s and the softmax scales them (kq = scale * log2 e).
+  const float kq = PRESCALE ? 1.f : p.sl2e;
+  float msub = 0.f;
+  f32x16 nmb;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) nmb[e] = 0.f;
 
   TileSeq ts{};
   int u0 = 0, u1 = 0;
@@ -461,10 +485,6 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
   // S^T = K Q^T for the tile in Ks, K fragments read one k-step ahead; hook(s) runs
   // after k-step s (the caller's direct-to-LDS loads, spread over the steps)
   auto qk_tile = [&](const uint16_t *Ks, f32x16 *sacc, auto &&hook) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
     // K fragments of KP k-steps in flight; lane: key row 32 kb + n, 16-byte chunk
     // 2 s + hh of the row, stored at chunk (2 s + hh) ^ k_sw = 2 s ^ (hh ^ k_sw)
     constexpr int KP = NS < 3 ? NS : 3;
@@ -489,7 +509,8 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
         k_wait<0, NKB>(cur);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        sacc[kb] = mfma(__builtin_bit_cast(bf16x8, cur[kb]), qf[s], sacc[kb]);
+        sacc[kb] = mfma(__builtin_bit_cast(bf16x8, cur[kb]), qf[s],
+                        s == 0 ? (PRESCALE ? nmb : f32x16{}) : sacc[kb]);
       hook(s);
     }
     __builtin_amdgcn_s_setprio(0);
@@ -521,16 +542,23 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
       }
     }
 
-    // ---- online softmax in base 2.  Visible tiles keep raw scores s and use
-    // p = 2^(s*scale*log2e - m); masked tiles first form t = s*scale*log2e +
-    // bias*log2e and use p = 2^(t - m).  (scale > 0, so max(s)*c = max(s*c).)
+    // ---- online softmax in base 2 on s' = kq * (products) - msub (kq = 1, or the scale
+    // for the raw scores of the unscaled Q): visible tiles use p = 2^s' directly;
+    // masked tiles first add bias * log2 e.  (scale > 0, so max(s) * c = max(s * c).)
     float mt = -INFINITY;
     if (visible) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kb][e]);
-      mt *= p.sl2e;
+      if (!PRESCALE) {
+        mt *= kq;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) sacc[kb][e] = fmaf(sacc[kb][e], kq, -msub);
+        mt -= msub;
+      }
     } else if constexpr (EXPLICIT) {
       // mask block of this stage, row r of this lane; keys past the valid range -inf
       const float *Ms = Mst + r * KT;
@@ -547,7 +575,8 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
           for (int e = 0; e < 4; ++e) {
             const int k = 32 * kb + 8 * rq + e;
             const float a = k < xl ? m4[e] : -INFINITY;
-            const float tv = fmaf(sacc[kb][4 * rq + e], p.sl2e, a * kLog2e);
+            const float tv = PRESCALE ? sacc[kb][4 * rq + e] + a * kLog2e
+                                      : fmaf(sacc[kb][4 * rq + e], kq, a * kLog2e - msub);
             sacc[kb][4 * rq + e] = tv;
             mt = fmaxf(mt, tv);
           }
@@ -575,27 +604,40 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
             const int k = 32 * kb + 8 * rq + e;
             const bool att = (k < xc) & ((k < xa) | (k >= xb));
             const float a = k < xl ? (att ? 0.f : kMasked) : -INFINITY;
-            const float tv = fmaf(sacc[kb][4 * rq + e], p.sl2e, a * kLog2e);
+            const float tv = PRESCALE ? sacc[kb][4 * rq + e] + a * kLog2e
+                                      : fmaf(sacc[kb][4 * rq + e], kq, a * kLog2e - msub);
             sacc[kb][4 * rq + e] = tv;
             mt = fmaxf(mt, tv);
           }
     }
+    // The maximum over the lane pair; a rise by more than 2^8 over the running maximum
+    // (or the row's first attended key) moves msub there: the tile's scores shift by
+    // the rise, C = -msub for the next tiles, and l and O are rescaled.  A row with no
+    // attended key in the tile (its maximum near -1e30 log2 e, or -inf) never moves
+    // msub: C must stay near the real scores, or fp32 would lose them.
     mt = pair_max(mt);
-    const bool raise = mt > m_run + kRescaleSlack;
+    const float mabs = mt + msub;
+    const bool raise = mabs > m_run + kRescaleSlack && mabs > kNoKeyFloor;
     if (__any(raise)) {
-      const float m_new = raise ? mt : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
+      const float m_new = raise ? mabs : m_run;
+      const float delta = raise ? mt : 0.f;
+      const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 from -inf
       m_run = m_new;
+      msub = raise ? m_new : msub;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDW; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[kb][e] -= delta;
+      if (PRESCALE) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) nmb[e] = -msub;
+      }
     }
-    // p = 2^(x * k - m): x = s with k = scale*log2e on visible tiles, x = t with
-    // k = 1 on masked ones (fma(t, 1, -m) rounds exactly as t - m)
-    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
-    const float kx = visible ? p.sl2e : 1.f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -604,8 +646,8 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float x0 = sacc[kb][8 * half + 2 * e], x1 = sacc[kb][8 * half + 2 * e + 1];
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(x0, kx, neg_m));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(x1, kx, neg_m));
+          const float p0 = __builtin_amdgcn_exp2f(x0);
+          const float p1 = __builtin_amdgcn_exp2f(x1);
           l_run += p0 + p1;
           w[e] = pack_bf16x2(p0, p1);
         }

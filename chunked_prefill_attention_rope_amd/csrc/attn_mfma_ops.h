@@ -18,6 +18,8 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kRescaleSlack = 8.f;  // log2 units
+// scaled maxima at or below this carry no attended key (masked scores: -1e30 log2 e)
+constexpr float kNoKeyFloor = -1e29f;
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const f32x2 v = {a, b};

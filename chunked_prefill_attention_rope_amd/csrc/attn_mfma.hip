@@ -397,57 +397,94 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
   // ---- direct-to-LDS staging.  Wave-wide load q (= wave * NL + e) fills 1 KB of
   // the tile: rows q * RPI + lane / CPR, physical chunk lane % CPR, which holds the
   // row's logical chunk (physical ^ swizzle).  Rows outside the tile's valid range
-  // read a valid row instead; their scores are masked to -inf.
-  int koff[NL], voff[NL];
+  // read a valid row instead; their scores are masked to -inf.  The source of load e
+  // is a scalar base plus a 32-bit per-lane byte offset: lk[e] / lv[e] (the tile row
+  // lrow[e] and its swizzled chunk, fixed for the loop) plus, on a tile whose rows are
+  // not consecutive slots from `first` (ring wrap, a partial last tile), the lane's
+  // own row shift d[e].
+  uint32_t lk[NL], lv[NL];
+  int lrow[NL];
 #pragma unroll
   for (int e = 0; e < NL; ++e) {
     const int row = (wave * NL + e) * RPI + lane / CPR, phys = lane % CPR;
-    koff[e] = (phys ^ kswz<D>(row)) << 3;
-    voff[e] = (phys ^ vswz<D>(row)) << 3;
+    lrow[e] = row;
+    lk[e] = static_cast<uint32_t>(row * (2 * D) + ((phys ^ kswz<D>(row)) << 4));
+    lv[e] = static_cast<uint32_t>(row * (2 * D) + ((phys ^ vswz<D>(row)) << 4));
   }
-  // source rows (cache slot or chunk row) of this wave's loads of tile u
-  auto plan = [&](int u, int *srow, int &first, int &lim) __attribute__((always_inline)) {
-    const bool chunk = ts.at(u, KT, &first);
-    lim = chunk ? p.C : gl.L;
-    const int c_ns = imax(first, gl.ns);
-    int s_ns = 0;
-    if (!chunk && p.ring && !small_ring && c_ns < gl.L)
-      s_ns = slot_of(gl.lo + (c_ns - gl.ns), p.cap, 1, p.sink);
+  const char *KCb = reinterpret_cast<const char *>(KC), *VCb = reinterpret_cast<const char *>(VC);
+  const char *KNb = reinterpret_cast<const char *>(KN), *VNb = reinterpret_cast<const char *>(VN);
+  // Tile u's sources.  In the long tile loops (D = 128, standard tiles) the loads ahead
+  // of the final tiles are issued too, reading the last tile again into the stage a
+  // real load would refill: every tile issues the same loads, with no branch.  Short
+  // calls (few tiles per split) skip them: there the repeated loads only add latency.
+  struct Src {
+    const char *k, *v;
+    uint32_t d[NL];
+    int first, lim;
+    bool chunk;
+  };
+  auto plan = [&](int u) __attribute__((always_inline)) {
+    Src sr;
+    sr.chunk = ts.at(imin(u, u1 - 1), KT, &sr.first);
+    sr.lim = sr.chunk ? p.C : gl.L;
+    sr.k = sr.chunk ? KNb : KCb;
+    sr.v = sr.chunk ? VNb : VCb;
+    const bool ringp = !sr.chunk && p.ring && sr.first + KT > gl.ns;
 #pragma unroll
-    for (int e = 0; e < NL; ++e) {
-      const int row = (wave * NL + e) * RPI + lane / CPR;
-      const int col = imin(first + row, lim - 1);
-      int sl = col;
-      if (!chunk && p.ring && col >= gl.ns) {
-        if (!small_ring) {
-          sl = s_ns + (col - c_ns);
-          if (sl >= p.cap) sl -= R;
-        } else {
-          sl = slot_of(gl.lo + (col - gl.ns), p.cap, 1, p.sink);
-        }
-      }
-      srow[e] = sl;
+    for (int e = 0; e < NL; ++e) sr.d[e] = 0;
+    // a tile of KT consecutive slots from base_row, or -1.  A ring tile past the sinks
+    // that does not wrap qualifies at D = 256 only: same box, the ring path was faster
+    // per lane at D = 128 (sliding layers 132.4-132.9 against 136.0-137.4 us) and as a
+    // base at D = 256 (16.6 against 16.9 us).
+    int base_row = -1;
+    if (!ringp) {
+      if (sr.first + KT <= sr.lim) base_row = sr.first;
+    } else if (D != 128 && !small_ring && sr.first >= gl.ns && sr.first + KT <= sr.lim) {
+      const int s0 = slot_of(gl.lo + (sr.first - gl.ns), p.cap, 1, p.sink);
+      if (s0 + KT <= p.cap) base_row = s0;
     }
-    return chunk;
+    if (base_row >= 0) {
+      // the shift is the base's
+      const size_t off = static_cast<size_t>(base_row) * (2 * D);
+      sr.k += off;
+      sr.v += off;
+    } else {
+      const int c_ns = imax(sr.first, gl.ns);
+      int s_ns = 0;
+      if (ringp && !small_ring && c_ns < gl.L) s_ns = slot_of(gl.lo + (c_ns - gl.ns), p.cap, 1, p.sink);
+#pragma unroll
+      for (int e = 0; e < NL; ++e) {
+        const int col = imin(sr.first + lrow[e], sr.lim - 1);
+        int sl = col;
+        if (ringp && col >= gl.ns) {
+          if (!small_ring) {
+            sl = s_ns + (col - c_ns);
+            if (sl >= p.cap) sl -= R;
+          } else {
+            sl = slot_of(gl.lo + (col - gl.ns), p.cap, 1, p.sink);
+          }
+        }
+        sr.d[e] = static_cast<uint32_t>(sl - lrow[e]) * (2 * D);
+      }
+    }
+    return sr;
   };
   // load j of a tile into ring stage st: j < NL K rows, j < 2 NL V rows, else 256
   // bytes of the mask block (positions from mrow / mcol above; columns clamped into the
   // valid range -- those past it are masked to -inf)
-  auto dma = [&](int j, bool chunk, const int *srow, int first, int lim, uint16_t *st)
-                 __attribute__((always_inline)) {
+  auto dma = [&](int j, const Src &sr, uint16_t *st) __attribute__((always_inline)) {
     if (j < 2 * NL) {
       const int e = j < NL ? j : j - NL;
       const int q = wave * NL + e;
-      const size_t r = static_cast<size_t>(srow[e]) * D;
       if (j < NL)
-        dma16((chunk ? KN + r : KC + r) + koff[e], st + q * 512);
+        dma16(reinterpret_cast<const uint16_t *>(sr.k + (lk[e] + sr.d[e])), st + q * 512);
       else
-        dma16((chunk ? VN + r : VC + r) + voff[e], st + TILE + q * 512);
+        dma16(reinterpret_cast<const uint16_t *>(sr.v + (lv[e] + sr.d[e])), st + TILE + q * 512);
     } else if constexpr (EXPLICIT) {
       const int jm = j - 2 * NL;
       const int q = wave * NMK + jm;
-      const int col = imin(first + mcol[jm], lim - 1);
-      dma4(p.mask + mrow[jm] + (chunk ? static_cast<int64_t>(gl.L) : 0) + col,
+      const int col = imin(sr.first + mcol[jm], sr.lim - 1);
+      dma4(p.mask + mrow[jm] + (sr.chunk ? static_cast<int64_t>(gl.L) : 0) + col,
            reinterpret_cast<float *>(st + 2 * TILE) + q * 64);
     }
   };
@@ -686,17 +723,19 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
   // tile u, so the ring loads STAGES - 2 tiles ahead instead of STAGES - 1.
   constexpr bool STAG = !EXPLICIT && NW == 8 && CF::WAVES == 2 && SM == 0 && STAGES >= 3;
   constexpr int PD = STAG ? STAGES - 2 : STAGES - 1;  // tiles loaded ahead
+  constexpr bool ALL_LOADS = D == 128 && SM == 0;     // loads past the last tile too
   const bool lagging = STAG && __builtin_amdgcn_readfirstlane(wave) >= 4;
 
   // tile u lives in stage u % STAGES of a ring of (K, V) tiles (a key split starts
-  // at u0 > 0)
-  for (int j = 0; j < PD; ++j)
-    if (u0 + j < u1) {
-      int srow[NL], f0, l0;
-      const bool ch = plan(u0 + j, srow, f0, l0);
+  // at u0 > 0); tiles u0 .. u0 + PD - 1 are loaded ahead (repeats of the last tile past
+  // it)
+  if (u1 > u0)
+    for (int j = 0; j < PD; ++j) {
+      if (!ALL_LOADS && u0 + j >= u1) break;
+      const Src sr = plan(u0 + j);
       uint16_t *st = ring + ((u0 + j) % STAGES) * STAGE;
 #pragma unroll
-      for (int l = 0; l < ND; ++l) dma(l, ch, srow, f0, l0, st);
+      for (int l = 0; l < ND; ++l) dma(l, sr, st);
     }
 
   // the tile loop, specialized for the leading and the lagging order (one copy each, so
@@ -710,7 +749,7 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
       // tile u has landed in this wave's share of the ring once at most the loads of
       // the tiles issued after it are outstanding; the barrier makes that true for all
       // waves and also guarantees every wave has finished reading the stage refilled
-      wait_tiles_after<ND, STAGES>(imin(u1 - 1, u + PD - 1) - u);
+      wait_tiles_after<ND, STAGES>(ALL_LOADS ? PD - 1 : imin(u1 - 1, u + PD - 1) - u);
       __builtin_amdgcn_s_barrier();
       const uint16_t *Ks = ring + (u % STAGES) * STAGE;
       const uint16_t *Vs = Ks + TILE;
@@ -724,19 +763,15 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
 
       // the tile PD ahead is loaded while this one's QK^T runs
       const int w_pf = u + PD;
-      const bool pf = w_pf < u1;
-      int srow[NL], pfirst = 0, plim = 1;
-      bool pch = false;
-  #pragma unroll
-      for (int e = 0; e < NL; ++e) srow[e] = 0;
-      if (pf) pch = plan(w_pf, srow, pfirst, plim);
+      const bool pf = ALL_LOADS || w_pf < u1;
+      const Src psr = plan(w_pf);
       uint16_t *pst = ring + (w_pf % STAGES) * STAGE;
 
       f32x16 sacc[NKB];
       qk_tile(Ks, sacc, [&](int s) __attribute__((always_inline)) {
   #pragma unroll
         for (int j = s * ND / NS; j < (s + 1) * ND / NS; ++j)
-          if (pf) dma(j, pch, srow, pfirst, plim, pst);
+          if (pf) dma(j, psr, pst);
       });
 
       if (LAG) {
@@ -762,6 +797,8 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
     tile_loop(std::integral_constant<bool, true>{});
   else
     tile_loop(std::integral_constant<bool, false>{});
+  // the repeated loads of the last tiles land before the workgroup's LDS is released
+  if (ALL_LOADS) wait_vm<0>();
 
   const float l_tot = pair_sum(l_run);
   if (!row_ok) return;

@@ -25,7 +25,8 @@ import sys
 
 _CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 # sources whose change invalidates counters measured on the attention call
-ATTN_SOURCES = ("attn_mfma.hip", "attn_valu.hip", "attn_common.h", "cp_common.h", "cp_api.hip")
+ATTN_SOURCES = ("attn_mfma.hip", "attn_mfma_ops.h", "attn_valu.hip", "attn_common.h", "cp_common.h",
+                "cp_api.hip")
 
 
 def source_digest(names=ATTN_SOURCES):

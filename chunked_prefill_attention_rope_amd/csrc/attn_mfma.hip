@@ -413,10 +413,10 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
   }
   const char *KCb = reinterpret_cast<const char *>(KC), *VCb = reinterpret_cast<const char *>(VC);
   const char *KNb = reinterpret_cast<const char *>(KN), *VNb = reinterpret_cast<const char *>(VN);
-  // Tile u's sources.  In the long tile loops (D = 128, standard tiles) the loads ahead
-  // of the final tiles are issued too, reading the last tile again into the stage a
-  // real load would refill: every tile issues the same loads, with no branch.  Short
-  // calls (few tiles per split) skip them: there the repeated loads only add latency.
+  // Tile u's sources.  At D = 128 (long tile loops) the loads ahead of the final tiles
+  // are issued too, reading the last tile again into the stage a real load would
+  // refill: every tile issues the same loads, with no branch.  At D = 64 and 256 (short
+  // calls, few tiles per split) they are skipped: there they only added latency.
   struct Src {
     const char *k, *v;
     uint32_t d[NL];
@@ -723,7 +723,7 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
   // tile u, so the ring loads STAGES - 2 tiles ahead instead of STAGES - 1.
   constexpr bool STAG = !EXPLICIT && NW == 8 && CF::WAVES == 2 && SM == 0 && STAGES >= 3;
   constexpr int PD = STAG ? STAGES - 2 : STAGES - 1;  // tiles loaded ahead
-  constexpr bool ALL_LOADS = D == 128 && SM == 0;     // loads past the last tile too
+  constexpr bool ALL_LOADS = D == 128;                // loads past the last tile too
   const bool lagging = STAG && __builtin_amdgcn_readfirstlane(wave) >= 4;
 
   // tile u lives in stage u % STAGES of a ring of (K, V) tiles (a key split starts

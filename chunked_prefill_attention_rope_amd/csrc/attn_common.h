@@ -51,6 +51,16 @@ struct AttnParams {
   // RoPE of q at load time: fp32 [q_tables][C][D] tables, or nullptr (q already rotated)
   const float *q_cos, *q_sin;
   int q_tables;
+  // Block order of the matrix-core kernel when its (split, sequence, KV head) groups are
+  // not a multiple of 8: 1 pads their count to one (the query tiles of each group share
+  // an XCD, its K/V fetched once), 0 deals the query tiles in order.  (This and xmerge
+  // are 16-bit and sit in the padding after q_tables: the block stays 320 bytes, five
+  // 64-byte lines that the kernels request at once.)
+  int16_t xpad;
+  // Merge of fragment-order partials: 0 deals its blocks in order; M > 0 puts the blocks
+  // of M consecutive 32-row groups (numbered as in AttnParams::wo) on one XCD, unit j
+  // on XCD j % 8, so that the output lines a unit writes are whole in one L2.
+  int16_t xmerge;
   // Balanced key splits (matrix-core kernel): the plan written by the plan kernel, or
   // nullptr.  Block i of the attention takes item i; split items write their partials to
   // their slot (AttnParams::wo in fragment order, slot * (frag_rows / 32) groups).
@@ -60,6 +70,9 @@ struct AttnParams {
   int plan_kt;     // keys per tile
   int plan_tmin;   // fewest tiles per piece
 };
+// the kernels request their argument block as five 64-byte lines; a sixth line measured
+// 0.2 us more per short step
+static_assert(sizeof(AttnParams) <= 320, "AttnParams outgrew five 64-byte lines");
 
 // Plan layout (int32): a header (split entries, piece length, total tiles, units), then
 // plan_grid items of kPlanItemInts (sequence, KV head, query tile, piece, pieces, partial

@@ -185,7 +185,9 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
   // the XCDs, so that sequences of different lengths spread evenly (each XCD drains
   // only its own blocks); and the split index varies slowest, so that the first part
   // of every sequence starts at once and the later parts of long sequences fill the
-  // CUs that short sequences free.
+  // CUs that short sequences free.  When the groups are not a multiple of 8 the blocks
+  // go in tile-minor order (a multiple of 8 query tiles: each tile's splits on one XCD),
+  // or the group count is padded to the next multiple of 8 (AttnParams::xpad).
   // With a balancing plan, block i takes item i of the plan: its sequence, KV head,
   // query tile, key piece and partial slot, and the sequence's seen and n_valid (one
   // scalar load; the plan kernel read them).
@@ -205,10 +207,11 @@ __global__ void __launch_bounds__((64 * Sel<D, EXT, SM>::ROWW * Sel<D, EXT, SM>:
     const unsigned nbg = static_cast<unsigned>(p.B) * p.nKV;
     const unsigned groups = static_cast<unsigned>(p.splits) * nbg;
     unsigned gi, qt;
-    if (groups % 8 == 0) {
+    if (groups % 8 == 0 || p.xpad) {
       const unsigned rest = blockIdx.x / 8;
       qt = rest % p.qtiles;
       gi = (rest / p.qtiles) * 8 + blockIdx.x % 8;
+      if (gi >= groups) return;  // padding of the last 8 groups (uniform)
     } else {
       qt = blockIdx.x % p.qtiles;
       gi = blockIdx.x / p.qtiles;
@@ -871,9 +874,15 @@ hipError_t launch_mode(const AttnParams &p, unsigned blocks, hipStream_t s) {
 
 template <int D>
 hipError_t launch_d(const AttnParams &p, hipStream_t s) {
-  const unsigned blocks =
-      p.plan ? static_cast<unsigned>(p.plan_grid)
-             : static_cast<unsigned>(p.qtiles) * p.splits * p.B * p.nKV;
+  const unsigned nu = static_cast<unsigned>(p.qtiles) * p.B * p.nKV;
+  unsigned blocks = nu * p.splits;
+  if (p.plan) {
+    blocks = static_cast<unsigned>(p.plan_grid);
+  } else if (p.xpad) {
+    // the (split, sequence, KV head) groups padded to a multiple of 8
+    const unsigned groups = static_cast<unsigned>(p.splits) * p.B * p.nKV;
+    blocks = (groups + 7) / 8 * 8 * p.qtiles;
+  }
   if (blocks == 0) return hipSuccess;
   hipError_t e;
   if (p.small_rows == 3) {

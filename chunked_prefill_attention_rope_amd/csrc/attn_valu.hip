@@ -321,8 +321,17 @@ __global__ void __launch_bounds__(256) k_attn_combine(AttnParams p, int D) {
   const I o_str = static_cast<I>(prow) * D, m_str = static_cast<I>(prow) * 2;
   const int lg_blk = FRAG ? __builtin_ctz(static_cast<unsigned>(D)) - 5 : 0;  // log2(D / 32)
   T *O = static_cast<T *>(p.out);
-  for (I t = blockIdx.x * static_cast<I>(blockDim.x) + threadIdx.x; t < total;
-       t += static_cast<I>(gridDim.x) * blockDim.x) {
+  I t0 = blockIdx.x * static_cast<I>(blockDim.x) + threadIdx.x;
+  I tstep = static_cast<I>(gridDim.x) * blockDim.x;
+  if (FRAG && p.xmerge > 0) {
+    // XCD placement (AttnParams::xmerge): block k is slot k / 8 of XCD k % 8; a unit of
+    // xmerge 32-row groups is 8 D threads per group, one pass
+    const unsigned bpu = static_cast<unsigned>(p.xmerge) * 8u * D / blockDim.x;
+    const unsigned j = blockIdx.x / 8, unit = blockIdx.x % 8 + 8 * (j / bpu);
+    t0 = (static_cast<I>(unit) * bpu + j % bpu) * blockDim.x + threadIdx.x;
+    tstep = total;
+  }
+  for (I t = t0; t < total; t += tstep) {
     // The split count and strides pass through an empty asm each iteration: loop
     // invariants to the compiler, which would otherwise compute the SB per-split
     // conditions and offsets once ahead of the loop and keep them (spilled) across it
@@ -525,6 +534,13 @@ hipError_t launch_attn_combine(const AttnParams &p, int D, int dtype, hipStream_
   const unsigned bs = 64;  // threads per workgroup: the rows spread over more CUs
   size_t blocks = (total / (v4 ? 4 : 1) + bs - 1) / bs;
   if (blocks > 16384) blocks = 16384;
+  if (frag && p.xmerge > 0) {
+    // XCD placement: 8 XCDs x the units of one XCD, every partial in one pass
+    const size_t groups = prow / 32;
+    const size_t units = (groups + p.xmerge - 1) / p.xmerge;
+    if ((8 * static_cast<size_t>(D)) % bs != 0) return hipErrorInvalidValue;
+    blocks = 8 * ((units + 7) / 8) * p.xmerge * (8 * static_cast<size_t>(D) / bs);
+  }
   // 32-bit offsets when the whole workspace's byte offsets fit 32 bits
   const bool i32 = total * static_cast<size_t>(p.splits) < (size_t(1) << 30);
   const bool wide = p.splits > 16;

@@ -162,6 +162,20 @@ AttnPlan plan_attention(const cp_cache &c, const cp_attn_args &a, bool for_works
     pl.splits = 1;
     pl.planned = false;
   }
+  // XCD placement (blocks are dealt round-robin over the 8 XCDs, each with its own
+  // L2).  A split call whose (split, sequence, KV head) groups are not a multiple of 8
+  // pads their count to one, so that the query tiles of a group share an XCD and its
+  // K/V is fetched once -- unless its query tiles are themselves a multiple of 8, where
+  // the tile-minor order keeps every split of a tile on one XCD (with its queries).  The
+  // merge deals whole units to the XCDs: the query tile when each tile's splits ran on
+  // one XCD, else one 32-row group, so that the output lines of a unit are written
+  // whole from one L2 (spread over the XCDs, two L2s write halves of a line).
+  if (pl.mfma && !pl.planned && pl.splits > 1) {
+    const long groups = static_cast<long>(pl.splits) * c.B * c.nKV;
+    const bool tile_local = groups % 8 != 0 && pl.qtiles % 8 == 0;
+    pl.xpad = groups % 8 != 0 && !tile_local && groups >= 8 ? 1 : 0;
+    pl.xmerge = tile_local ? pl.rows / 32 : 1;
+  }
   return pl;
 }
 
@@ -235,6 +249,8 @@ hipError_t launch_attention(const cp_cache &c, const cp_attn_args &a, hipStream_
   const bool advance = (a.flags & CP_ATTN_ADVANCE_SEEN) != 0;
   p.advance = advance && pl.splits > 1 ? 1 : 0;
   p.frag_rows = pl.mfma ? pl.rows : 0;
+  p.xpad = static_cast<int16_t>(pl.xpad);
+  p.xmerge = static_cast<int16_t>(pl.xmerge);
   if (pl.planned) {
     unsigned char *w = static_cast<unsigned char *>(a.workspace);
     const size_t rows = static_cast<size_t>(pl.plan_grid) * pl.rows;

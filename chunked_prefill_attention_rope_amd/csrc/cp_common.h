@@ -189,6 +189,8 @@ struct AttnPlan {
   bool planned;     // balanced key splits from a device-side plan (CP_ATTN_BALANCE)
   int plan_grid;    // ... its attention blocks (item entries)
   int plan_slots;   // ... workgroups the GPU holds at once
+  int xpad;         // block order of the split groups (AttnParams::xpad)
+  int xmerge;       // XCD placement of the merge (AttnParams::xmerge)
 };
 
 AttnPlan plan_attention(const cp_cache &c, const cp_attn_args &a, bool for_workspace);

@@ -421,6 +421,49 @@ def test_merge_fragment_rows(cp, shape, splits, mode):
     assert int(status.item()) == 0
 
 
+@pytest.mark.parametrize("shape", [
+    # (B, H, nKV, D, C, cap, seen, n_valid, splits).  The blocks of a split call go to the
+    # XCDs by (split, sequence, KV head) group; the group count decides the order:
+    # 8 query tiles per group (1024 rows of 128) with 3 and 9 groups: each query tile's
+    # splits on one XCD, the merge dealing whole tiles;
+    (2, 8, 1, 256, 128, 800, [650, 200], [128, 77], 3),
+    (3, 8, 1, 256, 128, 800, [600, 10, 333], [100, 128, 1], 3),
+    # 2 query tiles, 14 groups: padded to 16; 5 groups: in order (fewer than 8)
+    (1, 4, 1, 256, 64, 1024, [800], [52], 14),
+    (1, 4, 1, 256, 64, 1024, [800], [52], 5),
+    # 3 KV heads x 3 splits = 9 groups of 1 tile at D = 128
+    (1, 12, 3, 128, 50, 900, [870], [49], 3),
+])
+@pytest.mark.parametrize("mode", ["inkernel", "explicit"])
+def test_split_placement(cp, shape, mode):
+    """Key splits in each block order of the XCD placement (tile-minor with whole tiles
+    per XCD in the merge, padded groups, groups in order): every real row matches the
+    oracle, pad rows are zeros, a repeat is bit-identical, and the selection is the
+    merged row."""
+    B, H, nKV, D, C, cap, seen, n_valid, splits = shape
+    cfg = I.small(dtype=I.BF16, B=B, H=H, nKV=nKV, D=D, C=C, cap=cap, seen=seen,
+                  n_valid=n_valid)
+    t, cache, status = _setup(cp, cfg)
+    q, k, v = dev(t["q"]), dev(t["k"]), dev(t["v"])
+    nv = dev(t["n_valid"])
+    mask = None
+    if mode == "explicit":
+        mask = cp.build_mask(cache, nv, cfg.H, cfg.C, cfg.mask_ld(), window=cfg.window)
+    flags = cp.ATTN_SPLITS(splits)
+    nb = cp.attn_workspace_bytes(cache, q, k, v, mask=mask, flags=flags)
+    assert nb > 0
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    sel = torch.zeros((cfg.B, cfg.H, cfg.D), dtype=q.dtype, device="cuda")
+    outs = [cp.attn_chunk_with_past(cache, q, k, v, n_valid=nv, mask=mask, scale=cfg.scale,
+                                    workspace=ws, select_out=sel, flags=flags)
+            for _ in range(2)]
+    torch.cuda.synchronize()
+    _check(cfg, outs[0], _oracle(cfg, t))
+    assert np.array_equal(bits(outs[1]), bits(outs[0]))
+    assert np.array_equal(bits(sel), bits(cp.select_row(outs[0], nv, -1)))
+    assert int(status.item()) == 0
+
+
 @pytest.mark.parametrize("splits", [16, 17, 33, 64])
 @pytest.mark.parametrize("mode", ["inkernel", "explicit"])
 def test_merge_rounds(cp, splits, mode):

@@ -189,6 +189,12 @@ __global__ void __launch_bounds__(256) k_attn_valu(AttnParams p, int D) {
   const float *mrow = nullptr;
   if (EXPLICIT)
     mrow = p.mask + b * p.mbs + head * p.mhs + static_cast<int64_t>(i < p.C ? i : 0) * p.mld;
+  // this lane's columns, clamped into the row: the tile loops run without a branch per
+  // element (a guarded LDS read waited for its own round trip, element by element);
+  // columns past D carry q = 0 into the scores, and their sums are never stored
+  int dcl[DPT];
+#pragma unroll
+  for (int e = 0; e < DPT; ++e) dcl[e] = imin(ql + 16 * e, D - 1);
   if (u0 < u1) fetch(u0);
   for (int u = u0; u < u1; ++u) {
     int first;
@@ -221,10 +227,7 @@ __global__ void __launch_bounds__(256) k_attn_valu(AttnParams p, int D) {
     for (int kk = 0; kk < KTG; ++kk) {
       float part = 0.f;
 #pragma unroll
-      for (int e = 0; e < DPT; ++e) {
-        const int d = ql + 16 * e;
-        if (d < D) part = fmaf(q[e], Ks[kk * D + d], part);
-      }
+      for (int e = 0; e < DPT; ++e) part = fmaf(q[e], Ks[kk * D + dcl[e]], part);
       part = row16_sum(part);
       const int col = first + kk;
       float add;
@@ -253,10 +256,7 @@ __global__ void __launch_bounds__(256) k_attn_valu(AttnParams p, int D) {
       const float pk = __builtin_amdgcn_exp2f(t[kk] - m_use);
       l_run += pk;
 #pragma unroll
-      for (int e = 0; e < DPT; ++e) {
-        const int d = ql + 16 * e;
-        if (d < D) acc[e] = fmaf(pk, Vs[kk * D + d], acc[e]);
-      }
+      for (int e = 0; e < DPT; ++e) acc[e] = fmaf(pk, Vs[kk * D + dcl[e]], acc[e]);
     }
   }
 
